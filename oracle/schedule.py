@@ -1,0 +1,74 @@
+"""Chunk partition and the ring's index rules (oracle; test infrastructure only).
+
+[InDepth] "The schedule": p ranks sit on a logical ring; each sends only to its
+right neighbour and receives only from its left.  The N-element buffer of every
+rank is cut into p chunks.  Reduce-scatter step s: rank r sends chunk
+(r - s) mod p to rank r + 1, which adds it into its own copy.  All-gather step s:
+rank r sends chunk (r + 1 - s) mod p and the receiver overwrites.  After the
+reduce-scatter rank r holds the finished sum of chunk (r + 1) mod p.
+
+[InDepth] "An implementation": when p does not divide N, the first N mod p chunks
+carry one element more than the rest (the same rule as torch.tensor_split, whose
+first pieces are the largest).
+
+The second ring of the bidirectional variant ([InDepth] "What real libraries
+add", bidirectional rings) runs the other way round.  It is the forward ring seen
+through the mirror r -> -r (mod p): rank r sends to r - 1, reduce-scatter step s
+sends chunk (r + s) mod p, all-gather step s sends chunk (r - 1 + s) mod p, and
+rank r ends the reduce-scatter owning chunk (r - 1) mod p.  ``direction`` selects
+the ring: +1 forward, -1 mirrored.
+"""
+
+
+def chunk_bounds(n, p):
+    """Half-open element ranges [start, end) of the p chunks of an n-element buffer.
+
+    [InDepth] "An implementation": chunk i starts at i*floor(n/p) + min(i, n mod p),
+    so the first n mod p chunks are one element longer.  Python ints throughout,
+    so buffers beyond 2**32 elements are exact.
+    """
+    if p < 1:
+        raise ValueError("p must be >= 1")
+    if n < 0:
+        raise ValueError("n must be >= 0")
+    base, extra = divmod(n, p)
+    starts = [i * base + min(i, extra) for i in range(p + 1)]
+    return [(starts[i], starts[i + 1]) for i in range(p)]
+
+
+def chunk_of(i, n, p):
+    """Index of the chunk that element i of an n-element buffer belongs to.
+
+    Found by scanning the bounds, so it holds by construction for every i.
+    """
+    if not 0 <= i < n:
+        raise IndexError(i)
+    for c, (lo, hi) in enumerate(chunk_bounds(n, p)):
+        if lo <= i < hi:
+            return c
+    raise AssertionError("unreachable")
+
+
+def right_of(r, p, direction=1):
+    """Rank that r sends to: r + 1 on the forward ring, r - 1 on the mirrored ring."""
+    return (r + direction) % p
+
+
+def left_of(r, p, direction=1):
+    """Rank that r receives from."""
+    return (r - direction) % p
+
+
+def rs_send_chunk(r, s, p, direction=1):
+    """Chunk rank r sends at reduce-scatter step s ([InDepth] "The schedule")."""
+    return (r - direction * s) % p
+
+
+def ag_send_chunk(r, s, p, direction=1):
+    """Chunk rank r sends at all-gather step s ([InDepth] "The schedule")."""
+    return (r + direction * (1 - s)) % p
+
+
+def owned_chunk(r, p, direction=1):
+    """Chunk whose full sum rank r holds once the reduce-scatter is over."""
+    return (r + direction) % p

@@ -1,0 +1,96 @@
+"""Pins for the oracle's tree and bidirectional variants (CPU only)."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import cost
+from oracle.tree import tree_levels, tree_pairs
+from ring_all_reduce_schedule_amd import inputs
+
+
+@pytest.mark.parametrize("p", [1, 2, 3, 4, 5, 7, 8, 9, 16, 33, 64])
+def test_tree_int32_equals_brute_force(p):
+    n = 37
+    rng = np.random.default_rng(p)
+    xs = [rng.integers(-2**31, 2**31, n, dtype=np.int64).astype(np.int32) for _ in range(p)]
+    want = [((sum(int(x[i]) for x in xs) + 2**31) % 2**32) - 2**31 for i in range(n)]
+    final, reduced, steps = oracle.tree_allreduce(xs, "int32")
+    assert reduced.tolist() == want
+    assert all(f.tolist() == want for f in final)
+    assert steps == cost.tree_steps(p) == 2 * math.ceil(math.log2(p)) if p > 1 else steps == 0
+
+
+@pytest.mark.parametrize("p", [2, 3, 5, 8, 9, 64])
+def test_tree_pairs_cover_every_rank_once(p):
+    # every rank except the root is a child exactly once over the reduce levels
+    children = [c for k in range(tree_levels(p)) for _, c in tree_pairs(p, k)]
+    assert sorted(children) == list(range(1, p))
+
+
+def test_tree_order_by_hand():
+    # p = 4, one element: x0 = 1, x1 = x2 = x3 = 2**-24.
+    # tree: level 0 gives 1 + 2**-24 -> 1 (tie to even) and 2**-24 + 2**-24 = 2**-23;
+    #       level 1 gives 1 + 2**-23 exactly.
+    # ring (chunk 0 summed x0, x1, x2, x3): every step ties back to 1.
+    e = np.float32(2.0 ** -24)
+    xs = [np.array([1.0], np.float32)] + [np.array([e], np.float32) for _ in range(3)]
+    final, _, _ = oracle.tree_allreduce(xs, "float32")
+    assert all(f[0] == np.float32(1.0 + 2.0 ** -23) for f in final)
+    ring, _, _ = oracle.ring_allreduce(xs, "float32")
+    assert ring[0][0] == np.float32(1.0)
+
+
+@pytest.mark.parametrize("dtype,tol,p,n,sigma", [
+    ("float32", 1e-5, 8, 20_000, 1e-2),
+    ("bfloat16", 1e-2, 64, 4_096, 1.0),
+    ("bfloat16", 1e-2, 8, 20_000, 1e-3),
+])
+def test_tree_within_tolerance_of_exact(dtype, tol, p, n, sigma):
+    xs = inputs.make_inputs(p, n, dtype, seed=4, sigma=sigma)
+    final, _, _ = oracle.tree_allreduce(xs, dtype)
+    exact = oracle.exact_sum(xs, dtype)
+    err = oracle.normwise_error(oracle.as_values(final[0], dtype), exact)
+    assert err < tol
+
+
+def test_bidir_halves():
+    assert oracle.bidir_halves(11) == [(0, 6), (6, 11)]
+    assert oracle.bidir_halves(1) == [(0, 1), (1, 1)]
+    assert oracle.bidir_halves(0) == [(0, 0), (0, 0)]
+
+
+@pytest.mark.parametrize("p,n", [(2, 5), (3, 7), (4, 4), (9, 1003), (8, 1), (5, 0)])
+def test_bidir_int32_equals_brute_force(p, n):
+    rng = np.random.default_rng(n + p)
+    xs = [rng.integers(-5000, 5000, n).astype(np.int32) for _ in range(p)]
+    want = np.sum(np.stack(xs).astype(np.int64), axis=0) if n else np.zeros(0)
+    final, after_rs = oracle.bidir_allreduce(xs, "int32")
+    assert all(f.tolist() == want.tolist() for f in final)
+    # mirrored half: rank r owns chunk (r - 1) mod p of that half
+    (a0, a1), (b0, b1) = oracle.bidir_halves(n)
+    fb = oracle.chunk_bounds(a1 - a0, p)
+    mb = oracle.chunk_bounds(b1 - b0, p)
+    for r in range(p):
+        lo, hi = fb[(r + 1) % p]
+        assert after_rs[r][a0 + lo:a0 + hi].tolist() == want[a0 + lo:a0 + hi].tolist()
+        lo, hi = mb[(r - 1) % p]
+        assert after_rs[r][b0 + lo:b0 + hi].tolist() == want[b0 + lo:b0 + hi].tolist()
+
+
+def test_bidir_mirrored_half_order_by_hand():
+    # p = 3, n = 6: elements 0..2 ride the forward ring (one per chunk), 3..5 the
+    # mirrored ring.  Put the same order-sensitive values in both halves; the
+    # mirrored half must give the mirrored sums (see test_oracle_ring)
+    e = 2.0 ** -24
+    seq = {0: (1.0, e, -e), 1: (e, e, 1.0), 2: (e, 1.0, e)}
+    xs = [np.zeros(6, np.float32) for _ in range(3)]
+    for c, vals in seq.items():
+        for k, v in enumerate(vals):
+            xs[(c + k) % 3][c] = v
+            xs[(c + k) % 3][3 + c] = v
+    final, _ = oracle.bidir_allreduce(xs, "float32")
+    want = np.array([1 - e, 1 + 2 * e, 1, 1, 1, 1 + 2 * e], np.float32)
+    assert all(np.array_equal(f, want) for f in final)
