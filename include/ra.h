@@ -1,0 +1,191 @@
+/*
+ * ra.h -- C ABI of the ring all-reduce library (libra.so) for one MI355X (gfx950).
+ *
+ * The library runs the ring all-reduce chunk schedule over p "virtual ranks"
+ * whose buffers all live in the HBM of one GPU.  Sources, by page and section:
+ *
+ *   [InDepth]   "Ring All-Reduce, in depth: the chunk schedule step by step, a
+ *               working implementation, pipelining, multi-ring and hierarchical
+ *               variants" (aicassindra.com)
+ *   [Derive]    "Derive the cost of a ring all-reduce" (aiinfrainterviews.com)
+ *   [Deepinsea] "AllReduce 与 Ring 通信算法详解" (deepinsea.top)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  bufs    host array of p device pointers, one buffer per rank.  The array is
+ *          read during the call only and never retained.  Every buffer holds n
+ *          contiguous elements of `dtype`, starts on a 16-byte boundary and
+ *          must not overlap another.  The caller owns the buffers and keeps
+ *          them alive until the stream work completes.
+ *  n       elements per rank (int64; buffers beyond 2^32 elements are fine).
+ *  dtype   RA_INT32, RA_FLOAT32 or RA_BFLOAT16.
+ *  op      RA_SUM only ([Deepinsea] "AllReduce 语义" names sum, average and
+ *          max; this library implements sum).
+ *  stream  HIP stream the work is enqueued on.  Calls return as soon as the
+ *          work is enqueued.  Argument errors are reported synchronously by
+ *          the return value, before anything is enqueued; errors that happen
+ *          on the device (a wait that timed out) are sticky per stream and are
+ *          reported by ra_stream_status().
+ *  In place: results overwrite the inputs.  p == 1 or n == 0 is a no-op that
+ *  returns RA_OK ([InDepth] "An implementation": a world of one returns at once).
+ *  Rounding: every hop's sum is rounded to the buffer type (int32 wraps modulo
+ *  2^32, float32 and bfloat16 round to nearest even), which is how an in-place
+ *  add in the buffer's dtype accumulates ([InDepth] "An implementation";
+ *  [Derive] "What interviewers probe next").
+ *  Concurrency: calls on different streams may overlap; calls on one stream
+ *  are ordered by the stream.  The library keeps a small device workspace per
+ *  (device, stream), allocated on first use and kept until process exit.
+ *
+ * Return codes are ra_status values; ra_status_string() names them and
+ * ra_last_error() gives the calling thread's last error message.
+ */
+#ifndef RA_H
+#define RA_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RA_MAX_RANKS 64
+
+typedef enum ra_status {
+  RA_OK = 0,
+  RA_ERR_INVALID_ARG = 1,  /* p < 1, n < 0, NULL pointer (buffers may be NULL when n == 0),
+                              unknown enum value */
+  RA_ERR_UNSUPPORTED = 2,  /* p > RA_MAX_RANKS, op other than RA_SUM, algo not valid for the call */
+  RA_ERR_ALIAS = 3,        /* two rank buffers overlap */
+  RA_ERR_MISALIGNED = 4,   /* a buffer does not start on a 16-byte boundary */
+  RA_ERR_HIP = 5,          /* a HIP runtime call failed (see ra_last_error) */
+  RA_ERR_TIMEOUT = 6       /* a device-side wait exceeded its time budget */
+} ra_status;
+
+typedef enum ra_dtype { RA_INT32 = 0, RA_FLOAT32 = 1, RA_BFLOAT16 = 2 } ra_dtype;
+
+typedef enum ra_op { RA_SUM = 0 } ra_op;
+
+/* Algorithms.  All ring variants give bit-identical results to the step-by-step
+ * schedule; the tree sums in a different order. */
+typedef enum ra_algo {
+  RA_ALGO_DEFAULT = -1,       /* RA_ALGO_FUSED for all-reduce, RING_STEP for RS/AG,
+                                 overridable with the RA_ALGO environment variable */
+  RA_ALGO_RING_STEP = 0,      /* one persistent kernel, 2(p-1) steps, grid barrier between steps */
+  RA_ALGO_RING_PIPELINED = 1, /* chunks cut into slices; per-slice ready flags instead of barriers */
+  RA_ALGO_RING_BIDIR = 2,     /* two counter-rotating rings, each on half of the buffer */
+  RA_ALGO_FUSED = 3,          /* one pass: each element folded in its ring order, written to all ranks */
+  RA_ALGO_TREE = 4            /* binomial tree: reduce to rank 0, broadcast back */
+} ra_algo;
+
+/* ra_options.flags bits */
+#define RA_FLAG_FORCE_TIMEOUT 1u  /* test hook: the first device wait expects an
+                                     arrival that never comes, so it times out
+                                     after timeout_us and every workgroup exits */
+
+typedef struct ra_options {
+  int64_t slice_elems;  /* RING_PIPELINED slice length in elements; 0 = library default.
+                           Rounded up to a multiple of 16 bytes. */
+  int64_t timeout_us;   /* budget of any single device-side wait; 0 = 10 s */
+  int32_t grid;         /* workgroups of persistent kernels; 0 = as many as fit the GPU */
+  uint32_t flags;       /* RA_FLAG_* */
+  uint64_t* step_ts;    /* optional DEVICE array of (steps + 1) uint64: device wall-clock
+                           ticks at kernel start and as each step's barrier releases
+                           (RING_STEP, RING_BIDIR, TREE).  NULL = not recorded. */
+} ra_options;
+
+/*
+ * ra_chunk_bounds -- chunk partition of an n-element buffer into p chunks.
+ * [InDepth] "An implementation": chunk i starts at i*floor(n/p) + min(i, n mod p),
+ * so the first n mod p chunks hold one element more.
+ *   starts  host array of p + 1 int64, written: chunk i is [starts[i], starts[i+1]).
+ * Pure host code, no GPU needed.  RA_ERR_INVALID_ARG for p < 1, n < 0 or NULL;
+ * RA_ERR_UNSUPPORTED for p > RA_MAX_RANKS.
+ */
+int ra_chunk_bounds(int64_t n, int p, int64_t* starts);
+
+/*
+ * ra_reduce_scatter -- the p - 1 reduce-scatter steps ([InDepth] "The schedule";
+ * [Deepinsea] "Phase 1: Reduce-Scatter").  Step s: rank r's chunk (r - s) mod p is
+ * added into rank r+1's copy of that chunk.  Afterwards rank r's chunk
+ * (r + 1) mod p holds the full sum; every other chunk of rank r holds the ring's
+ * partial sum of chunk c over ranks c, c+1, ..., r (the step-by-step states).
+ */
+int ra_reduce_scatter(void* const* bufs, int p, int64_t n, int dtype, int op,
+                      hipStream_t stream);
+
+/*
+ * ra_all_gather -- the p - 1 all-gather steps ([InDepth] "The schedule";
+ * [Deepinsea] "Phase 2: All-Gather").  Expects the layout ra_reduce_scatter
+ * leaves (rank r owns chunk (r + 1) mod p).  Step s: rank r's chunk
+ * (r + 1 - s) mod p overwrites rank r+1's copy; afterwards every rank holds every
+ * owned chunk.  ra_reduce_scatter followed by ra_all_gather equals ra_allreduce.
+ */
+int ra_all_gather(void* const* bufs, int p, int64_t n, int dtype, hipStream_t stream);
+
+/*
+ * ra_allreduce -- reduce-scatter then all-gather ([InDepth] "The schedule";
+ * [Derive] "A strong answer"): every rank ends with the element-wise sum,
+ * accumulated in ring order (element i of chunk c summed over ranks
+ * c, c+1, ..., c+p-1 mod p, rounding every hop).  Uses RA_ALGO_DEFAULT.
+ */
+int ra_allreduce(void* const* bufs, int p, int64_t n, int dtype, int op,
+                 hipStream_t stream);
+
+/*
+ * ra_allreduce_ex -- ra_allreduce with an explicit algorithm and options.
+ *   algo  an ra_algo value.  RING_BIDIR: [InDepth] "What real libraries add",
+ *         bidirectional rings -- the first ceil(n/2) elements go round the
+ *         forward ring, the rest round the mirrored ring (rank r sends to r - 1,
+ *         reduce-scatter step s sends chunk (r + s) mod p).  RING_PIPELINED:
+ *         [InDepth] "What real libraries add", pipelining.  TREE: [Derive]
+ *         "Where it stops scaling", a binomial tree rooted at rank 0 (reduce
+ *         level k adds rank r + 2^k into rank r for r a multiple of 2^(k+1)).
+ *   opt   may be NULL (all defaults).
+ */
+int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
+                    const ra_options* opt, hipStream_t stream);
+
+/* ra_reduce_scatter / ra_all_gather with algo RING_STEP or RING_PIPELINED and options. */
+int ra_reduce_scatter_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
+                         const ra_options* opt, hipStream_t stream);
+int ra_all_gather_ex(void* const* bufs, int p, int64_t n, int dtype, int algo,
+                     const ra_options* opt, hipStream_t stream);
+
+/*
+ * ra_stream_status -- waits for `stream`, then returns RA_ERR_TIMEOUT if a
+ * device-side wait of an earlier call on it timed out ([InDepth] "Failure
+ * modes": a dead or stalled rank must fail fast instead of hanging), else
+ * RA_OK (or RA_ERR_HIP if synchronising failed).  A timed-out call leaves its
+ * buffers in an unspecified state; calls enqueued after it on the same stream
+ * do no work until this function has reported the error, which also clears it.
+ */
+int ra_stream_status(hipStream_t stream);
+
+/* Static name of a status code ("RA_OK", ...). */
+const char* ra_status_string(int code);
+
+/* Message of the calling thread's last failing call ("" if none).  Valid until
+ * that thread's next call into the library. */
+const char* ra_last_error(void);
+
+/*
+ * ra_wallclock_hz -- frequency of the device clock step_ts is stamped with.
+ * Writes it to *hz; RA_ERR_HIP if the device cannot be queried.
+ */
+int ra_wallclock_hz(int64_t* hz);
+
+/*
+ * ra_stream_copy -- plain device copy of `bytes` bytes (16-byte aligned
+ * pointers, bytes a multiple of 16), one read and one write per byte.  A
+ * measurement helper: the streaming ceiling the all-reduce kernels are
+ * compared with, and the known-size kernel that HBM byte counters are
+ * calibrated against.  Not part of the all-reduce.
+ */
+int ra_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RA_H */

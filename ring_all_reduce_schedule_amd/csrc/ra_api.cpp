@@ -1,0 +1,383 @@
+// ra_api.cpp -- host side of libra.so: argument checks, per-stream workspace,
+// algorithm dispatch and error reporting for the C ABI declared in include/ra.h.
+#include "ra.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "ra_device.h"
+#include "ra_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+  return fail(RA_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool debug_on() {
+  static int on = [] {
+    const char* v = std::getenv("RA_DEBUG");
+    return v && *v && std::strcmp(v, "0") != 0 ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+const char* algo_name(int a) {
+  switch (a) {
+    case RA_ALGO_RING_STEP: return "ring_step";
+    case RA_ALGO_RING_PIPELINED: return "ring_pipelined";
+    case RA_ALGO_RING_BIDIR: return "ring_bidir";
+    case RA_ALGO_FUSED: return "fused";
+    case RA_ALGO_TREE: return "tree";
+    default: return "?";
+  }
+}
+
+// RA_ALGO overrides the default algorithm (diagnosis only), by name or number.
+int env_algo(int fallback) {
+  const char* v = std::getenv("RA_ALGO");
+  if (!v || !*v) return fallback;
+  for (int a = RA_ALGO_RING_STEP; a <= RA_ALGO_TREE; ++a)
+    if (std::strcmp(v, algo_name(a)) == 0) return a;
+  char* end = nullptr;
+  long x = std::strtol(v, &end, 10);
+  if (end && *end == 0 && x >= RA_ALGO_RING_STEP && x <= RA_ALGO_TREE) return (int)x;
+  return fallback;
+}
+
+// ---------------------------------------------------------------- validation
+
+int check_args(void* const* bufs, int p, int64_t n, int dtype) {
+  if (!bufs) return fail(RA_ERR_INVALID_ARG, "bufs is NULL");
+  if (p < 1) return fail(RA_ERR_INVALID_ARG, "p = %d, need p >= 1", p);
+  if (p > RA_MAX_RANKS) return fail(RA_ERR_UNSUPPORTED, "p = %d exceeds RA_MAX_RANKS = %d", p, RA_MAX_RANKS);
+  if (n < 0) return fail(RA_ERR_INVALID_ARG, "n = %lld, need n >= 0", (long long)n);
+  if (dtype < RA_INT32 || dtype > RA_BFLOAT16) return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (n == 0) return RA_OK;   // nothing is accessed: empty buffers may be NULL
+  for (int r = 0; r < p; ++r) {
+    if (!bufs[r]) return fail(RA_ERR_INVALID_ARG, "bufs[%d] is NULL", r);
+    if (reinterpret_cast<uintptr_t>(bufs[r]) % 16 != 0)
+      return fail(RA_ERR_MISALIGNED, "bufs[%d] = %p is not 16-byte aligned", r, bufs[r]);
+  }
+  {
+    const uint64_t bytes = (uint64_t)n * (uint64_t)ra::elem_bytes(dtype);
+    if (bytes / (uint64_t)ra::elem_bytes(dtype) != (uint64_t)n)
+      return fail(RA_ERR_INVALID_ARG, "n = %lld overflows the address space", (long long)n);
+    std::vector<std::pair<uintptr_t, int>> starts;
+    for (int r = 0; r < p; ++r) starts.emplace_back(reinterpret_cast<uintptr_t>(bufs[r]), r);
+    std::sort(starts.begin(), starts.end());
+    for (int i = 0; i + 1 < p; ++i)
+      if (starts[i].first + bytes > starts[i + 1].first)
+        return fail(RA_ERR_ALIAS, "buffers of ranks %d and %d overlap", starts[i].second,
+                    starts[i + 1].second);
+  }
+  return RA_OK;
+}
+
+int check_op(int op) {
+  if (op != RA_SUM) return fail(RA_ERR_UNSUPPORTED, "op %d not supported (only RA_SUM)", op);
+  return RA_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+
+struct Workspace {
+  ra::WsHeader* hdr = nullptr;     // device
+  uint32_t* flags = nullptr;       // device, pipelined ready counters
+  int64_t flag_cap = 0;            // entries
+  uint32_t epoch = 0;              // pipelined calls so far (flag base = epoch * kFlagStride)
+};
+
+constexpr uint32_t kFlagStride = 128;   // > 2(p-1) hops for p <= 64
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int get_workspace(hipStream_t s, Workspace** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace& w = g_ws[{dev, s}];
+  if (!w.hdr) {
+    void* p = nullptr;
+    e = hipMalloc(&p, sizeof(ra::WsHeader));
+    if (e != hipSuccess) return fail_hip(e, "hipMalloc(workspace)");
+    e = hipMemset(p, 0, sizeof(ra::WsHeader));
+    if (e != hipSuccess) { (void)hipFree(p); return fail_hip(e, "hipMemset(workspace)"); }
+    w.hdr = static_cast<ra::WsHeader*>(p);
+  }
+  *out = &w;
+  return RA_OK;
+}
+
+// Make room for `entries` ready counters and return the flag base of this call.
+int reserve_flags(Workspace* w, int64_t entries, hipStream_t s, uint32_t* base) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if (entries > w->flag_cap) {
+    if (w->flags) {
+      // the old counters may still be read by queued work on this stream
+      hipError_t e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+      (void)hipFree(w->flags);
+      w->flags = nullptr;
+      w->flag_cap = 0;
+    }
+    const int64_t cap = std::max<int64_t>(entries, 4096);
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, (size_t)cap * sizeof(uint32_t));
+    if (e != hipSuccess) return fail_hip(e, "hipMalloc(flags)");
+    e = hipMemset(p, 0, (size_t)cap * sizeof(uint32_t));
+    if (e != hipSuccess) { (void)hipFree(p); return fail_hip(e, "hipMemset(flags)"); }
+    w->flags = static_cast<uint32_t*>(p);
+    w->flag_cap = cap;
+  }
+  // counters only grow: every call starts above anything an earlier call left
+  w->epoch += 1;
+  if ((uint64_t)w->epoch * kFlagStride + kFlagStride >= 0xFFFFFFFFull) {
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipMemset(w->flags, 0, (size_t)w->flag_cap * sizeof(uint32_t));
+    if (e != hipSuccess) return fail_hip(e, "resetting flags");
+    w->epoch = 1;
+  }
+  *base = w->epoch * kFlagStride;
+  return RA_OK;
+}
+
+int sync_cfg(const ra_options* opt, Workspace* w, ra::SyncCfg* sc) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  int khz = 0;
+  e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess || khz <= 0) khz = 100000;   // 100 MHz, the gfx9 constant clock
+  const int64_t us = opt && opt->timeout_us > 0 ? opt->timeout_us : 10 * 1000 * 1000;
+  sc->ws = w->hdr;
+  sc->limit_ticks = (uint64_t)us * (uint64_t)khz / 1000u;
+  sc->expect_extra = opt && (opt->flags & RA_FLAG_FORCE_TIMEOUT) ? 1u : 0u;
+  sc->step_ts = opt ? opt->step_ts : nullptr;
+  sc->grid = opt && opt->grid > 0 ? opt->grid : 0;
+  return RA_OK;
+}
+
+void fill_ptrs(void* const* bufs, int p, ra::RankPtrs* P) {
+  std::memset(P, 0, sizeof(*P));
+  for (int r = 0; r < p; ++r) P->b[r] = bufs[r];
+}
+
+void debug_line(const char* call, int algo, int p, int64_t n, int dtype, int grid) {
+  if (!debug_on()) return;
+  std::fprintf(stderr, "[ra] %s algo=%s p=%d n=%lld dtype=%d grid=%d ring=", call,
+               algo_name(algo), p, (long long)n, dtype, grid);
+  for (int r = 0; r < p; ++r) std::fprintf(stderr, "%d%s", r, r + 1 < p ? "->" : "->0\n");
+}
+
+int64_t default_slice(int dtype) { return (int64_t)(64 * 1024) / ra::elem_bytes(dtype); }
+
+// Run phases [hop_begin, hop_end) (0..p-2 reduce-scatter, p-1..2p-3 all-gather)
+// with a ring algorithm.
+int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, int algo,
+             int hop_begin, int hop_end, const ra_options* opt, hipStream_t s) {
+  Workspace* w = nullptr;
+  int rc = get_workspace(s, &w);
+  if (rc != RA_OK) return rc;
+  ra::SyncCfg sc;
+  rc = sync_cfg(opt, w, &sc);
+  if (rc != RA_OK) return rc;
+  ra::RankPtrs P;
+  fill_ptrs(bufs, p, &P);
+  int grid = 0;
+  hipError_t e;
+  if (algo == RA_ALGO_RING_PIPELINED) {
+    int64_t slice = opt && opt->slice_elems > 0 ? opt->slice_elems : default_slice(dtype);
+    const int64_t V = 16 / ra::elem_bytes(dtype);
+    slice = (slice + V - 1) / V * V;
+    const int64_t kmax = ra::pipelined_slices_per_chunk(p, n, dtype, slice);
+    uint32_t base = 0;
+    rc = reserve_flags(w, kmax * p, s, &base);
+    if (rc != RA_OK) return rc;
+    e = ra::launch_pipelined(P, p, n, dtype, hop_begin, hop_end, slice, kmax, w->flags, base,
+                             sc, s, &grid);
+  } else {
+    e = ra::launch_steps(P, p, n, dtype, ra::kModeRing, hop_begin, hop_end, sc, s, &grid);
+  }
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  debug_line(call, algo, p, n, dtype, grid);
+  return RA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ra_chunk_bounds(int64_t n, int p, int64_t* starts) {
+  if (!starts) return fail(RA_ERR_INVALID_ARG, "starts is NULL");
+  if (p < 1) return fail(RA_ERR_INVALID_ARG, "p = %d, need p >= 1", p);
+  if (p > RA_MAX_RANKS) return fail(RA_ERR_UNSUPPORTED, "p = %d exceeds RA_MAX_RANKS", p);
+  if (n < 0) return fail(RA_ERR_INVALID_ARG, "n = %lld, need n >= 0", (long long)n);
+  const int64_t base = n / p, extra = n % p;
+  for (int i = 0; i <= p; ++i) starts[i] = (int64_t)i * base + std::min<int64_t>(i, extra);
+  return RA_OK;
+}
+
+int ra_reduce_scatter_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
+                         const ra_options* opt, hipStream_t stream) {
+  int rc = check_args(bufs, p, n, dtype);
+  if (rc == RA_OK) rc = check_op(op);
+  if (rc != RA_OK) return rc;
+  if (algo == RA_ALGO_DEFAULT) algo = RA_ALGO_RING_STEP;
+  if (algo != RA_ALGO_RING_STEP && algo != RA_ALGO_RING_PIPELINED)
+    return fail(RA_ERR_UNSUPPORTED, "reduce-scatter runs RING_STEP or RING_PIPELINED, not %d", algo);
+  if (p == 1 || n == 0) return RA_OK;
+  return run_ring("reduce_scatter", bufs, p, n, dtype, algo, 0, p - 1, opt, stream);
+}
+
+int ra_all_gather_ex(void* const* bufs, int p, int64_t n, int dtype, int algo,
+                     const ra_options* opt, hipStream_t stream) {
+  int rc = check_args(bufs, p, n, dtype);
+  if (rc != RA_OK) return rc;
+  if (algo == RA_ALGO_DEFAULT) algo = RA_ALGO_RING_STEP;
+  if (algo != RA_ALGO_RING_STEP && algo != RA_ALGO_RING_PIPELINED)
+    return fail(RA_ERR_UNSUPPORTED, "all-gather runs RING_STEP or RING_PIPELINED, not %d", algo);
+  if (p == 1 || n == 0) return RA_OK;
+  return run_ring("all_gather", bufs, p, n, dtype, algo, p - 1, 2 * (p - 1), opt, stream);
+}
+
+int ra_reduce_scatter(void* const* bufs, int p, int64_t n, int dtype, int op, hipStream_t stream) {
+  return ra_reduce_scatter_ex(bufs, p, n, dtype, op, RA_ALGO_DEFAULT, nullptr, stream);
+}
+
+int ra_all_gather(void* const* bufs, int p, int64_t n, int dtype, hipStream_t stream) {
+  return ra_all_gather_ex(bufs, p, n, dtype, RA_ALGO_DEFAULT, nullptr, stream);
+}
+
+int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
+                    const ra_options* opt, hipStream_t stream) {
+  int rc = check_args(bufs, p, n, dtype);
+  if (rc == RA_OK) rc = check_op(op);
+  if (rc != RA_OK) return rc;
+  if (algo == RA_ALGO_DEFAULT) algo = env_algo(RA_ALGO_FUSED);
+  if (algo < RA_ALGO_RING_STEP || algo > RA_ALGO_TREE)
+    return fail(RA_ERR_INVALID_ARG, "unknown algo %d", algo);
+  if (p == 1 || n == 0) return RA_OK;
+  if (algo == RA_ALGO_FUSED) {
+    ra::RankPtrs P;
+    fill_ptrs(bufs, p, &P);
+    int grid = 0;
+    hipError_t e = ra::launch_fused(P, p, n, dtype, stream, &grid);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    debug_line("allreduce", algo, p, n, dtype, grid);
+    return RA_OK;
+  }
+  if (algo == RA_ALGO_RING_STEP || algo == RA_ALGO_RING_PIPELINED)
+    return run_ring("allreduce", bufs, p, n, dtype, algo, 0, 2 * (p - 1), opt, stream);
+  // bidirectional rings or tree: one cooperative launch of the step kernel
+  Workspace* w = nullptr;
+  rc = get_workspace(stream, &w);
+  if (rc != RA_OK) return rc;
+  ra::SyncCfg sc;
+  rc = sync_cfg(opt, w, &sc);
+  if (rc != RA_OK) return rc;
+  ra::RankPtrs P;
+  fill_ptrs(bufs, p, &P);
+  int grid = 0;
+  hipError_t e;
+  if (algo == RA_ALGO_RING_BIDIR) {
+    e = ra::launch_steps(P, p, n, dtype, ra::kModeBidir, 0, 2 * (p - 1), sc, stream, &grid);
+  } else {
+    int levels = 0;
+    while ((1 << levels) < p) ++levels;
+    e = ra::launch_steps(P, p, n, dtype, ra::kModeTree, 0, 2 * levels, sc, stream, &grid);
+  }
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  debug_line("allreduce", algo, p, n, dtype, grid);
+  return RA_OK;
+}
+
+int ra_allreduce(void* const* bufs, int p, int64_t n, int dtype, int op, hipStream_t stream) {
+  return ra_allreduce_ex(bufs, p, n, dtype, op, RA_ALGO_DEFAULT, nullptr, stream);
+}
+
+int ra_stream_status(hipStream_t stream) {
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  ra::WsHeader* hdr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    auto it = g_ws.find({dev, stream});
+    if (it == g_ws.end() || !it->second.hdr) return RA_OK;
+    hdr = it->second.hdr;
+  }
+  uint32_t status = 0;
+  e = hipMemcpy(&status, &hdr->status, sizeof status, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail_hip(e, "reading device status");
+  if (status == 0) return RA_OK;
+  // clear the sticky error and the barrier word the aborted kernel left behind
+  e = hipMemset(hdr, 0, 2 * sizeof(uint32_t));
+  if (e != hipSuccess) return fail_hip(e, "clearing device status");
+  return fail((int)status, "a device-side wait timed out (status %u)", status);
+}
+
+const char* ra_status_string(int code) {
+  switch (code) {
+    case RA_OK: return "RA_OK";
+    case RA_ERR_INVALID_ARG: return "RA_ERR_INVALID_ARG";
+    case RA_ERR_UNSUPPORTED: return "RA_ERR_UNSUPPORTED";
+    case RA_ERR_ALIAS: return "RA_ERR_ALIAS";
+    case RA_ERR_MISALIGNED: return "RA_ERR_MISALIGNED";
+    case RA_ERR_HIP: return "RA_ERR_HIP";
+    case RA_ERR_TIMEOUT: return "RA_ERR_TIMEOUT";
+    default: return "RA_ERR_UNKNOWN";
+  }
+}
+
+const char* ra_last_error(void) { return g_last_error.c_str(); }
+
+int ra_wallclock_hz(int64_t* hz) {
+  if (!hz) return fail(RA_ERR_INVALID_ARG, "hz is NULL");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  int khz = 0;
+  e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return fail_hip(e, "hipDeviceGetAttribute(WallClockRate)");
+  *hz = (int64_t)khz * 1000;
+  return RA_OK;
+}
+
+int ra_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
+  if (!dst || !src) return fail(RA_ERR_INVALID_ARG, "NULL pointer");
+  if (bytes < 0 || bytes % 16 != 0) return fail(RA_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  if (reinterpret_cast<uintptr_t>(dst) % 16 || reinterpret_cast<uintptr_t>(src) % 16)
+    return fail(RA_ERR_MISALIGNED, "pointers must be 16-byte aligned");
+  hipError_t e = ra::launch_copy(dst, src, bytes, stream);
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  return RA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,251 @@
+// ra_device.h -- device-side building blocks of the ring all-reduce kernels (gfx950).
+//
+// * element types: one hop of the ring is "receiver's chunk += incoming chunk",
+//   rounded to the buffer type ("Ring All-Reduce, in depth", section "An
+//   implementation": the torch ring adds in the tensor's dtype).  Values move in
+//   16-byte vectors (global_load/store_dwordx4): 4 int32, 4 float32 or 8 bfloat16.
+// * chunk geometry: chunk c of an n-element buffer split p ways starts at
+//   c*floor(n/p) + min(c, n mod p) (same page, "An implementation").
+// * synchronisation between workgroups: a self-resetting grid barrier and
+//   per-slice ready counters, both with bounded waits that report a timeout
+//   instead of hanging ("Ring All-Reduce, in depth", "Failure modes").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ra {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxRanks = 64;
+constexpr int kBlock = 256;               // threads per workgroup (4 wave64s)
+
+// Device pointers of the p rank buffers, passed by value in the kernel
+// arguments; a wave-uniform index into it compiles to a scalar load from the
+// argument segment.
+struct RankPtrs {
+  void* b[kMaxRanks];
+};
+
+// Partition of a segment [off, off + len) into p chunks.
+struct ChunkGeo {
+  int64_t off;    // first element of the segment
+  int64_t base;   // floor(len / p)
+  int64_t extra;  // len mod p
+};
+
+__device__ __forceinline__ int64_t chunk_lo(const ChunkGeo& g, int c) {
+  return g.off + (int64_t)c * g.base + (c < g.extra ? c : g.extra);
+}
+__device__ __forceinline__ int64_t chunk_hi(const ChunkGeo& g, int c) {
+  return chunk_lo(g, c + 1);
+}
+
+__device__ __forceinline__ int mod_p(int x, int p) {
+  x %= p;
+  return x < 0 ? x + p : x;
+}
+
+// ---------------------------------------------------------------- element types
+// dtype codes match ra_dtype: 0 int32, 1 float32, 2 bfloat16.
+
+template <int DT> struct Elem;
+
+template <> struct Elem<0> {                 // int32: wraps modulo 2^32
+  static constexpr int V = 4;                // elements per 16-byte vector
+  typedef uint32_t S;                        // storage of one element
+  __device__ static __forceinline__ u32x4 add(u32x4 a, u32x4 b) { return a + b; }
+  __device__ static __forceinline__ S add1(S a, S b) { return a + b; }
+};
+
+template <> struct Elem<1> {                 // float32: IEEE add, nearest even
+  static constexpr int V = 4;
+  typedef uint32_t S;
+  __device__ static __forceinline__ u32x4 add(u32x4 a, u32x4 b) {
+    f32x4 s = __builtin_bit_cast(f32x4, a) + __builtin_bit_cast(f32x4, b);
+    return __builtin_bit_cast(u32x4, s);
+  }
+  __device__ static __forceinline__ S add1(S a, S b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }
+};
+
+// bfloat16: both operands widened exactly to float32 (a bf16 is the top half of
+// a float32), added in float32 (nearest even), narrowed back to bf16 (nearest
+// even) with the gfx950 packed convert.  Rounding through float32 first gives
+// the same result as rounding the exact sum once, because float32 carries more
+// than twice bf16's precision plus two bits.
+__device__ __forceinline__ uint32_t bf16_pair_add(uint32_t a, uint32_t b) {
+  f32x2 s;
+  s.x = __uint_as_float(a << 16) + __uint_as_float(b << 16);
+  s.y = __uint_as_float(a & 0xffff0000u) + __uint_as_float(b & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(s, bf16x2));
+}
+
+template <> struct Elem<2> {
+  static constexpr int V = 8;
+  typedef uint16_t S;
+  __device__ static __forceinline__ u32x4 add(u32x4 a, u32x4 b) {
+    u32x4 r;
+    r.x = bf16_pair_add(a.x, b.x);
+    r.y = bf16_pair_add(a.y, b.y);
+    r.z = bf16_pair_add(a.z, b.z);
+    r.w = bf16_pair_add(a.w, b.w);
+    return r;
+  }
+  __device__ static __forceinline__ S add1(S a, S b) {
+    return (S)(bf16_pair_add((uint32_t)a, (uint32_t)b) & 0xffffu);
+  }
+};
+
+// ---------------------------------------------------------------- memory access
+
+__device__ __forceinline__ u32x4 ld16(const void* base, int64_t vec) {
+  return reinterpret_cast<const u32x4*>(base)[vec];
+}
+__device__ __forceinline__ void st16(void* base, int64_t vec, u32x4 v) {
+  reinterpret_cast<u32x4*>(base)[vec] = v;
+}
+template <int DT>
+__device__ __forceinline__ typename Elem<DT>::S ld1(const void* base, int64_t i) {
+  return reinterpret_cast<const typename Elem<DT>::S*>(base)[i];
+}
+template <int DT>
+__device__ __forceinline__ void st1(void* base, int64_t i, typename Elem<DT>::S v) {
+  reinterpret_cast<typename Elem<DT>::S*>(base)[i] = v;
+}
+
+// Split [lo, hi) into a scalar head, whole 16-byte vectors, and a scalar tail.
+// All rank buffers start 16-byte aligned, so element i has the same alignment
+// in every buffer.
+struct Span {
+  int64_t v0, v1;       // vector indices [v0, v1)
+  int64_t head_hi;      // head = [lo, head_hi)
+  int64_t tail_lo;      // tail = [tail_lo, hi)
+};
+
+template <int V>
+__device__ __forceinline__ Span split_span(int64_t lo, int64_t hi) {
+  Span s;
+  int64_t a0 = (lo + V - 1) / V * V;
+  int64_t a1 = hi / V * V;
+  if (a0 >= a1) {                 // no whole vector: all scalar
+    s.v0 = s.v1 = 0;
+    s.head_hi = hi;
+    s.tail_lo = hi;
+  } else {
+    s.v0 = a0 / V;
+    s.v1 = a1 / V;
+    s.head_hi = a0;
+    s.tail_lo = a1;
+  }
+  return s;
+}
+
+// ---------------------------------------------------------------- workspace
+
+// Device workspace shared by the calls on one (device, stream).
+struct WsHeader {
+  uint32_t bar;          // grid-barrier word (self-resetting, see grid_barrier)
+  uint32_t status;       // sticky: 0 ok, else an ra_status code set on device
+  uint32_t pad[62];      // keep flags on their own cache lines
+};
+
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Make this wave's earlier global stores visible device-wide (the L2 of every
+// XCD) before anything the workgroup does next.  Issued by every wave: the
+// workgroup barrier alone does not wait for other waves' stores to complete.
+__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Grid-wide barrier over `nblocks` co-resident workgroups.
+//
+// Every workgroup adds 1 to the barrier word except workgroup 0, which adds
+// 2^31 - (nblocks - 1); one full round therefore adds exactly 2^31, so the top
+// bit flips precisely when the last workgroup arrives and the low bits return to
+// where they were -- the word never needs resetting between rounds or calls.  A
+// waiter watches for the top bit to differ from what it saw when it arrived.
+//
+// `expect_extra` = 1 makes the round wait for one arrival that never comes (a
+// test hook for the timeout path).  Waits are bounded by `limit` ticks of the
+// constant-rate device clock; on expiry the waiter records RA_ERR_TIMEOUT (6)
+// in the sticky status word.  A workgroup also gives up as soon as it sees a
+// nonzero status.  Returns false when the caller must exit.
+__device__ __forceinline__ bool grid_barrier(WsHeader* ws, uint32_t nblocks,
+                                             uint32_t expect_extra, uint64_t limit) {
+  __shared__ int go;
+  release_agent();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t inc = blockIdx.x == 0 ? 0x80000000u - (nblocks + expect_extra - 1u) : 1u;
+    uint32_t old = __hip_atomic_fetch_add(&ws->bar, inc, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t t0 = now_ticks();
+    int ok = 1;
+    while (((ld_relaxed(&ws->bar) ^ old) & 0x80000000u) == 0) {
+      if (ld_relaxed(&ws->status) != 0) { ok = 0; break; }
+      if (now_ticks() - t0 > limit) {
+        __hip_atomic_store(&ws->status, 6u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    acquire_agent();
+    go = ok;
+  }
+  __syncthreads();
+  return go != 0;
+}
+
+// Wait until *flag >= target (thread 0 spins, the workgroup follows).  Same
+// timeout and abort rules as grid_barrier.  Returns false when the caller must exit.
+__device__ __forceinline__ bool wait_flag(WsHeader* ws, const uint32_t* flag, uint32_t target,
+                                          uint64_t limit) {
+  __shared__ int go;
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    if ((int32_t)(ld_relaxed(flag) - target) < 0) {
+      uint64_t t0 = now_ticks();
+      while ((int32_t)(ld_relaxed(flag) - target) < 0) {
+        if (ld_relaxed(&ws->status) != 0) { ok = 0; break; }
+        if (now_ticks() - t0 > limit) {
+          __hip_atomic_store(&ws->status, 6u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    acquire_agent();
+    go = ok;
+  }
+  __syncthreads();
+  return go != 0;
+}
+
+// Publish *flag = value after every wave's stores of this workgroup.
+__device__ __forceinline__ void post_flag(uint32_t* flag, uint32_t value) {
+  release_agent();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool ws_failed(WsHeader* ws) {
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = ld_relaxed(&ws->status) != 0;
+  __syncthreads();
+  return bad != 0;
+}
+
+}  // namespace ra

@@ -1,0 +1,569 @@
+// ra_kernels.hip -- HIP kernels of the ring all-reduce for gfx950, and their launchers.
+//
+// p virtual ranks live in one GPU's HBM; a "send" of the ring is a read of the
+// sender's chunk and a "receive" is an add into (or a copy over) the receiver's
+// chunk.  Sources: "Ring All-Reduce, in depth" (aicassindra.com), sections "The
+// schedule", "An implementation", "What real libraries add"; "Derive the cost of
+// a ring all-reduce" (aiinfrainterviews.com), section "Where it stops scaling".
+//
+// Kernels
+//   k_fused      one pass over the elements; each element is folded in its
+//                chunk's ring order (chunk c: ranks c, c+1, ..., c+p-1, rounding
+//                every hop) and the result is stored to all p ranks.  Reads and
+//                writes every buffer once: 2*p*S bytes, the least any one-GPU
+//                all-reduce can move.
+//   k_steps      the schedule step by step in one persistent cooperative launch:
+//                reduce-scatter steps, all-gather steps (forward ring, or both
+//                rings of the bidirectional variant on the two halves), or the
+//                binomial tree's levels; a grid barrier separates steps.
+//   k_pipelined  the forward ring with chunks cut into slices; workgroups are
+//                assigned to ranks, and a rank forwards slice k as soon as its
+//                left neighbour has finished slice k (per-slice ready counters
+//                instead of step barriers).
+//   k_copy       plain streaming copy, a measurement helper.
+//
+// All element traffic uses 16-byte vector loads/stores with consecutive lanes
+// on consecutive vectors; chunk edges that fall inside a vector are handled
+// element by element.  Every index into a buffer is 64-bit.
+#include "ra_device.h"
+#include "ra_internal.h"
+
+#include <algorithm>
+#include <mutex>
+#include <unordered_map>
+
+namespace ra {
+
+int elem_bytes(int dtype) { return dtype == 2 ? 2 : 4; }
+
+static int elems_per_vec(int dtype) { return 16 / elem_bytes(dtype); }
+
+// Whole 16-byte vectors inside [lo, hi) (host mirror of split_span).
+static int64_t vecs_in(int64_t lo, int64_t hi, int V) {
+  int64_t a0 = (lo + V - 1) / V * V;
+  int64_t a1 = hi / V * V;
+  return a1 > a0 ? (a1 - a0) / V : 0;
+}
+
+static int64_t host_chunk_lo(int64_t off, int64_t len, int p, int c) {
+  int64_t base = len / p, extra = len % p;
+  return off + (int64_t)c * base + std::min<int64_t>(c, extra);
+}
+
+static ChunkGeo make_geo(int64_t off, int64_t len, int p) {
+  ChunkGeo g;
+  g.off = off;
+  g.base = len / p;
+  g.extra = len % p;
+  return g;
+}
+
+// ================================================================ hop on one tile
+
+// Tile j of the segment [lo, hi): dst[i] = dst[i] + src[i] (ADD) or dst[i] = src[i].
+// A tile covers kBlock*U consecutive vectors; tile 0 also takes the scalar
+// head and tail of the segment.
+template <int DT, int U, bool ADD>
+__device__ __forceinline__ void hop_tile(const void* __restrict__ src, void* __restrict__ dst,
+                                         int64_t lo, int64_t hi, int64_t j) {
+  typedef Elem<DT> E;
+  constexpr int V = E::V;
+  const Span sp = split_span<V>(lo, hi);
+  const int64_t tv = (int64_t)kBlock * U;
+  const int64_t t0 = sp.v0 + j * tv;
+  const int64_t t1 = t0 + tv < sp.v1 ? t0 + tv : sp.v1;
+  if (t0 < t1) {
+    int64_t v[U];
+    u32x4 a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      v[u] = t0 + u * kBlock + threadIdx.x;
+      if (v[u] < t1) {
+        a[u] = ld16(src, v[u]);
+        if (ADD) b[u] = ld16(dst, v[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v[u] < t1) st16(dst, v[u], ADD ? E::add(b[u], a[u]) : a[u]);
+  }
+  if (j == 0) {
+    const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
+    const int t = threadIdx.x;
+    if (t < nh + nt) {
+      const int64_t i = t < nh ? lo + t : sp.tail_lo + (t - nh);
+      typename E::S x = ld1<DT>(src, i);
+      st1<DT>(dst, i, ADD ? E::add1(ld1<DT>(dst, i), x) : x);
+    }
+  }
+}
+
+// ================================================================ fused one-pass
+
+// Tile t = (chunk c, tile j of that chunk).  For every element of the tile:
+// acc = x_c; acc = acc + x_{c+1}; ...; acc = acc + x_{c+p-1} (indices mod p,
+// rounding each addition), then acc is stored to every rank.  This is the
+// order in which the step-by-step ring accumulates chunk c, so the bits match.
+template <int DT, int U>
+__global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p, int64_t T,
+                                                  int64_t ntiles) {
+  typedef Elem<DT> E;
+  constexpr int V = E::V;
+  constexpr int KB = 8;                     // ranks loaded per batch
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int c = (int)(t / T);
+    const int64_t j = t - (int64_t)c * T;
+    const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
+    const Span sp = split_span<V>(lo, hi);
+    const int64_t tv = (int64_t)kBlock * U;
+    const int64_t t0 = sp.v0 + j * tv;
+    const int64_t t1 = t0 + tv < sp.v1 ? t0 + tv : sp.v1;
+    if (t0 < t1) {
+      int64_t v[U];
+      u32x4 acc[U];
+      const void* first = P.b[c];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        v[u] = t0 + u * kBlock + threadIdx.x;
+        if (v[u] < t1) acc[u] = ld16(first, v[u]);
+      }
+      for (int k0 = 1; k0 < p; k0 += KB) {
+        u32x4 x[KB][U];
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+          if (k0 + i < p) {
+            int r = c + k0 + i;
+            r = r >= p ? r - p : r;
+            const void* src = P.b[r];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+              if (v[u] < t1) x[i][u] = ld16(src, v[u]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < KB; ++i)
+          if (k0 + i < p) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[u] = E::add(acc[u], x[i][u]);
+          }
+      }
+      for (int r = 0; r < p; ++r) {
+        void* dst = P.b[r];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (v[u] < t1) st16(dst, v[u], acc[u]);
+      }
+    }
+    if (j == 0) {
+      const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
+      const int tt = threadIdx.x;
+      if (tt < nh + nt) {
+        const int64_t i = tt < nh ? lo + tt : sp.tail_lo + (tt - nh);
+        typename E::S acc = ld1<DT>(P.b[c], i);
+        for (int k = 1; k < p; ++k) {
+          int r = c + k;
+          r = r >= p ? r - p : r;
+          acc = E::add1(acc, ld1<DT>(P.b[r], i));
+        }
+        for (int r = 0; r < p; ++r) st1<DT>(P.b[r], i, acc);
+      }
+    }
+  }
+}
+
+// ================================================================ step by step
+
+struct StepArgs {
+  RankPtrs P;
+  ChunkGeo half[2];     // ring: half[0] = whole buffer; bidir: forward, mirrored half
+  int64_t T;            // tiles per segment
+  int64_t n;            // elements per rank (tree segments are whole buffers)
+  WsHeader* ws;
+  uint64_t* step_ts;
+  uint64_t limit;
+  int p, mode, step_begin, step_end, levels;
+  uint32_t expect_extra;
+};
+
+struct Seg {
+  int64_t lo, hi;
+  int src, dst;
+  bool add;
+};
+
+// Number of segments (independent chunk transfers) in a step.
+__device__ __forceinline__ int step_segments(const StepArgs& a, int step) {
+  if (a.mode == kModeTree) {
+    const int k = step < a.levels ? step : 2 * a.levels - 1 - step;
+    return (a.p - 1 - (1 << k)) / (2 << k) + 1;
+  }
+  return a.mode == kModeBidir ? 2 * a.p : a.p;
+}
+
+// Segment `seg` of `step`.
+//   Ring, direction d (+1 forward, -1 mirrored), chunk c:
+//     reduce-scatter step s: sender c + d*s, receiver c + d*(s+1), add
+//       (forward: rank r sends chunk r - s to r + 1; mirrored: chunk r + s to r - 1)
+//     all-gather step s:     sender c + d*(s-1), receiver c + d*s, copy
+//       (forward: rank r sends chunk r + 1 - s; mirrored: chunk r - 1 + s)
+//   Tree level k, pair q, r = q * 2^(k+1): reduce adds rank r + 2^k into rank r;
+//     broadcast copies rank r over rank r + 2^k; whole buffers.
+__device__ __forceinline__ Seg step_segment(const StepArgs& a, int step, int seg) {
+  Seg g;
+  const int p = a.p;
+  if (a.mode == kModeTree) {
+    const bool reduce = step < a.levels;
+    const int k = reduce ? step : 2 * a.levels - 1 - step;
+    const int r = seg * (2 << k);
+    g.lo = 0;
+    g.hi = a.n;
+    g.add = reduce;
+    g.src = reduce ? r + (1 << k) : r;
+    g.dst = reduce ? r : r + (1 << k);
+    return g;
+  }
+  const int h = seg >= p ? 1 : 0;
+  const int c = seg - h * p;
+  const int d = h ? -1 : 1;
+  g.lo = chunk_lo(a.half[h], c);
+  g.hi = chunk_hi(a.half[h], c);
+  if (step < p - 1) {
+    const int s = step;
+    g.src = mod_p(c + d * s, p);
+    g.dst = mod_p(c + d * (s + 1), p);
+    g.add = true;
+  } else {
+    const int s = step - (p - 1);
+    g.src = mod_p(c + d * (s - 1), p);
+    g.dst = mod_p(c + d * s, p);
+    g.add = false;
+  }
+  return g;
+}
+
+template <int DT, int U>
+__global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
+  if (ws_failed(a.ws)) return;
+  const uint32_t nb = gridDim.x;
+  if (a.step_ts && blockIdx.x == 0 && threadIdx.x == 0) a.step_ts[0] = now_ticks();
+  uint32_t extra = a.expect_extra;
+  for (int step = a.step_begin; step < a.step_end; ++step) {
+    const int64_t ntiles = (int64_t)step_segments(a, step) * a.T;
+    for (int64_t t = blockIdx.x; t < ntiles; t += nb) {
+      const int seg = (int)(t / a.T);
+      const int64_t j = t - (int64_t)seg * a.T;
+      const Seg g = step_segment(a, step, seg);
+      if (g.add)
+        hop_tile<DT, U, true>(a.P.b[g.src], a.P.b[g.dst], g.lo, g.hi, j);
+      else
+        hop_tile<DT, U, false>(a.P.b[g.src], a.P.b[g.dst], g.lo, g.hi, j);
+    }
+    const bool last = step + 1 == a.step_end;
+    if (!last || a.step_ts || extra) {
+      if (!grid_barrier(a.ws, nb, extra, a.limit)) return;
+      extra = 0;
+      if (a.step_ts && blockIdx.x == 0 && threadIdx.x == 0)
+        a.step_ts[step - a.step_begin + 1] = now_ticks();
+    }
+  }
+}
+
+// ================================================================ pipelined
+
+struct PipeArgs {
+  RankPtrs P;
+  ChunkGeo g;
+  int64_t slice;        // elements per slice (multiple of the vector width)
+  int64_t kmax;         // flag entries per chunk
+  uint32_t* flags;      // flags[c * kmax + k]: hops finished on slice k of chunk c, + base
+  WsHeader* ws;
+  uint64_t limit;
+  int p, workers, hop_begin, hop_end;
+  uint32_t base, expect_extra;
+};
+
+// Slices of chunk [lo, hi): slice 0 starts at lo, later slices start at
+// A + k*slice with A = lo rounded up to a whole vector, the last ends at hi.
+template <int V>
+__device__ __forceinline__ int64_t n_slices(int64_t lo, int64_t hi, int64_t slice) {
+  const int64_t A = (lo + V - 1) / V * V;
+  if (A >= hi) return 1;
+  const int64_t k = (hi - A + slice - 1) / slice;
+  return k < 1 ? 1 : k;
+}
+
+// Workgroup (d, w) plays rank d: for each hop h it receives chunk c from rank
+// d-1 (reduce-scatter hop s: c = d-1-s, add; all-gather hop s: c = d-s, copy),
+// slice by slice (slices k = w, w + W, ...).  Slice k of chunk c may take hop h
+// once its counter says hops 0..h-1 are done, i.e. once rank d-1 has finished
+// with it; afterwards the counter is advanced for rank d+1.  Every dependency
+// points to an earlier hop of the same slice, handled by workgroup (d-1, w), and
+// every workgroup takes its hops in increasing order, so with all workgroups
+// resident the chain always progresses.
+template <int DT, int U>
+__global__ __launch_bounds__(kBlock) void k_pipelined(PipeArgs a) {
+  typedef Elem<DT> E;
+  constexpr int V = E::V;
+  if (ws_failed(a.ws)) return;
+  const int p = a.p;
+  const int d = blockIdx.x / a.workers;
+  const int w = blockIdx.x - d * a.workers;
+  const int left = d == 0 ? p - 1 : d - 1;
+  const void* src = a.P.b[left];
+  void* dst = a.P.b[d];
+  uint32_t extra = a.expect_extra;
+  for (int h = a.hop_begin; h < a.hop_end; ++h) {
+    const bool rs = h < p - 1;
+    const int s = rs ? h : h - (p - 1);
+    const int c = mod_p(rs ? d - 1 - s : d - s, p);
+    const int64_t lo = chunk_lo(a.g, c), hi = chunk_hi(a.g, c);
+    const int64_t K = n_slices<V>(lo, hi, a.slice);
+    const int64_t A = (lo + V - 1) / V * V;
+    const uint32_t done = a.base + (uint32_t)(h - a.hop_begin);
+    for (int64_t k = w; k < K; k += a.workers) {
+      uint32_t* f = a.flags + (int64_t)c * a.kmax + k;
+      // the first hop reads untouched inputs and depends on nothing; counters
+      // left by earlier calls are all below `base`, so it must not wait
+      if (h > a.hop_begin || extra) {
+        if (!wait_flag(a.ws, f, done + extra, a.limit)) return;
+        extra = 0;
+      }
+      const int64_t slo = k == 0 ? lo : A + k * a.slice;
+      const int64_t shi = k == K - 1 ? hi : A + (k + 1) * a.slice;
+      const Span sp = split_span<V>(slo, shi);
+      const int64_t tv = (int64_t)kBlock * U;
+      for (int64_t j = 0; sp.v0 + j * tv < sp.v1 || j == 0; ++j) {
+        if (rs)
+          hop_tile<DT, U, true>(src, dst, slo, shi, j);
+        else
+          hop_tile<DT, U, false>(src, dst, slo, shi, j);
+      }
+      post_flag(f, done + 1);
+    }
+  }
+}
+
+// ================================================================ copy
+
+__global__ __launch_bounds__(kBlock) void k_copy(u32x4* __restrict__ dst,
+                                                 const u32x4* __restrict__ src, int64_t nvec) {
+  constexpr int U = 4;
+  const int64_t stride = (int64_t)gridDim.x * kBlock * U;
+  for (int64_t base = (int64_t)blockIdx.x * kBlock * U; base < nvec; base += stride) {
+    u32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = base + u * kBlock + threadIdx.x;
+      if (v < nvec) x[u] = src[v];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = base + u * kBlock + threadIdx.x;
+      if (v < nvec) dst[v] = x[u];
+    }
+  }
+}
+
+// ================================================================ launchers
+
+static constexpr int kFusedU = 2;
+static constexpr int kStepU = 2;
+static constexpr int kPipeU = 2;
+static constexpr int64_t kMaxGrid = 1 << 22;     // non-persistent grids; beyond, blocks loop
+
+static hipError_t device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::unordered_map<int, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) { *cus = it->second; return hipSuccess; }
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) cache[dev] = *cus;
+  return e;
+}
+
+// Workgroups per CU that persistent kernels rely on being co-resident.  The
+// occupancy query (and the cooperative-launch check built on it) counts vector
+// registers but not the scalar-register budget: kernels using ~100 SGPRs per
+// wave fit only 7 waves per SIMD on gfx950 while the query reports 8, so a
+// grid sized from the query can leave workgroups waiting for a slot that never
+// frees (measured: 2043 workgroups of the pipelined kernel stall, 576 do not).
+// Four workgroups of 256 threads put 4 waves on each SIMD, which fits any wave
+// using <= 128 VGPRs whatever its SGPR count; every kernel here uses < 64.
+static constexpr int kPersistentPerCU = 4;
+
+// Workgroups of `func` that can be resident at once on the current device.
+static hipError_t resident_blocks(const void* func, int* out) {
+  int cus = 0;
+  hipError_t e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, func, kBlock, 0);
+  if (e != hipSuccess) return e;
+  *out = std::max(1, std::min(per_cu, kPersistentPerCU)) * cus;
+  return hipSuccess;
+}
+
+template <int DT>
+static hipError_t fused_dt(const RankPtrs& P, int p, int64_t n, hipStream_t s, int* grid_used) {
+  const int V = Elem<DT>::V;
+  const ChunkGeo g = make_geo(0, n, p);
+  int64_t T = 1;
+  for (int c = 0; c < p; ++c) {
+    const int64_t lo = host_chunk_lo(0, n, p, c), hi = host_chunk_lo(0, n, p, c + 1);
+    T = std::max<int64_t>(T, (vecs_in(lo, hi, V) + (int64_t)kBlock * kFusedU - 1) /
+                                 ((int64_t)kBlock * kFusedU));
+  }
+  const int64_t ntiles = (int64_t)p * T;
+  const int grid = (int)std::min<int64_t>(ntiles, kMaxGrid);
+  *grid_used = grid;
+  hipLaunchKernelGGL((k_fused<DT, kFusedU>), dim3(grid), dim3(kBlock), 0, s, P, g, p, T, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, hipStream_t s,
+                        int* grid_used) {
+  switch (dtype) {
+    case 0: return fused_dt<0>(P, p, n, s, grid_used);
+    case 1: return fused_dt<1>(P, p, n, s, grid_used);
+    default: return fused_dt<2>(P, p, n, s, grid_used);
+  }
+}
+
+template <int DT>
+static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, int step_begin,
+                           int step_end, const SyncCfg& sc, hipStream_t s, int* grid_used) {
+  const int V = Elem<DT>::V;
+  StepArgs a;
+  a.P = P;
+  a.n = n;
+  a.ws = sc.ws;
+  a.step_ts = sc.step_ts;
+  a.limit = sc.limit_ticks;
+  a.p = p;
+  a.mode = mode;
+  a.step_begin = step_begin;
+  a.step_end = step_end;
+  a.expect_extra = sc.expect_extra;
+  a.levels = 0;
+  while ((1 << a.levels) < p) ++a.levels;
+  // segment geometry and the widest segment in vectors
+  int64_t maxvec = 0;
+  if (mode == kModeTree) {
+    a.half[0] = a.half[1] = make_geo(0, n, p);
+    maxvec = vecs_in(0, n, V);
+  } else {
+    const int64_t len0 = mode == kModeBidir ? (n + 1) / 2 : n;
+    a.half[0] = make_geo(0, len0, p);
+    a.half[1] = make_geo(len0, n - len0, p);
+    const int nh = mode == kModeBidir ? 2 : 1;
+    for (int h = 0; h < nh; ++h) {
+      const int64_t off = h ? len0 : 0, len = h ? n - len0 : len0;
+      for (int c = 0; c < p; ++c)
+        maxvec = std::max(maxvec, vecs_in(host_chunk_lo(off, len, p, c),
+                                          host_chunk_lo(off, len, p, c + 1), V));
+    }
+  }
+  const int64_t tv = (int64_t)kBlock * kStepU;
+  a.T = std::max<int64_t>(1, (maxvec + tv - 1) / tv);
+  // most tiles any step has
+  int64_t most = 0;
+  for (int st = step_begin; st < step_end; ++st) {
+    int nseg;
+    if (mode == kModeTree) {
+      const int k = st < a.levels ? st : 2 * a.levels - 1 - st;
+      nseg = (p - 1 - (1 << k)) / (2 << k) + 1;
+    } else {
+      nseg = mode == kModeBidir ? 2 * p : p;
+    }
+    most = std::max(most, (int64_t)nseg * a.T);
+  }
+  const void* func = reinterpret_cast<const void*>(&k_steps<DT, kStepU>);
+  int resident = 0;
+  hipError_t e = resident_blocks(func, &resident);
+  if (e != hipSuccess) return e;
+  int grid = sc.grid > 0 ? std::min(sc.grid, resident) : resident;
+  grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, most));
+  *grid_used = grid;
+  void* args[] = {&a};
+  return hipLaunchCooperativeKernel(func, dim3(grid), dim3(kBlock), args, 0, s);
+}
+
+hipError_t launch_steps(const RankPtrs& P, int p, int64_t n, int dtype, StepMode mode,
+                        int step_begin, int step_end, const SyncCfg& sc, hipStream_t s,
+                        int* grid_used) {
+  switch (dtype) {
+    case 0: return steps_dt<0>(P, p, n, mode, step_begin, step_end, sc, s, grid_used);
+    case 1: return steps_dt<1>(P, p, n, mode, step_begin, step_end, sc, s, grid_used);
+    default: return steps_dt<2>(P, p, n, mode, step_begin, step_end, sc, s, grid_used);
+  }
+}
+
+int64_t pipelined_slices_per_chunk(int p, int64_t n, int dtype, int64_t slice) {
+  const int V = elems_per_vec(dtype);
+  int64_t kmax = 1;
+  for (int c = 0; c < p; ++c) {
+    const int64_t lo = host_chunk_lo(0, n, p, c), hi = host_chunk_lo(0, n, p, c + 1);
+    const int64_t A = (lo + V - 1) / V * V;
+    int64_t k = 1;
+    if (A < hi) k = std::max<int64_t>(1, (hi - A + slice - 1) / slice);
+    kmax = std::max(kmax, k);
+  }
+  return kmax;
+}
+
+template <int DT>
+static hipError_t pipelined_dt(const RankPtrs& P, int p, int64_t n, int hop_begin, int hop_end,
+                               int64_t slice, int64_t kmax, uint32_t* flags, uint32_t base,
+                               const SyncCfg& sc, hipStream_t s, int* grid_used) {
+  PipeArgs a;
+  a.P = P;
+  a.g = make_geo(0, n, p);
+  a.slice = slice;
+  a.kmax = kmax;
+  a.flags = flags;
+  a.ws = sc.ws;
+  a.limit = sc.limit_ticks;
+  a.p = p;
+  a.hop_begin = hop_begin;
+  a.hop_end = hop_end;
+  a.base = base;
+  a.expect_extra = sc.expect_extra;
+  const void* func = reinterpret_cast<const void*>(&k_pipelined<DT, kPipeU>);
+  int resident = 0;
+  hipError_t e = resident_blocks(func, &resident);
+  if (e != hipSuccess) return e;
+  int budget = sc.grid > 0 ? std::min(sc.grid, resident) : resident;
+  int workers = (int)std::max<int64_t>(1, std::min<int64_t>(budget / p, kmax));
+  if (workers * p > resident) return hipErrorCooperativeLaunchTooLarge;
+  a.workers = workers;
+  *grid_used = workers * p;
+  void* args[] = {&a};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(func), dim3(workers * p),
+                                    dim3(kBlock), args, 0, s);
+}
+
+hipError_t launch_pipelined(const RankPtrs& P, int p, int64_t n, int dtype, int hop_begin,
+                            int hop_end, int64_t slice, int64_t kmax, uint32_t* flags,
+                            uint32_t base, const SyncCfg& sc, hipStream_t s, int* grid_used) {
+  switch (dtype) {
+    case 0: return pipelined_dt<0>(P, p, n, hop_begin, hop_end, slice, kmax, flags, base, sc, s, grid_used);
+    case 1: return pipelined_dt<1>(P, p, n, hop_begin, hop_end, slice, kmax, flags, base, sc, s, grid_used);
+    default: return pipelined_dt<2>(P, p, n, hop_begin, hop_end, slice, kmax, flags, base, sc, s, grid_used);
+  }
+}
+
+hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s) {
+  const int64_t nvec = bytes / 16;
+  if (nvec == 0) return hipSuccess;
+  const int64_t per = (int64_t)kBlock * 4;
+  const int grid = (int)std::min<int64_t>((nvec + per - 1) / per, kMaxGrid);
+  hipLaunchKernelGGL(k_copy, dim3(grid), dim3(kBlock), 0, s, reinterpret_cast<u32x4*>(dst),
+                     reinterpret_cast<const u32x4*>(src), nvec);
+  return hipGetLastError();
+}
+
+}  // namespace ra

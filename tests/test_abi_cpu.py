@@ -1,0 +1,102 @@
+"""Host-side checks of libra.so that need no GPU: it loads, exports every symbol
+include/ra.h declares, and its host logic (chunk partition, argument checks)
+agrees with the oracle and the header's contract.  No call here reaches a kernel."""
+
+import ctypes
+import os
+
+import pytest
+
+import oracle
+from ring_all_reduce_schedule_amd import binding as B
+
+
+def test_library_exports_every_header_symbol():
+    names = B.header_symbols()
+    assert len(names) >= 12
+    lib = B.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+    # and the binding wraps each of them under the same name
+    for name in names:
+        assert name in B._SIGNATURES, name
+        assert hasattr(B, name), name
+
+
+@pytest.mark.parametrize("n,p", [(n, p) for p in (1, 2, 3, 4, 8, 9, 64)
+                                 for n in (0, 1, 3, 4, 63, 64, 65, 1000, 1_000_003,
+                                           67_108_864, 8_000_000_000, 2**40 + 7)])
+def test_chunk_bounds_matches_oracle(n, p):
+    starts = B.ra_chunk_bounds(n, p)
+    assert [(starts[i], starts[i + 1]) for i in range(p)] == oracle.chunk_bounds(n, p)
+
+
+def test_chunk_bounds_errors():
+    for n, p, code in [(4, 0, B.RA_ERR_INVALID_ARG), (-1, 4, B.RA_ERR_INVALID_ARG),
+                       (4, 65, B.RA_ERR_UNSUPPORTED)]:
+        with pytest.raises(B.RaError) as e:
+            B.ra_chunk_bounds(n, p)
+        assert e.value.code == code
+    assert B.lib().ra_chunk_bounds(4, 2, None) == B.RA_ERR_INVALID_ARG
+
+
+def _ptrs(addrs):
+    return (ctypes.c_void_p * len(addrs))(*addrs)
+
+
+def _call(addrs, n, dtype=B.RA_FLOAT32, op=B.RA_SUM, algo=-1, p=None):
+    lib = B.lib()
+    p = len(addrs) if p is None else p
+    return lib.ra_allreduce_ex(_ptrs(addrs) if addrs is not None else None, p, n, dtype, op,
+                               algo, None, None)
+
+
+MiB = 1 << 20
+
+
+def test_argument_errors_are_reported_before_any_gpu_work():
+    base = 0x7f0000000000
+    ok = [base + i * MiB for i in range(4)]
+    assert _call(None, 16, p=4) == B.RA_ERR_INVALID_ARG
+    assert _call(ok, 16, p=0) == B.RA_ERR_INVALID_ARG
+    assert _call(ok, -1) == B.RA_ERR_INVALID_ARG
+    assert _call(ok, 16, dtype=7) == B.RA_ERR_INVALID_ARG
+    assert _call(ok, 16, op=1) == B.RA_ERR_UNSUPPORTED
+    assert _call(ok, 16, algo=9) == B.RA_ERR_INVALID_ARG
+    assert _call([base + i * MiB for i in range(65)], 16) == B.RA_ERR_UNSUPPORTED
+    assert _call([ok[0], 0, ok[2], ok[3]], 16) == B.RA_ERR_INVALID_ARG
+    assert _call([ok[0], ok[1] + 8, ok[2], ok[3]], 16) == B.RA_ERR_MISALIGNED
+    # 16 float32 = 64 bytes: buffers 32 bytes apart overlap
+    assert _call([base, base + 32, base + 4096, base + 8192], 16) == B.RA_ERR_ALIAS
+    assert "overlap" in B.ra_last_error()
+    # ... 64 bytes apart do not (and n = 0 never touches the device)
+    assert _call([base, base + 64, base + 128, base + 192], 0) == B.RA_OK
+    # a world of one is a no-op
+    assert _call([base], 1 << 20) == B.RA_OK
+    # empty buffers may be NULL (nothing is read or written)
+    assert _call([0, 0, 0], 0) == B.RA_OK
+    lib = B.lib()
+    assert lib.ra_reduce_scatter_ex(_ptrs(ok), 4, 16, 0, 0, B.ALGOS["tree"], None, None) == B.RA_ERR_UNSUPPORTED
+    assert lib.ra_all_gather_ex(_ptrs(ok), 4, 16, 0, B.ALGOS["fused"], None, None) == B.RA_ERR_UNSUPPORTED
+    assert lib.ra_stream_copy(None, None, 16, None) == B.RA_ERR_INVALID_ARG
+    assert lib.ra_stream_copy(base, base + 4096, 15, None) == B.RA_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    names = ["RA_OK", "RA_ERR_INVALID_ARG", "RA_ERR_UNSUPPORTED", "RA_ERR_ALIAS",
+             "RA_ERR_MISALIGNED", "RA_ERR_HIP", "RA_ERR_TIMEOUT"]
+    assert [B.ra_status_string(i) for i in range(7)] == names
+    assert B.ra_status_string(99) == "RA_ERR_UNKNOWN"
+
+
+def test_options_struct_layout():
+    # int64, int64, int32, uint32, pointer: 32 bytes with no padding
+    assert ctypes.sizeof(B.ra_options) == 32
+    assert B.ra_options.step_ts.offset == 24
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        B.lib()
