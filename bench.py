@@ -1,0 +1,348 @@
+#!/usr/bin/env python3
+"""Benchmark: effective all-reduce bandwidth of the ring schedule on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--algo ALGO]
+
+One "step" is one all-reduce of the workload's p rank buffers (all resident in
+HBM before timing starts) through the C ABI (ra_allreduce_ex).  The default
+workload is p8_bf16_16GB: 8 virtual ranks x 8e9 bf16 elements (16 GB per rank,
+128 GB in all), drawn on the device.  The figure of merit is the effective
+bandwidth on the least traffic any one-GPU all-reduce needs, 2*p*S bytes (every
+rank buffer read once and written once), against the 8 TB/s HBM3E peak.
+
+Prints ONE JSON line.  Besides the driver's fields it carries
+  roofline      the all-reduce kernel's achieved bytes/s vs the HBM peak, its
+                launch duration from HIP events on the launch stream, and the
+                HBM traffic read from the committed rocprofv3 counter summary
+                (null when that summary was taken on different kernel source)
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+  variants      the other algorithms on the same buffers
+  alpha         per-step latency of the step-by-step ring, from in-kernel
+                timestamps and from a fit of T = 2(p-1)a + 2(p-1)/p*S/B
+  ceiling       a plain copy of the same byte count (read + write)
+
+Buffers are all-reduced in place, so values grow by about p per call; the
+default step counts stay far from bf16 overflow and inputs are redrawn before
+the variant timings.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("effective all-reduce GB/s & % of HBM peak per S,p on 1 MI355X; "
+          "per-step α (µs)")
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_p8_bf16_16GB_hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "ring_all_reduce_schedule_amd", "csrc", f)
+                  for f in ("ra_kernels.hip", "ra_device.h")]
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="p8_bf16_16GB")
+    ap.add_argument("--algo", default="fused")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip variants, alpha, ceiling (profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 27,
+                    help="elements per rank of the CPU-oracle sample")
+    ap.add_argument("--mode", default="allreduce", choices=["allreduce", "copy"],
+                    help="copy: only the plain copy kernel, for counter calibration")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def alloc_workload(name, torch, B, inputs):
+    w = inputs.WORKLOADS[name]
+    p, n, dtype = w["p"], w["n"], w["dtype"]
+    tdt = {"int32": torch.int32, "float32": torch.float32, "bfloat16": torch.bfloat16}[dtype]
+    bufs = [torch.empty(n, dtype=tdt, device="cuda") for _ in range(p)]
+    fill_workload(name, bufs, torch, inputs)
+    return w, bufs
+
+
+def fill_workload(name, bufs, torch, inputs):
+    w = inputs.WORKLOADS[name]
+    if w.get("on_device"):
+        inputs.device_normal_bf16(bufs, w["sigma"], w["seed"])
+    else:
+        import numpy as np
+        for b, x in zip(bufs, inputs.workload_inputs(name)):
+            if w["dtype"] == "bfloat16":
+                b.copy_(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16))
+            else:
+                b.copy_(torch.from_numpy(x))
+    torch.cuda.synchronize()
+
+
+def time_calls(fn, k, torch):
+    """Per-call durations (ms) from HIP events on the current stream, plus the
+    span from the first start to the last end."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+    torch.cuda.synchronize()
+    for i in range(k):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    span = starts[0].elapsed_time(ends[-1])
+    return per, span
+
+
+def read_traffic(sha, launch_bytes):
+    """HBM bytes per launch from the committed counter summary, if it matches."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    text = open(TRAFFIC_SUMMARY).read()
+    m_sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_wb = re.search(r"workload_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_b and m_wb) or m_sha.group(1) != sha:
+        return None
+    if abs(float(m_wb.group(1)) - launch_bytes) > 1:
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(bufs, w, sample, torch):
+    """The oracle (lock-step ring simulator) on the first `sample` elements of each rank."""
+    import numpy as np
+    import oracle
+    p = w["p"]
+    m = min(sample, w["n"])
+    xs = []
+    for b in bufs:
+        t = b[:m].cpu()
+        if w["dtype"] == "bfloat16":
+            xs.append(t.view(torch.int16).numpy().view(np.uint16).copy())
+        else:
+            xs.append(t.numpy().copy())
+    item = {"int32": 4, "float32": 4, "bfloat16": 2}[w["dtype"]]
+    t0 = time.perf_counter()
+    oracle.ring_allreduce(xs, w["dtype"])
+    dt = time.perf_counter() - t0
+    gbps = 2 * p * m * item / dt / 1e9
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 3), "host_cores_available": avail,
+            "sample": (f"lock-step oracle (numpy, one thread) all-reducing the first {m:,} "
+                       f"elements of each of the {p} rank buffers of the workload "
+                       f"(p={p}, N={m:,} {w['dtype']}); rate on 2*p*S of that sample")}
+
+
+def alpha_measure(torch, B, inputs):
+    """Per-step latency of the step-by-step ring.
+
+    (1) in-kernel: device wall-clock stamps as each step's grid barrier
+        releases, tiny buffers (p=64, 1 KiB per rank): median step time.
+    (2) fit: T(S) = 2(p-1) a + 2(p-1)/p * S / B over S/p from 4 KiB to 4 MiB at
+        p=8 and p=64 (bf16), least squares per p.
+    """
+    import numpy as np
+    hz = B.ra_wallclock_hz()
+    out = {}
+    p = 64
+    n = 512
+    bufs = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    ts = torch.zeros(2 * (p - 1) + 1, dtype=torch.int64, device="cuda")
+    steps = []
+    for _ in range(5):
+        B.ra_allreduce_ex(bufs, algo="ring_step", step_ts=ts)
+        B.ra_stream_status()
+        v = ts.cpu().numpy().astype(np.float64)
+        steps.append(np.diff(v) / hz * 1e6)
+    out["in_kernel_step_us_p64_1KiB"] = round(float(np.median(np.concatenate(steps))), 3)
+    fits = {}
+    for p in (8, 64):
+        xs, ys, ts_tree = [], [], []
+        for per_rank in (4 << 10, 64 << 10, 1 << 20, 4 << 20):
+            n = per_rank // 2
+            bufs = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+            per, _ = time_calls(lambda: B.ra_allreduce_ex(bufs, algo="ring_step"), 7, torch)
+            t_ring = float(np.median(per[2:])) * 1e-3
+            per, _ = time_calls(lambda: B.ra_allreduce_ex(bufs, algo="tree"), 7, torch)
+            t_tree = float(np.median(per[2:])) * 1e-3
+            xs.append(2 * (p - 1) / p * per_rank)
+            ys.append(t_ring)
+            ts_tree.append((per_rank, t_ring, t_tree))
+            del bufs
+        A = np.stack([np.full(len(xs), 2.0 * (p - 1)), np.array(xs)], axis=1)
+        (a, inv_b), *_ = np.linalg.lstsq(A, np.array(ys), rcond=None)
+        cross = None
+        for per_rank, tr, tt in ts_tree:
+            if tt < tr:
+                cross = per_rank
+        fits[f"p{p}"] = {"alpha_us": round(a * 1e6, 3),
+                         "B_GBps_per_rank": round(1.0 / inv_b / 1e9, 2) if inv_b > 0 else None,
+                         "ring_vs_tree_ms": [(pr, round(tr * 1e3, 4), round(tt * 1e3, 4))
+                                             for pr, tr, tt in ts_tree],
+                         "largest_S_per_rank_where_tree_wins": cross}
+    out["fit"] = fits
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs the ring "
+              "schedule's p virtual ranks inside ONE GPU's HBM; nothing crosses GPUs, so "
+              "only --gpus 1 is measured.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from ring_all_reduce_schedule_amd import binding as B
+    from ring_all_reduce_schedule_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    B.lib()   # fails loudly if libra.so is missing
+    torch.cuda.set_device(0)
+
+    if args.mode == "copy":
+        # counter calibration: one plain copy of 2 x 16 GiB traffic
+        nbytes = 16 << 30
+        src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(2):
+            B.ra_stream_copy(dst, src)
+        per, _ = time_calls(lambda: B.ra_stream_copy(dst, src), 3, torch)
+        print(json.dumps({"mode": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                          "ms": [round(x, 3) for x in per],
+                          "GBps": round(2 * nbytes / (min(per) * 1e-3) / 1e9, 1)}), flush=True)
+        return
+
+    log(f"allocating workload {args.workload}")
+    w, bufs = alloc_workload(args.workload, torch, B, inputs)
+    p, n, dtype = w["p"], w["n"], w["dtype"]
+    item = inputs.ITEMSIZE[dtype]
+    S = n * item
+    min_bytes = 2 * p * S
+
+    def step():
+        B.ra_allreduce_ex(bufs, algo=args.algo)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    B.ra_stream_status()
+    # outputs of every rank must agree bit for bit
+    for r in range(1, p):
+        a, b = bufs[0], bufs[r]
+        if dtype == "bfloat16":
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        if not torch.equal(a, b):
+            raise SystemExit(f"rank {r} differs from rank 0 after the all-reduce")
+
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    per, span = time_calls(step, args.steps, torch)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    B.ra_stream_status()
+    ms_per_step = span / args.steps
+    value = min_bytes / (ms_per_step * 1e-3) / 1e9
+    launch_ms = sum(per) / len(per)
+    achieved = min_bytes / (launch_ms * 1e-3) / 1e9
+    sha = kernel_source_sha()
+    traffic = read_traffic(sha, min_bytes)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bfloat16": "bf16", "float32": "f32", "int32": "int32"}[dtype],
+        "data": "synthetic (seeded normal/uniform draws, generated in HBM or on the host)",
+        "config": {"workload": args.workload, "p": p, "n_per_rank": n,
+                   "bytes_per_rank": S, "algo": args.algo,
+                   "bytes_counted": "2*p*S (each rank buffer read once and written once)",
+                   "bytes_per_step": min_bytes},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": f"ra::k_fused<{dtype}>" if args.algo == "fused" else args.algo,
+                     "launch_ms_mean": round(launch_ms, 4),
+                     "launch_ms_min": round(min(per), 4),
+                     "kernel_source_sha": sha},
+        "wall_s_timed": round(wall, 3),
+    }
+
+    if not args.no_extras:
+        log("variants")
+        fill_workload(args.workload, bufs, torch, inputs)
+        variants = {}
+        for algo in ("ring_step", "ring_pipelined", "ring_bidir", "tree"):
+            fn = lambda a=algo: B.ra_allreduce_ex(bufs, algo=a)
+            fn()
+            B.ra_stream_status()
+            vper, _ = time_calls(fn, 3, torch)
+            B.ra_stream_status()
+            t = sum(vper) / len(vper)
+            variants[algo] = {"ms": round(t, 3), "GBps_on_2pS": round(min_bytes / (t * 1e-3) / 1e9, 1)}
+        result["variants"] = variants
+        log("copy ceiling")
+        # the same byte count as the all-reduce, read + write, through a plain copy
+        half = min_bytes // 2
+        chunk = min(half, 8 << 30)
+        src = bufs[0].view(torch.int16)[: chunk // 2]
+        dst = bufs[1].view(torch.int16)[: chunk // 2]
+        cper, _ = time_calls(lambda: B.ra_stream_copy(dst, src), 5, torch)
+        result["ceiling"] = {"kernel": "ra::k_copy", "bytes_moved": 2 * chunk,
+                             "GBps": round(2 * chunk / (min(cper) * 1e-3) / 1e9, 1)}
+        if "GBps" in result["ceiling"] and result["ceiling"]["GBps"]:
+            result["pct_of_copy_ceiling"] = round(100.0 * value / result["ceiling"]["GBps"], 2)
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        fill_workload(args.workload, bufs, torch, inputs)
+        result["cpu_baseline"] = cpu_baseline(bufs, w, args.cpu_sample, torch)
+
+    if not args.no_extras:
+        del bufs
+        torch.cuda.empty_cache()
+        log("alpha")
+        result["alpha"] = alpha_measure(torch, B, inputs)
+        result["alpha_us"] = result["alpha"]["in_kernel_step_us_p64_1KiB"]
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -104,11 +104,19 @@ template <> struct Elem<2> {
 
 // ---------------------------------------------------------------- memory access
 
+// NT = true marks the access non-temporal (streaming): used when the buffers are
+// far larger than the 256 MB Infinity Cache, so nothing would be re-read from it.
+template <bool NT = false>
 __device__ __forceinline__ u32x4 ld16(const void* base, int64_t vec) {
-  return reinterpret_cast<const u32x4*>(base)[vec];
+  const u32x4* p = reinterpret_cast<const u32x4*>(base) + vec;
+  if (NT) return __builtin_nontemporal_load(p);
+  return *p;
 }
+template <bool NT = false>
 __device__ __forceinline__ void st16(void* base, int64_t vec, u32x4 v) {
-  reinterpret_cast<u32x4*>(base)[vec] = v;
+  u32x4* p = reinterpret_cast<u32x4*>(base) + vec;
+  if (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
 }
 template <int DT>
 __device__ __forceinline__ typename Elem<DT>::S ld1(const void* base, int64_t i) {

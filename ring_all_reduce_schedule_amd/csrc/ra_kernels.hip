@@ -63,7 +63,7 @@ static ChunkGeo make_geo(int64_t off, int64_t len, int p) {
 // Tile j of the segment [lo, hi): dst[i] = dst[i] + src[i] (ADD) or dst[i] = src[i].
 // A tile covers kBlock*U consecutive vectors; tile 0 also takes the scalar
 // head and tail of the segment.
-template <int DT, int U, bool ADD>
+template <int DT, int U, bool ADD, bool NT>
 __device__ __forceinline__ void hop_tile(const void* __restrict__ src, void* __restrict__ dst,
                                          int64_t lo, int64_t hi, int64_t j) {
   typedef Elem<DT> E;
@@ -79,13 +79,13 @@ __device__ __forceinline__ void hop_tile(const void* __restrict__ src, void* __r
     for (int u = 0; u < U; ++u) {
       v[u] = t0 + u * kBlock + threadIdx.x;
       if (v[u] < t1) {
-        a[u] = ld16(src, v[u]);
-        if (ADD) b[u] = ld16(dst, v[u]);
+        a[u] = ld16<NT>(src, v[u]);
+        if (ADD) b[u] = ld16<NT>(dst, v[u]);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (v[u] < t1) st16(dst, v[u], ADD ? E::add(b[u], a[u]) : a[u]);
+      if (v[u] < t1) st16<NT>(dst, v[u], ADD ? E::add(b[u], a[u]) : a[u]);
   }
   if (j == 0) {
     const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
@@ -104,7 +104,7 @@ __device__ __forceinline__ void hop_tile(const void* __restrict__ src, void* __r
 // acc = x_c; acc = acc + x_{c+1}; ...; acc = acc + x_{c+p-1} (indices mod p,
 // rounding each addition), then acc is stored to every rank.  This is the
 // order in which the step-by-step ring accumulates chunk c, so the bits match.
-template <int DT, int U>
+template <int DT, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p, int64_t T,
                                                   int64_t ntiles) {
   typedef Elem<DT> E;
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         v[u] = t0 + u * kBlock + threadIdx.x;
-        if (v[u] < t1) acc[u] = ld16(first, v[u]);
+        if (v[u] < t1) acc[u] = ld16<NT>(first, v[u]);
       }
       for (int k0 = 1; k0 < p; k0 += KB) {
         u32x4 x[KB][U];
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
             const void* src = P.b[r];
 #pragma unroll
             for (int u = 0; u < U; ++u)
-              if (v[u] < t1) x[i][u] = ld16(src, v[u]);
+              if (v[u] < t1) x[i][u] = ld16<NT>(src, v[u]);
           }
         }
 #pragma unroll
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
         void* dst = P.b[r];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          if (v[u] < t1) st16(dst, v[u], acc[u]);
+          if (v[u] < t1) st16<NT>(dst, v[u], acc[u]);
       }
     }
     if (j == 0) {
@@ -241,7 +241,7 @@ __device__ __forceinline__ Seg step_segment(const StepArgs& a, int step, int seg
   return g;
 }
 
-template <int DT, int U>
+template <int DT, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
   if (ws_failed(a.ws)) return;
   const uint32_t nb = gridDim.x;
@@ -254,9 +254,9 @@ __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
       const int64_t j = t - (int64_t)seg * a.T;
       const Seg g = step_segment(a, step, seg);
       if (g.add)
-        hop_tile<DT, U, true>(a.P.b[g.src], a.P.b[g.dst], g.lo, g.hi, j);
+        hop_tile<DT, U, true, NT>(a.P.b[g.src], a.P.b[g.dst], g.lo, g.hi, j);
       else
-        hop_tile<DT, U, false>(a.P.b[g.src], a.P.b[g.dst], g.lo, g.hi, j);
+        hop_tile<DT, U, false, NT>(a.P.b[g.src], a.P.b[g.dst], g.lo, g.hi, j);
     }
     const bool last = step + 1 == a.step_end;
     if (!last || a.step_ts || extra) {
@@ -300,7 +300,7 @@ __device__ __forceinline__ int64_t n_slices(int64_t lo, int64_t hi, int64_t slic
 // points to an earlier hop of the same slice, handled by workgroup (d-1, w), and
 // every workgroup takes its hops in increasing order, so with all workgroups
 // resident the chain always progresses.
-template <int DT, int U>
+template <int DT, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void k_pipelined(PipeArgs a) {
   typedef Elem<DT> E;
   constexpr int V = E::V;
@@ -334,9 +334,9 @@ __global__ __launch_bounds__(kBlock) void k_pipelined(PipeArgs a) {
       const int64_t tv = (int64_t)kBlock * U;
       for (int64_t j = 0; sp.v0 + j * tv < sp.v1 || j == 0; ++j) {
         if (rs)
-          hop_tile<DT, U, true>(src, dst, slo, shi, j);
+          hop_tile<DT, U, true, NT>(src, dst, slo, shi, j);
         else
-          hop_tile<DT, U, false>(src, dst, slo, shi, j);
+          hop_tile<DT, U, false, NT>(src, dst, slo, shi, j);
       }
       post_flag(f, done + 1);
     }
@@ -366,9 +366,22 @@ __global__ __launch_bounds__(kBlock) void k_copy(u32x4* __restrict__ dst,
 
 // ================================================================ launchers
 
-static constexpr int kFusedU = 2;
+// Vectors per thread.  Measured on MI355X at 8 x 16 GiB bf16: one vector per
+// thread with the most workgroups in flight streams best (6.40 TB/s on 2pS
+// against 6.35 with two and 6.30 with four).
+static constexpr int kFusedU = 1;
 static constexpr int kStepU = 2;
 static constexpr int kPipeU = 2;
+
+// Buffers larger than this in total (p * S) are streamed with non-temporal
+// loads and stores: they are far beyond the 256 MB Infinity Cache, and the
+// streaming hint measured +3.7% for the fused kernel at 8 x 16 GiB.  Smaller
+// working sets keep normal caching so that repeated calls can hit the cache.
+static constexpr int64_t kStreamingBytes = 512ll << 20;
+
+static bool streaming(int p, int64_t n, int dtype) {
+  return (int64_t)p * n * elem_bytes(dtype) > kStreamingBytes;
+}
 static constexpr int64_t kMaxGrid = 1 << 22;     // non-persistent grids; beyond, blocks loop
 
 static hipError_t device_cus(int* cus) {
@@ -420,7 +433,10 @@ static hipError_t fused_dt(const RankPtrs& P, int p, int64_t n, hipStream_t s, i
   const int64_t ntiles = (int64_t)p * T;
   const int grid = (int)std::min<int64_t>(ntiles, kMaxGrid);
   *grid_used = grid;
-  hipLaunchKernelGGL((k_fused<DT, kFusedU>), dim3(grid), dim3(kBlock), 0, s, P, g, p, T, ntiles);
+  if (streaming(p, n, DT))
+    hipLaunchKernelGGL((k_fused<DT, kFusedU, true>), dim3(grid), dim3(kBlock), 0, s, P, g, p, T, ntiles);
+  else
+    hipLaunchKernelGGL((k_fused<DT, kFusedU, false>), dim3(grid), dim3(kBlock), 0, s, P, g, p, T, ntiles);
   return hipGetLastError();
 }
 
@@ -481,7 +497,8 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
     }
     most = std::max(most, (int64_t)nseg * a.T);
   }
-  const void* func = reinterpret_cast<const void*>(&k_steps<DT, kStepU>);
+  const void* func = streaming(p, n, DT) ? reinterpret_cast<const void*>(&k_steps<DT, kStepU, true>)
+                                         : reinterpret_cast<const void*>(&k_steps<DT, kStepU, false>);
   int resident = 0;
   hipError_t e = resident_blocks(func, &resident);
   if (e != hipSuccess) return e;
@@ -532,7 +549,9 @@ static hipError_t pipelined_dt(const RankPtrs& P, int p, int64_t n, int hop_begi
   a.hop_end = hop_end;
   a.base = base;
   a.expect_extra = sc.expect_extra;
-  const void* func = reinterpret_cast<const void*>(&k_pipelined<DT, kPipeU>);
+  const void* func = streaming(p, n, DT)
+                         ? reinterpret_cast<const void*>(&k_pipelined<DT, kPipeU, true>)
+                         : reinterpret_cast<const void*>(&k_pipelined<DT, kPipeU, false>);
   int resident = 0;
   hipError_t e = resident_blocks(func, &resident);
   if (e != hipSuccess) return e;
