@@ -41,8 +41,9 @@ METRIC = ("effective all-reduce GB/s & % of HBM peak per S,p on 1 MI355X; "
           "per-step α (µs)")
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "fused_p8_bf16_16GB_hbm_traffic.md")
+# the sources k_fused is compiled from: the traffic figure is valid only for them
 KERNEL_SOURCES = [os.path.join(ROOT, "ring_all_reduce_schedule_amd", "csrc", f)
-                  for f in ("ra_kernels.hip", "ra_device.h")]
+                  for f in ("ra_fused.hip", "ra_elem.h")]
 
 
 def kernel_source_sha():

@@ -84,7 +84,8 @@ typedef enum ra_algo {
                                      after timeout_us and every workgroup exits */
 
 typedef struct ra_options {
-  int64_t slice_elems;  /* RING_PIPELINED slice length in elements; 0 = library default.
+  int64_t slice_elems;  /* RING_PIPELINED slice length in elements; 0 = library default
+                           (about four slices per worker per hop, at least 64 KiB).
                            Rounded up to a multiple of 16 bytes. */
   int64_t timeout_us;   /* budget of any single device-side wait; 0 = 10 s */
   int32_t grid;         /* workgroups of persistent kernels; 0 = as many as fit the GPU */

@@ -20,8 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libra.so")
 
-SOURCES = ["ra_kernels.hip", "ra_api.cpp"]
-HEADERS = ["ra_device.h", "ra_internal.h"]
+SOURCES = ["ra_fused.hip", "ra_steps.hip", "ra_copy.hip", "ra_api.cpp"]
+HEADERS = ["ra_elem.h", "ra_sync.h", "ra_internal.h"]
 
 
 def hipcc():

@@ -15,7 +15,8 @@
 #include <utility>
 #include <vector>
 
-#include "ra_device.h"
+#include "ra_elem.h"
+#include "ra_sync.h"
 #include "ra_internal.h"
 
 namespace {
@@ -194,8 +195,6 @@ void debug_line(const char* call, int algo, int p, int64_t n, int dtype, int gri
   for (int r = 0; r < p; ++r) std::fprintf(stderr, "%d%s", r, r + 1 < p ? "->" : "->0\n");
 }
 
-int64_t default_slice(int dtype) { return (int64_t)(64 * 1024) / ra::elem_bytes(dtype); }
-
 // Run phases [hop_begin, hop_end) (0..p-2 reduce-scatter, p-1..2p-3 all-gather)
 // with a ring algorithm.
 int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, int algo,
@@ -211,7 +210,9 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
   int grid = 0;
   hipError_t e;
   if (algo == RA_ALGO_RING_PIPELINED) {
-    int64_t slice = opt && opt->slice_elems > 0 ? opt->slice_elems : default_slice(dtype);
+    int64_t slice = opt && opt->slice_elems > 0
+                        ? opt->slice_elems
+                        : ra::pipelined_default_slice(p, n, dtype, sc.grid);
     const int64_t V = 16 / ra::elem_bytes(dtype);
     slice = (slice + V - 1) / V * V;
     const int64_t kmax = ra::pipelined_slices_per_chunk(p, n, dtype, slice);

@@ -1,4 +1,5 @@
-// ra_device.h -- device-side building blocks of the ring all-reduce kernels (gfx950).
+// ra_elem.h -- element types, vector memory access and chunk geometry of the
+// ring all-reduce kernels (gfx950).
 //
 // * element types: one hop of the ring is "receiver's chunk += incoming chunk",
 //   rounded to the buffer type ("Ring All-Reduce, in depth", section "An
@@ -6,9 +7,6 @@
 //   16-byte vectors (global_load/store_dwordx4): 4 int32, 4 float32 or 8 bfloat16.
 // * chunk geometry: chunk c of an n-element buffer split p ways starts at
 //   c*floor(n/p) + min(c, n mod p) (same page, "An implementation").
-// * synchronisation between workgroups: a self-resetting grid barrier and
-//   per-slice ready counters, both with bounded waits that report a timeout
-//   instead of hanging ("Ring All-Reduce, in depth", "Failure modes").
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -152,108 +150,6 @@ __device__ __forceinline__ Span split_span(int64_t lo, int64_t hi) {
     s.tail_lo = a1;
   }
   return s;
-}
-
-// ---------------------------------------------------------------- workspace
-
-// Device workspace shared by the calls on one (device, stream).
-struct WsHeader {
-  uint32_t bar;          // grid-barrier word (self-resetting, see grid_barrier)
-  uint32_t status;       // sticky: 0 ok, else an ra_status code set on device
-  uint32_t pad[62];      // keep flags on their own cache lines
-};
-
-__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
-
-__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Make this wave's earlier global stores visible device-wide (the L2 of every
-// XCD) before anything the workgroup does next.  Issued by every wave: the
-// workgroup barrier alone does not wait for other waves' stores to complete.
-__device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-
-// Grid-wide barrier over `nblocks` co-resident workgroups.
-//
-// Every workgroup adds 1 to the barrier word except workgroup 0, which adds
-// 2^31 - (nblocks - 1); one full round therefore adds exactly 2^31, so the top
-// bit flips precisely when the last workgroup arrives and the low bits return to
-// where they were -- the word never needs resetting between rounds or calls.  A
-// waiter watches for the top bit to differ from what it saw when it arrived.
-//
-// `expect_extra` = 1 makes the round wait for one arrival that never comes (a
-// test hook for the timeout path).  Waits are bounded by `limit` ticks of the
-// constant-rate device clock; on expiry the waiter records RA_ERR_TIMEOUT (6)
-// in the sticky status word.  A workgroup also gives up as soon as it sees a
-// nonzero status.  Returns false when the caller must exit.
-__device__ __forceinline__ bool grid_barrier(WsHeader* ws, uint32_t nblocks,
-                                             uint32_t expect_extra, uint64_t limit) {
-  __shared__ int go;
-  release_agent();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t inc = blockIdx.x == 0 ? 0x80000000u - (nblocks + expect_extra - 1u) : 1u;
-    uint32_t old = __hip_atomic_fetch_add(&ws->bar, inc, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-    uint64_t t0 = now_ticks();
-    int ok = 1;
-    while (((ld_relaxed(&ws->bar) ^ old) & 0x80000000u) == 0) {
-      if (ld_relaxed(&ws->status) != 0) { ok = 0; break; }
-      if (now_ticks() - t0 > limit) {
-        __hip_atomic_store(&ws->status, 6u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ok = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    acquire_agent();
-    go = ok;
-  }
-  __syncthreads();
-  return go != 0;
-}
-
-// Wait until *flag >= target (thread 0 spins, the workgroup follows).  Same
-// timeout and abort rules as grid_barrier.  Returns false when the caller must exit.
-__device__ __forceinline__ bool wait_flag(WsHeader* ws, const uint32_t* flag, uint32_t target,
-                                          uint64_t limit) {
-  __shared__ int go;
-  if (threadIdx.x == 0) {
-    int ok = 1;
-    if ((int32_t)(ld_relaxed(flag) - target) < 0) {
-      uint64_t t0 = now_ticks();
-      while ((int32_t)(ld_relaxed(flag) - target) < 0) {
-        if (ld_relaxed(&ws->status) != 0) { ok = 0; break; }
-        if (now_ticks() - t0 > limit) {
-          __hip_atomic_store(&ws->status, 6u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          ok = 0;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-    }
-    acquire_agent();
-    go = ok;
-  }
-  __syncthreads();
-  return go != 0;
-}
-
-// Publish *flag = value after every wave's stores of this workgroup.
-__device__ __forceinline__ void post_flag(uint32_t* flag, uint32_t value) {
-  release_agent();
-  __syncthreads();
-  if (threadIdx.x == 0)
-    __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ bool ws_failed(WsHeader* ws) {
-  __shared__ int bad;
-  if (threadIdx.x == 0) bad = ld_relaxed(&ws->status) != 0;
-  __syncthreads();
-  return bad != 0;
 }
 
 }  // namespace ra

@@ -1,0 +1,124 @@
+// ra_fused.hip -- the fused one-pass all-reduce kernel (gfx950) and its launcher.
+//
+// One launch per all-reduce.  Every element is folded in exactly the order the
+// ring accumulates it ("Ring All-Reduce, in depth", section "The schedule":
+// chunk c leaves rank c at reduce-scatter step 0 and picks up ranks c+1, c+2,
+// ... one hop per step, the all-gather then copies the finished sum), rounding
+// to the buffer type at every hop, and the result is stored to all p ranks.
+// Every rank buffer is read once and written once: 2*p*S bytes, the least any
+// one-GPU all-reduce can move.  All element traffic uses 16-byte vector
+// loads/stores with consecutive lanes on consecutive vectors; chunk edges that
+// fall inside a vector are handled element by element.  Indices are 64-bit.
+#include "ra_elem.h"
+#include "ra_internal.h"
+
+namespace ra {
+
+// Tile t = (chunk c, tile j of that chunk).  For every element of the tile:
+// acc = x_c; acc = acc + x_{c+1}; ...; acc = acc + x_{c+p-1} (indices mod p,
+// rounding each addition), then acc is stored to every rank.  This is the
+// order in which the step-by-step ring accumulates chunk c, so the bits match.
+template <int DT, int U, bool NT>
+__global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p, int64_t T,
+                                                  int64_t ntiles) {
+  typedef Elem<DT> E;
+  constexpr int V = E::V;
+  constexpr int KB = 8;                     // ranks loaded per batch
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int c = (int)(t / T);
+    const int64_t j = t - (int64_t)c * T;
+    const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
+    const Span sp = split_span<V>(lo, hi);
+    const int64_t tv = (int64_t)kBlock * U;
+    const int64_t t0 = sp.v0 + j * tv;
+    const int64_t t1 = t0 + tv < sp.v1 ? t0 + tv : sp.v1;
+    if (t0 < t1) {
+      int64_t v[U];
+      u32x4 acc[U];
+      const void* first = P.b[c];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        v[u] = t0 + u * kBlock + threadIdx.x;
+        if (v[u] < t1) acc[u] = ld16<NT>(first, v[u]);
+      }
+      for (int k0 = 1; k0 < p; k0 += KB) {
+        u32x4 x[KB][U];
+#pragma unroll
+        for (int i = 0; i < KB; ++i) {
+          if (k0 + i < p) {
+            int r = c + k0 + i;
+            r = r >= p ? r - p : r;
+            const void* src = P.b[r];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+              if (v[u] < t1) x[i][u] = ld16<NT>(src, v[u]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < KB; ++i)
+          if (k0 + i < p) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[u] = E::add(acc[u], x[i][u]);
+          }
+      }
+      for (int r = 0; r < p; ++r) {
+        void* dst = P.b[r];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (v[u] < t1) st16<NT>(dst, v[u], acc[u]);
+      }
+    }
+    if (j == 0) {
+      const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
+      const int tt = threadIdx.x;
+      if (tt < nh + nt) {
+        const int64_t i = tt < nh ? lo + tt : sp.tail_lo + (tt - nh);
+        typename E::S acc = ld1<DT>(P.b[c], i);
+        for (int k = 1; k < p; ++k) {
+          int r = c + k;
+          r = r >= p ? r - p : r;
+          acc = E::add1(acc, ld1<DT>(P.b[r], i));
+        }
+        for (int r = 0; r < p; ++r) st1<DT>(P.b[r], i, acc);
+      }
+    }
+  }
+}
+
+
+// Vectors per thread.  Measured on MI355X at 8 x 16 GiB bf16: one vector per
+// thread with the most workgroups in flight streams best (6.40 TB/s on 2pS
+// against 6.35 with two and 6.30 with four).
+static constexpr int kFusedU = 1;
+
+template <int DT>
+static hipError_t fused_dt(const RankPtrs& P, int p, int64_t n, hipStream_t s, int* grid_used) {
+  const int V = Elem<DT>::V;
+  const ChunkGeo g = make_geo(0, n, p);
+  int64_t T = 1;
+  for (int c = 0; c < p; ++c) {
+    const int64_t lo = host_chunk_lo(0, n, p, c), hi = host_chunk_lo(0, n, p, c + 1);
+    T = std::max<int64_t>(T, (vecs_in(lo, hi, V) + (int64_t)kBlock * kFusedU - 1) /
+                                 ((int64_t)kBlock * kFusedU));
+  }
+  const int64_t ntiles = (int64_t)p * T;
+  const int grid = (int)std::min<int64_t>(ntiles, kMaxGrid);
+  *grid_used = grid;
+  if (streaming(p, n, DT))
+    hipLaunchKernelGGL((k_fused<DT, kFusedU, true>), dim3(grid), dim3(kBlock), 0, s, P, g, p, T, ntiles);
+  else
+    hipLaunchKernelGGL((k_fused<DT, kFusedU, false>), dim3(grid), dim3(kBlock), 0, s, P, g, p, T, ntiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, hipStream_t s,
+                        int* grid_used) {
+  switch (dtype) {
+    case 0: return fused_dt<0>(P, p, n, s, grid_used);
+    case 1: return fused_dt<1>(P, p, n, s, grid_used);
+    default: return fused_dt<2>(P, p, n, s, grid_used);
+  }
+}
+
+
+}  // namespace ra

@@ -1,4 +1,5 @@
-// ra_kernels.hip -- HIP kernels of the ring all-reduce for gfx950, and their launchers.
+// ra_steps.hip -- the step-by-step and pipelined ring kernels (gfx950) and their
+// launchers.
 //
 // p virtual ranks live in one GPU's HBM; a "send" of the ring is a read of the
 // sender's chunk and a "receive" is an add into (or a copy over) the receiver's
@@ -6,12 +7,6 @@
 // schedule", "An implementation", "What real libraries add"; "Derive the cost of
 // a ring all-reduce" (aiinfrainterviews.com), section "Where it stops scaling".
 //
-// Kernels
-//   k_fused      one pass over the elements; each element is folded in its
-//                chunk's ring order (chunk c: ranks c, c+1, ..., c+p-1, rounding
-//                every hop) and the result is stored to all p ranks.  Reads and
-//                writes every buffer once: 2*p*S bytes, the least any one-GPU
-//                all-reduce can move.
 //   k_steps      the schedule step by step in one persistent cooperative launch:
 //                reduce-scatter steps, all-gather steps (forward ring, or both
 //                rings of the bidirectional variant on the two halves), or the
@@ -20,43 +15,14 @@
 //                assigned to ranks, and a rank forwards slice k as soon as its
 //                left neighbour has finished slice k (per-slice ready counters
 //                instead of step barriers).
-//   k_copy       plain streaming copy, a measurement helper.
-//
-// All element traffic uses 16-byte vector loads/stores with consecutive lanes
-// on consecutive vectors; chunk edges that fall inside a vector are handled
-// element by element.  Every index into a buffer is 64-bit.
-#include "ra_device.h"
+#include "ra_elem.h"
+#include "ra_sync.h"
 #include "ra_internal.h"
 
-#include <algorithm>
 #include <mutex>
 #include <unordered_map>
 
 namespace ra {
-
-int elem_bytes(int dtype) { return dtype == 2 ? 2 : 4; }
-
-static int elems_per_vec(int dtype) { return 16 / elem_bytes(dtype); }
-
-// Whole 16-byte vectors inside [lo, hi) (host mirror of split_span).
-static int64_t vecs_in(int64_t lo, int64_t hi, int V) {
-  int64_t a0 = (lo + V - 1) / V * V;
-  int64_t a1 = hi / V * V;
-  return a1 > a0 ? (a1 - a0) / V : 0;
-}
-
-static int64_t host_chunk_lo(int64_t off, int64_t len, int p, int c) {
-  int64_t base = len / p, extra = len % p;
-  return off + (int64_t)c * base + std::min<int64_t>(c, extra);
-}
-
-static ChunkGeo make_geo(int64_t off, int64_t len, int p) {
-  ChunkGeo g;
-  g.off = off;
-  g.base = len / p;
-  g.extra = len % p;
-  return g;
-}
 
 // ================================================================ hop on one tile
 
@@ -98,78 +64,6 @@ __device__ __forceinline__ void hop_tile(const void* __restrict__ src, void* __r
   }
 }
 
-// ================================================================ fused one-pass
-
-// Tile t = (chunk c, tile j of that chunk).  For every element of the tile:
-// acc = x_c; acc = acc + x_{c+1}; ...; acc = acc + x_{c+p-1} (indices mod p,
-// rounding each addition), then acc is stored to every rank.  This is the
-// order in which the step-by-step ring accumulates chunk c, so the bits match.
-template <int DT, int U, bool NT>
-__global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p, int64_t T,
-                                                  int64_t ntiles) {
-  typedef Elem<DT> E;
-  constexpr int V = E::V;
-  constexpr int KB = 8;                     // ranks loaded per batch
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int c = (int)(t / T);
-    const int64_t j = t - (int64_t)c * T;
-    const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
-    const Span sp = split_span<V>(lo, hi);
-    const int64_t tv = (int64_t)kBlock * U;
-    const int64_t t0 = sp.v0 + j * tv;
-    const int64_t t1 = t0 + tv < sp.v1 ? t0 + tv : sp.v1;
-    if (t0 < t1) {
-      int64_t v[U];
-      u32x4 acc[U];
-      const void* first = P.b[c];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        v[u] = t0 + u * kBlock + threadIdx.x;
-        if (v[u] < t1) acc[u] = ld16<NT>(first, v[u]);
-      }
-      for (int k0 = 1; k0 < p; k0 += KB) {
-        u32x4 x[KB][U];
-#pragma unroll
-        for (int i = 0; i < KB; ++i) {
-          if (k0 + i < p) {
-            int r = c + k0 + i;
-            r = r >= p ? r - p : r;
-            const void* src = P.b[r];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-              if (v[u] < t1) x[i][u] = ld16<NT>(src, v[u]);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < KB; ++i)
-          if (k0 + i < p) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) acc[u] = E::add(acc[u], x[i][u]);
-          }
-      }
-      for (int r = 0; r < p; ++r) {
-        void* dst = P.b[r];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (v[u] < t1) st16<NT>(dst, v[u], acc[u]);
-      }
-    }
-    if (j == 0) {
-      const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
-      const int tt = threadIdx.x;
-      if (tt < nh + nt) {
-        const int64_t i = tt < nh ? lo + tt : sp.tail_lo + (tt - nh);
-        typename E::S acc = ld1<DT>(P.b[c], i);
-        for (int k = 1; k < p; ++k) {
-          int r = c + k;
-          r = r >= p ? r - p : r;
-          acc = E::add1(acc, ld1<DT>(P.b[r], i));
-        }
-        for (int r = 0; r < p; ++r) st1<DT>(P.b[r], i, acc);
-      }
-    }
-  }
-}
 
 // ================================================================ step by step
 
@@ -268,6 +162,7 @@ __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
   }
 }
 
+
 // ================================================================ pipelined
 
 struct PipeArgs {
@@ -343,46 +238,8 @@ __global__ __launch_bounds__(kBlock) void k_pipelined(PipeArgs a) {
   }
 }
 
-// ================================================================ copy
-
-__global__ __launch_bounds__(kBlock) void k_copy(u32x4* __restrict__ dst,
-                                                 const u32x4* __restrict__ src, int64_t nvec) {
-  constexpr int U = 4;
-  const int64_t stride = (int64_t)gridDim.x * kBlock * U;
-  for (int64_t base = (int64_t)blockIdx.x * kBlock * U; base < nvec; base += stride) {
-    u32x4 x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t v = base + u * kBlock + threadIdx.x;
-      if (v < nvec) x[u] = src[v];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t v = base + u * kBlock + threadIdx.x;
-      if (v < nvec) dst[v] = x[u];
-    }
-  }
-}
 
 // ================================================================ launchers
-
-// Vectors per thread.  Measured on MI355X at 8 x 16 GiB bf16: one vector per
-// thread with the most workgroups in flight streams best (6.40 TB/s on 2pS
-// against 6.35 with two and 6.30 with four).
-static constexpr int kFusedU = 1;
-static constexpr int kStepU = 2;
-static constexpr int kPipeU = 2;
-
-// Buffers larger than this in total (p * S) are streamed with non-temporal
-// loads and stores: they are far beyond the 256 MB Infinity Cache, and the
-// streaming hint measured +3.7% for the fused kernel at 8 x 16 GiB.  Smaller
-// working sets keep normal caching so that repeated calls can hit the cache.
-static constexpr int64_t kStreamingBytes = 512ll << 20;
-
-static bool streaming(int p, int64_t n, int dtype) {
-  return (int64_t)p * n * elem_bytes(dtype) > kStreamingBytes;
-}
-static constexpr int64_t kMaxGrid = 1 << 22;     // non-persistent grids; beyond, blocks loop
 
 static hipError_t device_cus(int* cus) {
   int dev = 0;
@@ -420,34 +277,12 @@ static hipError_t resident_blocks(const void* func, int* out) {
   return hipSuccess;
 }
 
-template <int DT>
-static hipError_t fused_dt(const RankPtrs& P, int p, int64_t n, hipStream_t s, int* grid_used) {
-  const int V = Elem<DT>::V;
-  const ChunkGeo g = make_geo(0, n, p);
-  int64_t T = 1;
-  for (int c = 0; c < p; ++c) {
-    const int64_t lo = host_chunk_lo(0, n, p, c), hi = host_chunk_lo(0, n, p, c + 1);
-    T = std::max<int64_t>(T, (vecs_in(lo, hi, V) + (int64_t)kBlock * kFusedU - 1) /
-                                 ((int64_t)kBlock * kFusedU));
-  }
-  const int64_t ntiles = (int64_t)p * T;
-  const int grid = (int)std::min<int64_t>(ntiles, kMaxGrid);
-  *grid_used = grid;
-  if (streaming(p, n, DT))
-    hipLaunchKernelGGL((k_fused<DT, kFusedU, true>), dim3(grid), dim3(kBlock), 0, s, P, g, p, T, ntiles);
-  else
-    hipLaunchKernelGGL((k_fused<DT, kFusedU, false>), dim3(grid), dim3(kBlock), 0, s, P, g, p, T, ntiles);
-  return hipGetLastError();
-}
 
-hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, hipStream_t s,
-                        int* grid_used) {
-  switch (dtype) {
-    case 0: return fused_dt<0>(P, p, n, s, grid_used);
-    case 1: return fused_dt<1>(P, p, n, s, grid_used);
-    default: return fused_dt<2>(P, p, n, s, grid_used);
-  }
-}
+// Step-by-step kernels run on a persistent grid capped at 4 workgroups per CU
+// (see kPersistentPerCU), so each thread keeps more bytes in flight: measured at
+// 8 x 16 GB bf16, four vectors per thread ran 103.8 ms against 107.3 with two.
+static constexpr int kStepU = 4;
+static constexpr int kPipeU = 4;
 
 template <int DT>
 static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, int step_begin,
@@ -519,6 +354,27 @@ hipError_t launch_steps(const RankPtrs& P, int p, int64_t n, int dtype, StepMode
   }
 }
 
+// Default slice: about four slices per worker per hop, at least 64 KiB.  Every
+// slice hop pays one acquire and one release (an L2 invalidate and an L2
+// write-back); measured at 8 x 16 GB bf16, 64 KiB slices ran 719 ms and 4 MiB
+// slices 105 ms, so slices must be large enough to amortise that cost while
+// leaving every worker several slices to pipeline.
+
+int64_t pipelined_default_slice(int p, int64_t n, int dtype, int grid_override) {
+  const int V = elems_per_vec(dtype);
+  int cus = 0;
+  int64_t workers = 64;
+  if (device_cus(&cus) == hipSuccess && cus > 0) {
+    int64_t budget = (int64_t)cus * kPersistentPerCU;
+    if (grid_override > 0) budget = std::min<int64_t>(budget, grid_override);
+    workers = std::max<int64_t>(1, budget / p);
+  }
+  const int64_t chunk = n / p + 1;
+  int64_t slice = (chunk + 4 * workers - 1) / (4 * workers);
+  slice = std::max<int64_t>(slice, (64 << 10) / elem_bytes(dtype));
+  return (slice + V - 1) / V * V;
+}
+
 int64_t pipelined_slices_per_chunk(int p, int64_t n, int dtype, int64_t slice) {
   const int V = elems_per_vec(dtype);
   int64_t kmax = 1;
@@ -575,14 +431,5 @@ hipError_t launch_pipelined(const RankPtrs& P, int p, int64_t n, int dtype, int 
   }
 }
 
-hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s) {
-  const int64_t nvec = bytes / 16;
-  if (nvec == 0) return hipSuccess;
-  const int64_t per = (int64_t)kBlock * 4;
-  const int grid = (int)std::min<int64_t>((nvec + per - 1) / per, kMaxGrid);
-  hipLaunchKernelGGL(k_copy, dim3(grid), dim3(kBlock), 0, s, reinterpret_cast<u32x4*>(dst),
-                     reinterpret_cast<const u32x4*>(src), nvec);
-  return hipGetLastError();
-}
 
 }  // namespace ra
