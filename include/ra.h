@@ -69,13 +69,15 @@ typedef enum ra_op { RA_SUM = 0 } ra_op;
 /* Algorithms.  All ring variants give bit-identical results to the step-by-step
  * schedule; the tree sums in a different order. */
 typedef enum ra_algo {
-  RA_ALGO_DEFAULT = -1,       /* RA_ALGO_FUSED for all-reduce, RING_STEP for RS/AG,
-                                 overridable with the RA_ALGO environment variable */
+  RA_ALGO_DEFAULT = -1,       /* RA_ALGO_FUSED (all-reduce: overridable with the RA_ALGO
+                                 environment variable, by name or number) */
   RA_ALGO_RING_STEP = 0,      /* one persistent kernel, 2(p-1) steps, grid barrier between steps */
   RA_ALGO_RING_PIPELINED = 1, /* chunks cut into slices; per-slice ready flags instead of barriers */
   RA_ALGO_RING_BIDIR = 2,     /* two counter-rotating rings, each on half of the buffer */
   RA_ALGO_FUSED = 3,          /* one pass: each element folded in its ring order, written to all ranks */
-  RA_ALGO_TREE = 4            /* binomial tree: reduce to rank 0, broadcast back */
+  RA_ALGO_TREE = 4,           /* binomial tree: reduce to rank 0, broadcast back */
+  RA_ALGO_RING_CHANNELS = 5   /* RING_STEP split into independent channels: channel h takes
+                                 part h of every chunk and synchronises only with itself */
 } ra_algo;
 
 /* ra_options.flags bits */
@@ -92,7 +94,11 @@ typedef struct ra_options {
   uint32_t flags;       /* RA_FLAG_* */
   uint64_t* step_ts;    /* optional DEVICE array of (steps + 1) uint64: device wall-clock
                            ticks at kernel start and as each step's barrier releases
-                           (RING_STEP, RING_BIDIR, TREE).  NULL = not recorded. */
+                           (RING_STEP, RING_BIDIR, TREE, RING_CHANNELS: channel 0).
+                           NULL = not recorded. */
+  int32_t channels;     /* RING_CHANNELS: number of channels, 1..64; 0 = 8 (one per XCD).
+                           Capped at the number of workgroups.  Other algorithms ignore it. */
+  int32_t reserved;     /* must be 0 */
 } ra_options;
 
 /*
@@ -109,8 +115,12 @@ int ra_chunk_bounds(int64_t n, int p, int64_t* starts);
  * ra_reduce_scatter -- the p - 1 reduce-scatter steps ([InDepth] "The schedule";
  * [Deepinsea] "Phase 1: Reduce-Scatter").  Step s: rank r's chunk (r - s) mod p is
  * added into rank r+1's copy of that chunk.  Afterwards rank r's chunk
- * (r + 1) mod p holds the full sum; every other chunk of rank r holds the ring's
- * partial sum of chunk c over ranks c, c+1, ..., r (the step-by-step states).
+ * (r + 1) mod p holds the full sum, accumulated in ring order.  What the other
+ * chunks hold depends on the algorithm: RING_STEP, RING_PIPELINED and
+ * RING_CHANNELS leave the ring's partial sum of chunk c over ranks c, c+1, ..., r
+ * (the step-by-step states); FUSED (the default) leaves them as they were, and
+ * moves (p+1)*S bytes instead of 3(p-1)*S ([InDepth] "Trade-offs": reduce-scatter
+ * and all-gather are used on their own by sharded optimisers and FSDP).
  */
 int ra_reduce_scatter(void* const* bufs, int p, int64_t n, int dtype, int op,
                       hipStream_t stream);
@@ -120,7 +130,9 @@ int ra_reduce_scatter(void* const* bufs, int p, int64_t n, int dtype, int op,
  * [Deepinsea] "Phase 2: All-Gather").  Expects the layout ra_reduce_scatter
  * leaves (rank r owns chunk (r + 1) mod p).  Step s: rank r's chunk
  * (r + 1 - s) mod p overwrites rank r+1's copy; afterwards every rank holds every
- * owned chunk.  ra_reduce_scatter followed by ra_all_gather equals ra_allreduce.
+ * owned chunk.  Only the owned chunks are read, whatever the other chunks hold,
+ * so ra_reduce_scatter followed by ra_all_gather equals ra_allreduce for every
+ * pairing of the algorithms.  FUSED (the default) moves p*S bytes.
  */
 int ra_all_gather(void* const* bufs, int p, int64_t n, int dtype, hipStream_t stream);
 
@@ -142,12 +154,16 @@ int ra_allreduce(void* const* bufs, int p, int64_t n, int dtype, int op,
  *         [InDepth] "What real libraries add", pipelining.  TREE: [Derive]
  *         "Where it stops scaling", a binomial tree rooted at rank 0 (reduce
  *         level k adds rank r + 2^k into rank r for r a multiple of 2^(k+1)).
+ *         RING_CHANNELS: [InDepth] "What real libraries add", multiple rings or
+ *         channels -- the result is the same bits as RING_STEP for any channel count.
  *   opt   may be NULL (all defaults).
  */
 int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
                     const ra_options* opt, hipStream_t stream);
 
-/* ra_reduce_scatter / ra_all_gather with algo RING_STEP or RING_PIPELINED and options. */
+/* ra_reduce_scatter / ra_all_gather with algo RING_STEP, RING_PIPELINED, RING_CHANNELS
+ * or FUSED and options; other algorithms return RA_ERR_UNSUPPORTED, a channel count
+ * outside 0..64 RA_ERR_INVALID_ARG. */
 int ra_reduce_scatter_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
                          const ra_options* opt, hipStream_t stream);
 int ra_all_gather_ex(void* const* bufs, int p, int64_t n, int dtype, int algo,

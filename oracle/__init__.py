@@ -45,7 +45,7 @@ from .schedule import (chunk_bounds, chunk_of, rs_send_chunk, ag_send_chunk,
 from .arith import (DTYPES, STORAGE, add_rounded, bf16_bits_to_f32,
                     f32_to_bf16_bits, as_values)
 from .ring import (RingTimeout, reduce_scatter, all_gather, ring_allreduce)
-from .fold import ring_fold, ring_fold_window, rs_partial
+from .fold import ring_fold, ring_fold_window, rs_partial, rs_owned
 from .tree import tree_allreduce
 from .bidir import bidir_allreduce, bidir_halves
 from .exact import exact_sum, normwise_error
@@ -56,6 +56,6 @@ __all__ = [
     "right_of", "left_of", "DTYPES", "STORAGE", "add_rounded",
     "bf16_bits_to_f32", "f32_to_bf16_bits", "as_values", "RingTimeout",
     "reduce_scatter", "all_gather", "ring_allreduce", "ring_fold",
-    "ring_fold_window", "rs_partial", "tree_allreduce", "bidir_allreduce",
+    "ring_fold_window", "rs_partial", "rs_owned", "tree_allreduce", "bidir_allreduce",
     "bidir_halves", "exact_sum", "normwise_error", "cost",
 ]

@@ -60,6 +60,26 @@ def rs_partial(xs, dtype, r, direction=1):
     return out
 
 
+def rs_owned(xs, dtype, r, direction=1):
+    """Rank r's buffer after a reduce-scatter that writes only the owned chunk.
+
+    The owned chunk, (r + direction) mod p ([InDepth] "The schedule": rank r ends
+    the reduce-scatter holding chunk r + 1), carries the full ring-order fold;
+    every other chunk keeps rank r's input.  This is what a reduce-scatter used on
+    its own must deliver ([InDepth] "Trade-offs"); the partial sums the
+    step-by-step ring leaves in the other chunks are a by-product of its schedule.
+    """
+    p = len(xs)
+    n = len(xs[0])
+    out = np.array(xs[r], copy=True)
+    c = (r + direction) % p
+    lo, hi = chunk_bounds(n, p)[c]
+    if hi > lo:
+        order = [(c + direction * k) % p for k in range(p)]
+        out[lo:hi] = _fold_terms([np.asarray(xs[q])[lo:hi] for q in order], dtype)
+    return out
+
+
 def ring_fold_window(windows, lo, n, dtype, direction=1):
     """Ring-order result for elements [lo, lo + len(window)) of n-element buffers.
 

@@ -23,7 +23,7 @@ RA_MAX_RANKS = 64
 RA_FLAG_FORCE_TIMEOUT = 1
 
 ALGOS = {"default": -1, "ring_step": 0, "ring_pipelined": 1, "ring_bidir": 2,
-         "fused": 3, "tree": 4}
+         "fused": 3, "tree": 4, "ring_channels": 5}
 DTYPE_NAMES = {"int32": RA_INT32, "float32": RA_FLOAT32, "bfloat16": RA_BFLOAT16}
 
 
@@ -40,7 +40,9 @@ class ra_options(ctypes.Structure):
                 ("timeout_us", ctypes.c_int64),
                 ("grid", ctypes.c_int32),
                 ("flags", ctypes.c_uint32),
-                ("step_ts", ctypes.c_void_p)]
+                ("step_ts", ctypes.c_void_p),
+                ("channels", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -142,13 +144,15 @@ def _marshal(tensors):
     return ptrs, len(tensors), t0.numel(), dtype_code(t0), t0.device
 
 
-def _options(slice_elems=0, timeout_us=0, grid=0, flags=0, step_ts=None):
+def _options(slice_elems=0, timeout_us=0, grid=0, flags=0, step_ts=None, channels=0):
     o = ra_options()
     o.slice_elems = int(slice_elems)
     o.timeout_us = int(timeout_us)
     o.grid = int(grid)
     o.flags = int(flags)
     o.step_ts = None if step_ts is None else int(step_ts.data_ptr())
+    o.channels = int(channels)
+    o.reserved = 0
     return o
 
 

@@ -45,6 +45,11 @@ bool debug_on() {
   return on != 0;
 }
 
+constexpr int kLastAlgo = RA_ALGO_RING_CHANNELS;
+
+// Channels of RING_CHANNELS when the caller does not choose: one per XCD.
+constexpr int kDefaultChannels = 8;
+
 const char* algo_name(int a) {
   switch (a) {
     case RA_ALGO_RING_STEP: return "ring_step";
@@ -52,6 +57,7 @@ const char* algo_name(int a) {
     case RA_ALGO_RING_BIDIR: return "ring_bidir";
     case RA_ALGO_FUSED: return "fused";
     case RA_ALGO_TREE: return "tree";
+    case RA_ALGO_RING_CHANNELS: return "ring_channels";
     default: return "?";
   }
 }
@@ -60,11 +66,11 @@ const char* algo_name(int a) {
 int env_algo(int fallback) {
   const char* v = std::getenv("RA_ALGO");
   if (!v || !*v) return fallback;
-  for (int a = RA_ALGO_RING_STEP; a <= RA_ALGO_TREE; ++a)
+  for (int a = RA_ALGO_RING_STEP; a <= kLastAlgo; ++a)
     if (std::strcmp(v, algo_name(a)) == 0) return a;
   char* end = nullptr;
   long x = std::strtol(v, &end, 10);
-  if (end && *end == 0 && x >= RA_ALGO_RING_STEP && x <= RA_ALGO_TREE) return (int)x;
+  if (end && *end == 0 && x >= RA_ALGO_RING_STEP && x <= kLastAlgo) return (int)x;
   return fallback;
 }
 
@@ -95,6 +101,17 @@ int check_args(void* const* bufs, int p, int64_t n, int dtype) {
                     starts[i + 1].second);
   }
   return RA_OK;
+}
+
+int check_channels(const ra_options* opt) {
+  if (opt && (opt->channels < 0 || opt->channels > ra::kMaxChannels))
+    return fail(RA_ERR_INVALID_ARG, "channels = %d, need 0..%d", opt->channels, ra::kMaxChannels);
+  return RA_OK;
+}
+
+bool phase_algo(int algo) {
+  return algo == RA_ALGO_RING_STEP || algo == RA_ALGO_RING_PIPELINED ||
+         algo == RA_ALGO_RING_CHANNELS || algo == RA_ALGO_FUSED;
 }
 
 int check_op(int op) {
@@ -180,6 +197,7 @@ int sync_cfg(const ra_options* opt, Workspace* w, ra::SyncCfg* sc) {
   sc->expect_extra = opt && (opt->flags & RA_FLAG_FORCE_TIMEOUT) ? 1u : 0u;
   sc->step_ts = opt ? opt->step_ts : nullptr;
   sc->grid = opt && opt->grid > 0 ? opt->grid : 0;
+  sc->channels = 1;
   return RA_OK;
 }
 
@@ -199,6 +217,17 @@ void debug_line(const char* call, int algo, int p, int64_t n, int dtype, int gri
 // with a ring algorithm.
 int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, int algo,
              int hop_begin, int hop_end, const ra_options* opt, hipStream_t s) {
+  if (algo == RA_ALGO_FUSED) {
+    // the fused pass covers whole phases only
+    const int mode = hop_begin == 0 && hop_end == 2 * (p - 1) ? 0 : hop_begin == 0 ? 1 : 2;
+    ra::RankPtrs P;
+    fill_ptrs(bufs, p, &P);
+    int grid = 0;
+    hipError_t e = ra::launch_fused(P, p, n, dtype, mode, s, &grid);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    debug_line(call, algo, p, n, dtype, grid);
+    return RA_OK;
+  }
   Workspace* w = nullptr;
   int rc = get_workspace(s, &w);
   if (rc != RA_OK) return rc;
@@ -222,6 +251,8 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
     e = ra::launch_pipelined(P, p, n, dtype, hop_begin, hop_end, slice, kmax, w->flags, base,
                              sc, s, &grid);
   } else {
+    if (algo == RA_ALGO_RING_CHANNELS)
+      sc.channels = opt && opt->channels > 0 ? opt->channels : kDefaultChannels;
     e = ra::launch_steps(P, p, n, dtype, ra::kModeRing, hop_begin, hop_end, sc, s, &grid);
   }
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
@@ -247,10 +278,12 @@ int ra_reduce_scatter_ex(void* const* bufs, int p, int64_t n, int dtype, int op,
                          const ra_options* opt, hipStream_t stream) {
   int rc = check_args(bufs, p, n, dtype);
   if (rc == RA_OK) rc = check_op(op);
+  if (rc == RA_OK) rc = check_channels(opt);
   if (rc != RA_OK) return rc;
-  if (algo == RA_ALGO_DEFAULT) algo = RA_ALGO_RING_STEP;
-  if (algo != RA_ALGO_RING_STEP && algo != RA_ALGO_RING_PIPELINED)
-    return fail(RA_ERR_UNSUPPORTED, "reduce-scatter runs RING_STEP or RING_PIPELINED, not %d", algo);
+  if (algo == RA_ALGO_DEFAULT) algo = RA_ALGO_FUSED;
+  if (!phase_algo(algo))
+    return fail(RA_ERR_UNSUPPORTED,
+                "reduce-scatter runs RING_STEP, RING_PIPELINED, RING_CHANNELS or FUSED, not %d", algo);
   if (p == 1 || n == 0) return RA_OK;
   return run_ring("reduce_scatter", bufs, p, n, dtype, algo, 0, p - 1, opt, stream);
 }
@@ -258,10 +291,12 @@ int ra_reduce_scatter_ex(void* const* bufs, int p, int64_t n, int dtype, int op,
 int ra_all_gather_ex(void* const* bufs, int p, int64_t n, int dtype, int algo,
                      const ra_options* opt, hipStream_t stream) {
   int rc = check_args(bufs, p, n, dtype);
+  if (rc == RA_OK) rc = check_channels(opt);
   if (rc != RA_OK) return rc;
-  if (algo == RA_ALGO_DEFAULT) algo = RA_ALGO_RING_STEP;
-  if (algo != RA_ALGO_RING_STEP && algo != RA_ALGO_RING_PIPELINED)
-    return fail(RA_ERR_UNSUPPORTED, "all-gather runs RING_STEP or RING_PIPELINED, not %d", algo);
+  if (algo == RA_ALGO_DEFAULT) algo = RA_ALGO_FUSED;
+  if (!phase_algo(algo))
+    return fail(RA_ERR_UNSUPPORTED,
+                "all-gather runs RING_STEP, RING_PIPELINED, RING_CHANNELS or FUSED, not %d", algo);
   if (p == 1 || n == 0) return RA_OK;
   return run_ring("all_gather", bufs, p, n, dtype, algo, p - 1, 2 * (p - 1), opt, stream);
 }
@@ -278,21 +313,13 @@ int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int 
                     const ra_options* opt, hipStream_t stream) {
   int rc = check_args(bufs, p, n, dtype);
   if (rc == RA_OK) rc = check_op(op);
+  if (rc == RA_OK) rc = check_channels(opt);
   if (rc != RA_OK) return rc;
   if (algo == RA_ALGO_DEFAULT) algo = env_algo(RA_ALGO_FUSED);
-  if (algo < RA_ALGO_RING_STEP || algo > RA_ALGO_TREE)
+  if (algo < RA_ALGO_RING_STEP || algo > kLastAlgo)
     return fail(RA_ERR_INVALID_ARG, "unknown algo %d", algo);
   if (p == 1 || n == 0) return RA_OK;
-  if (algo == RA_ALGO_FUSED) {
-    ra::RankPtrs P;
-    fill_ptrs(bufs, p, &P);
-    int grid = 0;
-    hipError_t e = ra::launch_fused(P, p, n, dtype, stream, &grid);
-    if (e != hipSuccess) return fail_hip(e, "kernel launch");
-    debug_line("allreduce", algo, p, n, dtype, grid);
-    return RA_OK;
-  }
-  if (algo == RA_ALGO_RING_STEP || algo == RA_ALGO_RING_PIPELINED)
+  if (phase_algo(algo))
     return run_ring("allreduce", bufs, p, n, dtype, algo, 0, 2 * (p - 1), opt, stream);
   // bidirectional rings or tree: one cooperative launch of the step kernel
   Workspace* w = nullptr;
@@ -338,8 +365,8 @@ int ra_stream_status(hipStream_t stream) {
   e = hipMemcpy(&status, &hdr->status, sizeof status, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail_hip(e, "reading device status");
   if (status == 0) return RA_OK;
-  // clear the sticky error and the barrier word the aborted kernel left behind
-  e = hipMemset(hdr, 0, 2 * sizeof(uint32_t));
+  // clear the sticky error and the barrier words the aborted kernel left behind
+  e = hipMemset(hdr, 0, sizeof(ra::WsHeader));
   if (e != hipSuccess) return fail_hip(e, "clearing device status");
   return fail((int)status, "a device-side wait timed out (status %u)", status);
 }

@@ -14,11 +14,24 @@
 
 namespace ra {
 
+// What one fused pass produces.
+//   kAllReduce      every element folded in its ring order, stored to every rank
+//   kReduceScatter  the same fold, stored only to the chunk's owner: chunk c ends
+//                   the reduce-scatter on rank c - 1 ("Ring All-Reduce, in
+//                   depth", section "The schedule": rank r owns chunk r + 1);
+//                   the other chunks of every rank are left as they were
+//   kAllGather      the owner's copy of chunk c (rank c - 1) stored to the
+//                   other p - 1 ranks, no arithmetic
+// Bytes moved: 2pS, (p+1)S and pS.  A reduce-scatter and all-gather used on
+// their own, as sharded optimisers do ("Ring All-Reduce, in depth", section
+// "Trade-offs"), each move the least their output needs.
+enum FusedMode { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
+
 // Tile t = (chunk c, tile j of that chunk).  For every element of the tile:
 // acc = x_c; acc = acc + x_{c+1}; ...; acc = acc + x_{c+p-1} (indices mod p,
-// rounding each addition), then acc is stored to every rank.  This is the
-// order in which the step-by-step ring accumulates chunk c, so the bits match.
-template <int DT, int U, bool NT>
+// rounding each addition), the order in which the step-by-step ring
+// accumulates chunk c, so the bits match.
+template <int DT, int U, bool NT, int MODE>
 __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p, int64_t T,
                                                   int64_t ntiles) {
   typedef Elem<DT> E;
@@ -27,6 +40,7 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int c = (int)(t / T);
     const int64_t j = t - (int64_t)c * T;
+    const int owner = c == 0 ? p - 1 : c - 1;
     const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
     const Span sp = split_span<V>(lo, hi);
     const int64_t tv = (int64_t)kBlock * U;
@@ -35,37 +49,46 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
     if (t0 < t1) {
       int64_t v[U];
       u32x4 acc[U];
-      const void* first = P.b[c];
+      const void* first = P.b[MODE == kAllGather ? owner : c];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         v[u] = t0 + u * kBlock + threadIdx.x;
         if (v[u] < t1) acc[u] = ld16<NT>(first, v[u]);
       }
-      for (int k0 = 1; k0 < p; k0 += KB) {
-        u32x4 x[KB][U];
+      if (MODE != kAllGather) {
+        for (int k0 = 1; k0 < p; k0 += KB) {
+          u32x4 x[KB][U];
 #pragma unroll
-        for (int i = 0; i < KB; ++i) {
-          if (k0 + i < p) {
-            int r = c + k0 + i;
-            r = r >= p ? r - p : r;
-            const void* src = P.b[r];
+          for (int i = 0; i < KB; ++i) {
+            if (k0 + i < p) {
+              int r = c + k0 + i;
+              r = r >= p ? r - p : r;
+              const void* src = P.b[r];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-              if (v[u] < t1) x[i][u] = ld16<NT>(src, v[u]);
+              for (int u = 0; u < U; ++u)
+                if (v[u] < t1) x[i][u] = ld16<NT>(src, v[u]);
+            }
           }
+#pragma unroll
+          for (int i = 0; i < KB; ++i)
+            if (k0 + i < p) {
+#pragma unroll
+              for (int u = 0; u < U; ++u) acc[u] = E::add(acc[u], x[i][u]);
+            }
         }
-#pragma unroll
-        for (int i = 0; i < KB; ++i)
-          if (k0 + i < p) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) acc[u] = E::add(acc[u], x[i][u]);
-          }
       }
-      for (int r = 0; r < p; ++r) {
-        void* dst = P.b[r];
+      if (MODE == kReduceScatter) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
-          if (v[u] < t1) st16<NT>(dst, v[u], acc[u]);
+          if (v[u] < t1) st16<NT>(P.b[owner], v[u], acc[u]);
+      } else {
+        for (int r = 0; r < p; ++r) {
+          if (MODE == kAllGather && r == owner) continue;
+          void* dst = P.b[r];
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            if (v[u] < t1) st16<NT>(dst, v[u], acc[u]);
+        }
       }
     }
     if (j == 0) {
@@ -73,13 +96,20 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
       const int tt = threadIdx.x;
       if (tt < nh + nt) {
         const int64_t i = tt < nh ? lo + tt : sp.tail_lo + (tt - nh);
-        typename E::S acc = ld1<DT>(P.b[c], i);
-        for (int k = 1; k < p; ++k) {
-          int r = c + k;
-          r = r >= p ? r - p : r;
-          acc = E::add1(acc, ld1<DT>(P.b[r], i));
+        typename E::S acc = ld1<DT>(P.b[MODE == kAllGather ? owner : c], i);
+        if (MODE != kAllGather) {
+          for (int k = 1; k < p; ++k) {
+            int r = c + k;
+            r = r >= p ? r - p : r;
+            acc = E::add1(acc, ld1<DT>(P.b[r], i));
+          }
         }
-        for (int r = 0; r < p; ++r) st1<DT>(P.b[r], i, acc);
+        if (MODE == kReduceScatter) {
+          st1<DT>(P.b[owner], i, acc);
+        } else {
+          for (int r = 0; r < p; ++r)
+            if (!(MODE == kAllGather && r == owner)) st1<DT>(P.b[r], i, acc);
+        }
       }
     }
   }
@@ -91,7 +121,7 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
 // against 6.35 with two and 6.30 with four).
 static constexpr int kFusedU = 1;
 
-template <int DT>
+template <int DT, int MODE>
 static hipError_t fused_dt(const RankPtrs& P, int p, int64_t n, hipStream_t s, int* grid_used) {
   const int V = Elem<DT>::V;
   const ChunkGeo g = make_geo(0, n, p);
@@ -105,18 +135,30 @@ static hipError_t fused_dt(const RankPtrs& P, int p, int64_t n, hipStream_t s, i
   const int grid = (int)std::min<int64_t>(ntiles, kMaxGrid);
   *grid_used = grid;
   if (streaming(p, n, DT))
-    hipLaunchKernelGGL((k_fused<DT, kFusedU, true>), dim3(grid), dim3(kBlock), 0, s, P, g, p, T, ntiles);
+    hipLaunchKernelGGL((k_fused<DT, kFusedU, true, MODE>), dim3(grid), dim3(kBlock), 0, s, P, g,
+                       p, T, ntiles);
   else
-    hipLaunchKernelGGL((k_fused<DT, kFusedU, false>), dim3(grid), dim3(kBlock), 0, s, P, g, p, T, ntiles);
+    hipLaunchKernelGGL((k_fused<DT, kFusedU, false, MODE>), dim3(grid), dim3(kBlock), 0, s, P, g,
+                       p, T, ntiles);
   return hipGetLastError();
 }
 
-hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, hipStream_t s,
-                        int* grid_used) {
+template <int MODE>
+static hipError_t fused_mode(const RankPtrs& P, int p, int64_t n, int dtype, hipStream_t s,
+                             int* grid_used) {
   switch (dtype) {
-    case 0: return fused_dt<0>(P, p, n, s, grid_used);
-    case 1: return fused_dt<1>(P, p, n, s, grid_used);
-    default: return fused_dt<2>(P, p, n, s, grid_used);
+    case 0: return fused_dt<0, MODE>(P, p, n, s, grid_used);
+    case 1: return fused_dt<1, MODE>(P, p, n, s, grid_used);
+    default: return fused_dt<2, MODE>(P, p, n, s, grid_used);
+  }
+}
+
+hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, int mode, hipStream_t s,
+                        int* grid_used) {
+  switch (mode) {
+    case kReduceScatter: return fused_mode<kReduceScatter>(P, p, n, dtype, s, grid_used);
+    case kAllGather: return fused_mode<kAllGather>(P, p, n, dtype, s, grid_used);
+    default: return fused_mode<kAllReduce>(P, p, n, dtype, s, grid_used);
   }
 }
 

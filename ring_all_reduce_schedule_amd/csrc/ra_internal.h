@@ -24,12 +24,15 @@ struct SyncCfg {
   uint32_t expect_extra;  // 1 = first wait expects an arrival that never comes (test hook)
   uint64_t* step_ts;      // optional device array of step timestamps
   int grid;               // 0 = as many workgroups as are co-resident
+  int channels;           // step kernels: independent channels (1 = whole grid)
 };
 
 // Launch descriptions return the number of workgroups used through *grid_used.
 
-// One pass: each element folded in its chunk's ring order, result stored to all ranks.
-hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, hipStream_t s,
+// One pass: each element folded in its chunk's ring order.  mode 0 stores the
+// result to all ranks (all-reduce), 1 only to the chunk's owner (reduce-scatter),
+// 2 copies each owner's chunk to the other ranks (all-gather).
+hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, int mode, hipStream_t s,
                         int* grid_used);
 
 // Steps [step_begin, step_end) of a step-by-step schedule, one cooperative launch,

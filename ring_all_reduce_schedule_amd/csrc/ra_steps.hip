@@ -76,6 +76,7 @@ struct StepArgs {
   uint64_t* step_ts;
   uint64_t limit;
   int p, mode, step_begin, step_end, levels;
+  int channels;         // C: workgroup b serves channel b mod C
   uint32_t expect_extra;
 };
 
@@ -135,26 +136,40 @@ __device__ __forceinline__ Seg step_segment(const StepArgs& a, int step, int seg
   return g;
 }
 
+// Channels ("Ring All-Reduce, in depth", section "What real libraries add":
+// a collective split across channels, each its own ring): channel h takes part h
+// of every segment -- part h of [lo, hi) split C ways starts at
+// lo + h*floor(len/C) + min(h, len mod C) -- and its workgroups wait only for
+// each other between steps.  Every element still takes the same hops in the same
+// order, so the result does not depend on C; C = 1 is the plain step-by-step ring.
 template <int DT, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
   if (ws_failed(a.ws)) return;
-  const uint32_t nb = gridDim.x;
+  const int C = a.channels;
+  const int h = (int)(blockIdx.x % (uint32_t)C);
+  const uint32_t nbh = (gridDim.x - (uint32_t)h + (uint32_t)C - 1u) / (uint32_t)C;
+  const int64_t b = blockIdx.x / (uint32_t)C;       // index within the channel
+  uint32_t* bar = a.ws->bar[h];
+  const bool leader = b == 0;
   if (a.step_ts && blockIdx.x == 0 && threadIdx.x == 0) a.step_ts[0] = now_ticks();
   uint32_t extra = a.expect_extra;
   for (int step = a.step_begin; step < a.step_end; ++step) {
     const int64_t ntiles = (int64_t)step_segments(a, step) * a.T;
-    for (int64_t t = blockIdx.x; t < ntiles; t += nb) {
+    for (int64_t t = b; t < ntiles; t += nbh) {
       const int seg = (int)(t / a.T);
       const int64_t j = t - (int64_t)seg * a.T;
       const Seg g = step_segment(a, step, seg);
+      const int64_t len = g.hi - g.lo, q = len / C, rem = len % C;
+      const int64_t lo = g.lo + h * q + (h < rem ? h : rem);
+      const int64_t hi = lo + q + (h < rem ? 1 : 0);
       if (g.add)
-        hop_tile<DT, U, true, NT>(a.P.b[g.src], a.P.b[g.dst], g.lo, g.hi, j);
+        hop_tile<DT, U, true, NT>(a.P.b[g.src], a.P.b[g.dst], lo, hi, j);
       else
-        hop_tile<DT, U, false, NT>(a.P.b[g.src], a.P.b[g.dst], g.lo, g.hi, j);
+        hop_tile<DT, U, false, NT>(a.P.b[g.src], a.P.b[g.dst], lo, hi, j);
     }
     const bool last = step + 1 == a.step_end;
     if (!last || a.step_ts || extra) {
-      if (!grid_barrier(a.ws, nb, extra, a.limit)) return;
+      if (!grid_barrier(a.ws, bar, leader, nbh, extra, a.limit)) return;
       extra = 0;
       if (a.step_ts && blockIdx.x == 0 && threadIdx.x == 0)
         a.step_ts[step - a.step_begin + 1] = now_ticks();
@@ -299,6 +314,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   a.step_begin = step_begin;
   a.step_end = step_end;
   a.expect_extra = sc.expect_extra;
+  a.channels = 1;
   a.levels = 0;
   while ((1 << a.levels) < p) ++a.levels;
   // segment geometry and the widest segment in vectors
@@ -318,9 +334,20 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
                                           host_chunk_lo(off, len, p, c + 1), V));
     }
   }
+  const void* func = streaming(p, n, DT) ? reinterpret_cast<const void*>(&k_steps<DT, kStepU, true>)
+                                         : reinterpret_cast<const void*>(&k_steps<DT, kStepU, false>);
+  int resident = 0;
+  hipError_t e = resident_blocks(func, &resident);
+  if (e != hipSuccess) return e;
+  int grid = sc.grid > 0 ? std::min(sc.grid, resident) : resident;
+  // channels: at most one per workgroup.  Each segment is cut C ways; a part of
+  // ceil(len / C) elements holds fewer than maxvec / C + 4 whole vectors
+  // (len < (maxvec + 2) V)
+  a.channels = std::max(1, std::min(std::min(sc.channels, kMaxChannels), grid));
+  if (a.channels > 1) maxvec = maxvec / a.channels + 4;
   const int64_t tv = (int64_t)kBlock * kStepU;
   a.T = std::max<int64_t>(1, (maxvec + tv - 1) / tv);
-  // most tiles any step has
+  // most tiles any step has, per channel
   int64_t most = 0;
   for (int st = step_begin; st < step_end; ++st) {
     int nseg;
@@ -332,13 +359,9 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
     }
     most = std::max(most, (int64_t)nseg * a.T);
   }
-  const void* func = streaming(p, n, DT) ? reinterpret_cast<const void*>(&k_steps<DT, kStepU, true>)
-                                         : reinterpret_cast<const void*>(&k_steps<DT, kStepU, false>);
-  int resident = 0;
-  hipError_t e = resident_blocks(func, &resident);
-  if (e != hipSuccess) return e;
-  int grid = sc.grid > 0 ? std::min(sc.grid, resident) : resident;
-  grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, most));
+  // every channel gets the same number of workgroups, at least one
+  grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, most * a.channels));
+  grid = std::max(a.channels, grid / a.channels * a.channels);
   *grid_used = grid;
   void* args[] = {&a};
   return hipLaunchCooperativeKernel(func, dim3(grid), dim3(kBlock), args, 0, s);

@@ -12,11 +12,15 @@ namespace ra {
 
 // ---------------------------------------------------------------- workspace
 
-// Device workspace shared by the calls on one (device, stream).
+constexpr int kMaxChannels = 64;
+
+// Device workspace shared by the calls on one (device, stream).  Every word
+// that workgroups poll sits on a 128-byte line of its own.
 struct WsHeader {
-  uint32_t bar;          // grid-barrier word (self-resetting, see grid_barrier)
-  uint32_t status;       // sticky: 0 ok, else an ra_status code set on device
-  uint32_t pad[62];      // keep flags on their own cache lines
+  uint32_t status;                   // sticky: 0 ok, else an ra_status code set on device
+  uint32_t pad[31];
+  uint32_t bar[kMaxChannels][32];    // barrier word of channel h in bar[h][0]
+                                     // (self-resetting, see grid_barrier)
 };
 
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
@@ -47,9 +51,10 @@ __device__ __forceinline__ void workgroup_release_agent() {
   }
 }
 
-// Grid-wide barrier over `nblocks` co-resident workgroups.
+// Barrier over the `nblocks` co-resident workgroups that share the word `bar`
+// (the whole grid, or one channel of it).
 //
-// Every workgroup adds 1 to the barrier word except workgroup 0, which adds
+// Every workgroup adds 1 to the barrier word except one leader, which adds
 // 2^31 - (nblocks - 1); one full round therefore adds exactly 2^31, so the top
 // bit flips precisely when the last workgroup arrives and the low bits return to
 // where they were -- the word never needs resetting between rounds or calls.  A
@@ -60,17 +65,17 @@ __device__ __forceinline__ void workgroup_release_agent() {
 // constant-rate device clock; on expiry the waiter records RA_ERR_TIMEOUT (6)
 // in the sticky status word.  A workgroup also gives up as soon as it sees a
 // nonzero status.  Returns false when the caller must exit.
-__device__ __forceinline__ bool grid_barrier(WsHeader* ws, uint32_t nblocks,
-                                             uint32_t expect_extra, uint64_t limit) {
+__device__ __forceinline__ bool grid_barrier(WsHeader* ws, uint32_t* bar, bool leader,
+                                             uint32_t nblocks, uint32_t expect_extra,
+                                             uint64_t limit) {
   __shared__ int go;
   workgroup_release_agent();
   if (threadIdx.x == 0) {
-    uint32_t inc = blockIdx.x == 0 ? 0x80000000u - (nblocks + expect_extra - 1u) : 1u;
-    uint32_t old = __hip_atomic_fetch_add(&ws->bar, inc, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t inc = leader ? 0x80000000u - (nblocks + expect_extra - 1u) : 1u;
+    uint32_t old = __hip_atomic_fetch_add(bar, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint64_t t0 = now_ticks();
     int ok = 1;
-    while (((ld_relaxed(&ws->bar) ^ old) & 0x80000000u) == 0) {
+    while (((ld_relaxed(bar) ^ old) & 0x80000000u) == 0) {
       if (ld_relaxed(&ws->status) != 0) { ok = 0; break; }
       if (now_ticks() - t0 > limit) {
         __hip_atomic_store(&ws->status, 6u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

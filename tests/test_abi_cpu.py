@@ -77,7 +77,13 @@ def test_argument_errors_are_reported_before_any_gpu_work():
     assert _call([0, 0, 0], 0) == B.RA_OK
     lib = B.lib()
     assert lib.ra_reduce_scatter_ex(_ptrs(ok), 4, 16, 0, 0, B.ALGOS["tree"], None, None) == B.RA_ERR_UNSUPPORTED
-    assert lib.ra_all_gather_ex(_ptrs(ok), 4, 16, 0, B.ALGOS["fused"], None, None) == B.RA_ERR_UNSUPPORTED
+    assert lib.ra_all_gather_ex(_ptrs(ok), 4, 16, 0, B.ALGOS["ring_bidir"], None, None) == B.RA_ERR_UNSUPPORTED
+    for bad in (-1, 65):
+        o = B._options(channels=bad)
+        assert lib.ra_allreduce_ex(_ptrs(ok), 4, 16, 1, 0, B.ALGOS["ring_channels"],
+                                   ctypes.byref(o), None) == B.RA_ERR_INVALID_ARG
+        assert lib.ra_reduce_scatter_ex(_ptrs(ok), 4, 16, 1, 0, B.ALGOS["ring_channels"],
+                                        ctypes.byref(o), None) == B.RA_ERR_INVALID_ARG
     assert lib.ra_stream_copy(None, None, 16, None) == B.RA_ERR_INVALID_ARG
     assert lib.ra_stream_copy(base, base + 4096, 15, None) == B.RA_ERR_INVALID_ARG
 
@@ -90,9 +96,10 @@ def test_status_strings():
 
 
 def test_options_struct_layout():
-    # int64, int64, int32, uint32, pointer: 32 bytes with no padding
-    assert ctypes.sizeof(B.ra_options) == 32
+    # int64, int64, int32, uint32, pointer, int32, int32: 40 bytes with no padding
+    assert ctypes.sizeof(B.ra_options) == 40
     assert B.ra_options.step_ts.offset == 24
+    assert B.ra_options.channels.offset == 32
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -1,0 +1,137 @@
+"""GPU parity of the standalone phases and of the channel-split ring (through the C ABI).
+
+* FUSED reduce-scatter: the owned chunk of every rank equals the oracle's
+  ring-order fold; every other chunk is left as it was.
+* FUSED all-gather: equals the oracle's lock-step all-gather on any input
+  buffers (only owned chunks are read).
+* Any reduce-scatter followed by any all-gather equals the all-reduce.
+* RING_CHANNELS: bit-identical to the ring for every channel count and grid;
+  its reduce-scatter leaves the same partial sums as the step-by-step ring.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_all_reduce_schedule_amd import binding as B
+from ring_all_reduce_schedule_amd import inputs
+from tests.gpu_util import require_gpu, to_dev, from_dev, same_bits, first_diff
+
+pytestmark = pytest.mark.gpu
+
+PHASE_ALGOS = ["ring_step", "ring_pipelined", "ring_channels", "fused"]
+CASES = [(2, 1, "float32"), (3, 7, "int32"), (4, 4, "float32"), (5, 3, "bfloat16"),
+         (8, 1023, "bfloat16"), (9, 100_003, "bfloat16"), (9, 1_000_003, "int32"),
+         (16, 70_001, "float32"), (64, 4097, "bfloat16"), (64, 524_288, "float32")]
+
+
+@pytest.mark.parametrize("p,n,dtype", CASES)
+def test_fused_reduce_scatter_writes_owned_chunks_only(p, n, dtype):
+    require_gpu()
+    xs = inputs.make_inputs(p, n, dtype, seed=11 * p + n, sigma=1.0)
+    t = to_dev(xs, dtype)
+    print(f"[case] fused RS p={p} n={n} dtype={dtype}", flush=True)
+    B.ra_reduce_scatter_ex(t, algo="fused")
+    B.ra_stream_status()
+    got = from_dev(t, dtype)
+    for r in range(p):
+        want = oracle.rs_owned(xs, dtype, r)
+        assert same_bits(got[r], want, dtype), f"rank {r} at {first_diff(got[r], want, dtype)}"
+
+
+@pytest.mark.parametrize("p,n,dtype", CASES)
+def test_fused_all_gather_copies_owned_chunks(p, n, dtype):
+    # arbitrary buffers, not a reduce-scatter layout: only owned chunks may be read
+    require_gpu()
+    xs = inputs.make_inputs(p, n, dtype, seed=13 * p + n, sigma=1.0)
+    want, _ = oracle.all_gather(xs, dtype)
+    t = to_dev(xs, dtype)
+    print(f"[case] fused AG p={p} n={n} dtype={dtype}", flush=True)
+    B.ra_all_gather_ex(t, algo="fused")
+    B.ra_stream_status()
+    got = from_dev(t, dtype)
+    for r in range(p):
+        assert same_bits(got[r], want[r], dtype), f"rank {r} at {first_diff(got[r], want[r], dtype)}"
+
+
+@pytest.mark.parametrize("rs_algo", PHASE_ALGOS)
+@pytest.mark.parametrize("ag_algo", PHASE_ALGOS)
+def test_any_reduce_scatter_then_any_all_gather(rs_algo, ag_algo):
+    require_gpu()
+    p, n, dtype = 9, 100_003, "bfloat16"
+    xs = inputs.make_inputs(p, n, dtype, seed=17, sigma=1.0)
+    t = to_dev(xs, dtype)
+    print(f"[case] RS={rs_algo} then AG={ag_algo}", flush=True)
+    B.ra_reduce_scatter_ex(t, algo=rs_algo)
+    B.ra_all_gather_ex(t, algo=ag_algo)
+    B.ra_stream_status()
+    want = oracle.ring_fold(xs, dtype)
+    for r, g in enumerate(from_dev(t, dtype)):
+        assert same_bits(g, want, dtype), f"rank {r} at {first_diff(g, want, dtype)}"
+
+
+@pytest.mark.parametrize("channels", [1, 2, 3, 8, 13, 64])
+@pytest.mark.parametrize("p,n,dtype", [(2, 17, "float32"), (4, 4, "float32"), (5, 1023, "int32"),
+                                       (8, 70_001, "bfloat16"), (9, 1_000_003, "int32"),
+                                       (64, 4097, "bfloat16")])
+def test_channels_allreduce(channels, p, n, dtype):
+    require_gpu()
+    xs = inputs.make_inputs(p, n, dtype, seed=channels * 31 + p, sigma=1.0)
+    t = to_dev(xs, dtype)
+    print(f"[case] ring_channels C={channels} p={p} n={n} dtype={dtype}", flush=True)
+    B.ra_allreduce_ex(t, algo="ring_channels", channels=channels)
+    B.ra_stream_status()
+    want = oracle.ring_fold(xs, dtype)
+    for r, g in enumerate(from_dev(t, dtype)):
+        assert same_bits(g, want, dtype), f"rank {r} at {first_diff(g, want, dtype)}"
+
+
+@pytest.mark.parametrize("channels,grid", [(8, 8), (8, 9), (4, 37), (64, 3), (0, 0), (2, 1)])
+def test_channels_small_grids(channels, grid):
+    # grids smaller than, or not a multiple of, the channel count
+    require_gpu()
+    p, n, dtype = 8, 50_001, "float32"
+    xs = inputs.make_inputs(p, n, dtype, seed=grid, sigma=1.0)
+    t = to_dev(xs, dtype)
+    print(f"[case] ring_channels C={channels} grid={grid}", flush=True)
+    B.ra_allreduce_ex(t, algo="ring_channels", channels=channels, grid=grid)
+    B.ra_stream_status()
+    want = oracle.ring_fold(xs, dtype)
+    assert all(same_bits(g, want, dtype) for g in from_dev(t, dtype))
+
+
+@pytest.mark.parametrize("channels", [1, 8])
+def test_channels_reduce_scatter_leaves_partials(channels):
+    require_gpu()
+    p, n, dtype = 9, 100_003, "float32"
+    xs = inputs.make_inputs(p, n, dtype, seed=23, sigma=1.0)
+    t = to_dev(xs, dtype)
+    print(f"[case] ring_channels RS C={channels}", flush=True)
+    B.ra_reduce_scatter_ex(t, algo="ring_channels", channels=channels)
+    B.ra_stream_status()
+    got = from_dev(t, dtype)
+    for r in range(p):
+        want = oracle.rs_partial(xs, dtype, r)
+        assert same_bits(got[r], want, dtype), f"rank {r} at {first_diff(got[r], want, dtype)}"
+
+
+def test_channels_forced_timeout_and_timestamps():
+    require_gpu()
+    p, n = 4, 4096
+    xs = inputs.make_inputs(p, n, "float32", seed=1)
+    t = to_dev(xs, "float32")
+    print("[case] ring_channels forced timeout", flush=True)
+    B.ra_allreduce_ex(t, algo="ring_channels", channels=4, timeout_us=2000,
+                      flags=B.RA_FLAG_FORCE_TIMEOUT)
+    with pytest.raises(B.RaError) as e:
+        B.ra_stream_status()
+    assert e.value.code == B.RA_ERR_TIMEOUT
+    t = to_dev(xs, "float32")
+    ts = torch.zeros(2 * (p - 1) + 1, dtype=torch.int64, device="cuda")
+    B.ra_allreduce_ex(t, algo="ring_channels", channels=4, step_ts=ts)
+    B.ra_stream_status()
+    want = oracle.ring_fold(xs, "float32")
+    assert all(same_bits(g, want, "float32") for g in from_dev(t, "float32"))
+    v = ts.cpu().numpy()
+    assert np.all(v > 0) and np.all(np.diff(v) >= 0)

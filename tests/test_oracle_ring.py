@@ -189,6 +189,33 @@ def test_simulator_matches_closed_form(dtype, p, n):
             assert np.array_equal(after_rs[r], oracle.rs_partial(xs, dtype, r, d))
 
 
+@pytest.mark.parametrize("dtype", ["int32", "float32", "bfloat16"])
+@pytest.mark.parametrize("p,n", [(2, 9), (3, 10), (4, 4), (5, 3), (8, 1000), (9, 1003)])
+def test_rs_owned_is_simulator_owned_chunk_and_input_elsewhere(dtype, p, n):
+    # a reduce-scatter that writes only the owned chunk: that chunk equals what the
+    # lock-step simulator leaves there, every other chunk is the rank's input
+    xs = inputs.make_inputs(p, n, dtype, seed=7 * p + n, sigma=3.0)
+    bounds = oracle.chunk_bounds(n, p)
+    for d in (1, -1):
+        after_rs, _ = oracle.reduce_scatter(xs, dtype, direction=d)
+        for r in range(p):
+            got = oracle.rs_owned(xs, dtype, r, d)
+            own = oracle.owned_chunk(r, p, d)
+            for c, (lo, hi) in enumerate(bounds):
+                want = after_rs[r][lo:hi] if c == own else xs[r][lo:hi]
+                assert np.array_equal(got[lo:hi], want)
+
+
+def test_rs_owned_int32_brute_force():
+    p, n = 5, 23
+    rng = np.random.default_rng(5)
+    xs = [rng.integers(-2**31, 2**31, n, dtype=np.int64).astype(np.int32) for _ in range(p)]
+    total = np.sum(np.stack(xs).astype(np.int64), axis=0).astype(np.int32)
+    for r in range(p):
+        lo, hi = oracle.chunk_bounds(n, p)[(r + 1) % p]
+        assert np.array_equal(oracle.rs_owned(xs, "int32", r)[lo:hi], total[lo:hi])
+
+
 def test_fold_window_matches_whole():
     p, n = 9, 1003
     xs = inputs.make_inputs(p, n, "bfloat16", seed=9)
