@@ -98,13 +98,16 @@ def fill_workload(name, bufs, torch, inputs):
     torch.cuda.synchronize()
 
 
-def time_calls(fn, k, torch):
+def time_calls(fn, k, torch, flush=None):
     """Per-call durations (ms) from HIP events on the current stream, plus the
-    span from the first start to the last end."""
+    span from the first start to the last end.  `flush`, if given, runs before
+    each call, outside its events (to evict the Infinity Cache)."""
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
     torch.cuda.synchronize()
     for i in range(k):
+        if flush is not None:
+            flush()
         starts[i].record()
         fn()
         ends[i].record()
@@ -158,6 +161,69 @@ def cpu_baseline(bufs, w, sample, torch):
                        f"(p={p}, N={m:,} {w['dtype']}); rate on 2*p*S of that sample")}
 
 
+def per_workload(torch, B, inputs):
+    """Effective GB/s and % of HBM peak for every workload that fits comfortably,
+    per algorithm: fused (on its own 2pS), ring_step and tree (rated on 2pS too).
+
+    Workloads whose 2pS is below the 256 MB Infinity Cache are timed twice: with
+    a 1 GiB scratch write before every call (cold, HBM-bound) and back to back
+    (warm, partly cache-resident)."""
+    import numpy as np
+    scratch = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+
+    def flush():
+        scratch.fill_(1)
+
+    out = {}
+    for name in ("p9_int32_n1000003", "p64_bf16_1MiB", "p8_fp32_256MiB"):
+        w, bufs = alloc_workload(name, torch, B, inputs)
+        p, n, dtype = w["p"], w["n"], w["dtype"]
+        S = n * inputs.ITEMSIZE[dtype]
+        two_ps = 2 * p * S
+        rec = {"p": p, "n_per_rank": n, "dtype": dtype, "bytes_per_rank": S, "bytes_2pS": two_ps}
+        for algo in ("fused", "ring_step", "ring_channels", "tree"):
+            fn = lambda a=algo: B.ra_allreduce_ex(bufs, algo=a)
+            fn()
+            B.ra_stream_status()
+            cold, _ = time_calls(fn, 9, torch, flush=flush)
+            warm, _ = time_calls(fn, 9, torch)
+            B.ra_stream_status()
+            tc = float(np.median(cold[1:]))
+            tw = float(np.median(warm[1:]))
+            rec[algo] = {"ms_cold": round(tc, 4), "GBps_cold": round(two_ps / (tc * 1e-3) / 1e9, 1),
+                         "pct_peak_cold": round(100 * two_ps / (tc * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                         "ms_warm": round(tw, 4), "GBps_warm": round(two_ps / (tw * 1e-3) / 1e9, 1)}
+        out[name] = rec
+        del bufs
+        torch.cuda.empty_cache()
+    del scratch
+    torch.cuda.empty_cache()
+    return out
+
+
+def phase_measure(bufs, S, p, torch, B):
+    """Standalone reduce-scatter and all-gather on the workload's buffers, each
+    rated on its own byte floor: (p+1)S for the fused reduce-scatter (every rank
+    read, one owned chunk per rank written) and pS for the fused all-gather
+    (every owned chunk read once, written p-1 times)."""
+    out = {}
+    for call, algo, floor in (("reduce_scatter", "fused", (p + 1) * S),
+                              ("all_gather", "fused", p * S),
+                              ("reduce_scatter", "ring_step", (p + 1) * S),
+                              ("all_gather", "ring_step", p * S)):
+        f = B.ra_reduce_scatter_ex if call == "reduce_scatter" else B.ra_all_gather_ex
+        fn = lambda f=f, a=algo: f(bufs, algo=a)
+        fn()
+        B.ra_stream_status()
+        per, _ = time_calls(fn, 3, torch)
+        B.ra_stream_status()
+        t = sum(per) / len(per)
+        out[f"{call}_{algo}"] = {"ms": round(t, 3), "bytes_floor": floor,
+                                 "GBps_on_floor": round(floor / (t * 1e-3) / 1e9, 1),
+                                 "pct_peak": round(100 * floor / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+    return out
+
+
 def alpha_measure(torch, B, inputs):
     """Per-step latency of the step-by-step ring.
 
@@ -180,31 +246,44 @@ def alpha_measure(torch, B, inputs):
         v = ts.cpu().numpy().astype(np.float64)
         steps.append(np.diff(v) / hz * 1e6)
     out["in_kernel_step_us_p64_1KiB"] = round(float(np.median(np.concatenate(steps))), 3)
+    # the same with 8 channels: each barrier spans an eighth of the grid
+    steps = []
+    for _ in range(5):
+        B.ra_allreduce_ex(bufs, algo="ring_channels", step_ts=ts)
+        B.ra_stream_status()
+        v = ts.cpu().numpy().astype(np.float64)
+        steps.append(np.diff(v) / hz * 1e6)
+    out["in_kernel_step_us_p64_1KiB_8channels"] = round(float(np.median(np.concatenate(steps))), 3)
     fits = {}
+    algos = ("ring_step", "ring_channels", "tree", "fused")
     for p in (8, 64):
-        xs, ys, ts_tree = [], [], []
+        rows = []
         for per_rank in (4 << 10, 64 << 10, 1 << 20, 4 << 20):
             n = per_rank // 2
             bufs = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
-            per, _ = time_calls(lambda: B.ra_allreduce_ex(bufs, algo="ring_step"), 7, torch)
-            t_ring = float(np.median(per[2:])) * 1e-3
-            per, _ = time_calls(lambda: B.ra_allreduce_ex(bufs, algo="tree"), 7, torch)
-            t_tree = float(np.median(per[2:])) * 1e-3
-            xs.append(2 * (p - 1) / p * per_rank)
-            ys.append(t_ring)
-            ts_tree.append((per_rank, t_ring, t_tree))
+            row = {"S_per_rank": per_rank}
+            for algo in algos:
+                per, _ = time_calls(lambda a=algo: B.ra_allreduce_ex(bufs, algo=a), 7, torch)
+                row[f"{algo}_ms"] = round(float(np.median(per[2:])), 4)
+            rows.append(row)
             del bufs
-        A = np.stack([np.full(len(xs), 2.0 * (p - 1)), np.array(xs)], axis=1)
-        (a, inv_b), *_ = np.linalg.lstsq(A, np.array(ys), rcond=None)
+        rec = {"sizes": rows}
+        # T = 2(p-1) a + 2(p-1)/p * S / B, least squares over the sizes
+        x = np.array([2 * (p - 1) / p * r["S_per_rank"] for r in rows])
+        A = np.stack([np.full(len(x), 2.0 * (p - 1)), x], axis=1)
+        for algo in ("ring_step", "ring_channels"):
+            y = np.array([r[f"{algo}_ms"] * 1e-3 for r in rows])
+            (a, inv_b), *_ = np.linalg.lstsq(A, y, rcond=None)
+            rec[algo] = {"alpha_us": round(a * 1e6, 3),
+                         "B_GBps_per_rank": round(1.0 / inv_b / 1e9, 2) if inv_b > 0 else None}
         cross = None
-        for per_rank, tr, tt in ts_tree:
-            if tt < tr:
-                cross = per_rank
-        fits[f"p{p}"] = {"alpha_us": round(a * 1e6, 3),
-                         "B_GBps_per_rank": round(1.0 / inv_b / 1e9, 2) if inv_b > 0 else None,
-                         "ring_vs_tree_ms": [(pr, round(tr * 1e3, 4), round(tt * 1e3, 4))
-                                             for pr, tr, tt in ts_tree],
-                         "largest_S_per_rank_where_tree_wins": cross}
+        for r in rows:
+            if r["tree_ms"] < r["ring_step_ms"]:
+                cross = r["S_per_rank"]
+        rec["largest_S_per_rank_where_tree_beats_ring"] = cross
+        rec["fused_fastest_at_every_size"] = all(
+            r["fused_ms"] <= min(r[f"{a}_ms"] for a in algos) for r in rows)
+        fits[f"p{p}"] = rec
     out["fit"] = fits
     torch.cuda.empty_cache()
     return out
@@ -309,7 +388,7 @@ def main():
         log("variants")
         fill_workload(args.workload, bufs, torch, inputs)
         variants = {}
-        for algo in ("ring_step", "ring_pipelined", "ring_bidir", "tree"):
+        for algo in ("ring_step", "ring_pipelined", "ring_bidir", "ring_channels", "tree"):
             fn = lambda a=algo: B.ra_allreduce_ex(bufs, algo=a)
             fn()
             B.ra_stream_status()
@@ -318,6 +397,9 @@ def main():
             t = sum(vper) / len(vper)
             variants[algo] = {"ms": round(t, 3), "GBps_on_2pS": round(min_bytes / (t * 1e-3) / 1e9, 1)}
         result["variants"] = variants
+        log("standalone phases")
+        fill_workload(args.workload, bufs, torch, inputs)
+        result["phases"] = phase_measure(bufs, S, p, torch, B)
         log("copy ceiling")
         # the same byte count as the all-reduce, read + write, through a plain copy
         half = min_bytes // 2
@@ -338,6 +420,8 @@ def main():
     if not args.no_extras:
         del bufs
         torch.cuda.empty_cache()
+        log("per-workload rates")
+        result["per_workload"] = per_workload(torch, B, inputs)
         log("alpha")
         result["alpha"] = alpha_measure(torch, B, inputs)
         result["alpha_us"] = result["alpha"]["in_kernel_step_us_p64_1KiB"]

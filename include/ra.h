@@ -76,8 +76,9 @@ typedef enum ra_algo {
   RA_ALGO_RING_BIDIR = 2,     /* two counter-rotating rings, each on half of the buffer */
   RA_ALGO_FUSED = 3,          /* one pass: each element folded in its ring order, written to all ranks */
   RA_ALGO_TREE = 4,           /* binomial tree: reduce to rank 0, broadcast back */
-  RA_ALGO_RING_CHANNELS = 5   /* RING_STEP split into independent channels: channel h takes
+  RA_ALGO_RING_CHANNELS = 5,  /* RING_STEP split into independent channels: channel h takes
                                  part h of every chunk and synchronises only with itself */
+  RA_ALGO_AUTO = 6            /* chosen per call by ra_select_algo (all-reduce only) */
 } ra_algo;
 
 /* ra_options.flags bits */
@@ -98,7 +99,10 @@ typedef struct ra_options {
                            NULL = not recorded. */
   int32_t channels;     /* RING_CHANNELS: number of channels, 1..64; 0 = 8 (one per XCD).
                            Capped at the number of workgroups.  Other algorithms ignore it. */
-  int32_t reserved;     /* must be 0 */
+  int32_t reserved;     /* set to 0 */
+  double link_alpha_us; /* AUTO: per-step latency alpha of the link the schedule is priced
+                           for, in microseconds; 0 = no link model (see ra_select_algo) */
+  double link_GBps;     /* AUTO: per-direction link bandwidth B, in 10^9 bytes/s; 0 = none */
 } ra_options;
 
 /*
@@ -178,6 +182,25 @@ int ra_all_gather_ex(void* const* bufs, int p, int64_t n, int dtype, int algo,
  * do no work until this function has reported the error, which also clears it.
  */
 int ra_stream_status(hipStream_t stream);
+
+/*
+ * ra_select_algo -- the algorithm RA_ALGO_AUTO runs for an all-reduce of p buffers
+ * of n elements of `dtype` ([InDepth] "Trade-offs": the library picks ring or
+ * tree per call from message size and rank count; [Derive] "Where it stops
+ * scaling": the choice reverses when S/p falls to a few hundred kilobytes).
+ *   With opt->link_alpha_us > 0 and opt->link_GBps > 0: the pages' cost model for
+ *   S = n * element size bytes -- T_ring = 2(p-1) alpha + 2(p-1)/p * S/B
+ *   ([Derive] "Where it stops scaling") against T_tree = 2 ceil(log2 p) (alpha + S/B),
+ *   each tree step moving the whole buffer -- and RA_ALGO_TREE if the tree is
+ *   strictly faster, else RA_ALGO_RING_STEP.  This prices the schedule for the
+ *   given link; the chosen algorithm then runs over the p buffers in this GPU.
+ *   Otherwise (no link model): RA_ALGO_FUSED, the fastest all-reduce over buffers
+ *   that share one GPU's memory at every size and rank count measured on MI355X.
+ * Writes the ra_algo value to *algo_out.  Host only, no GPU needed.
+ * RA_ERR_INVALID_ARG for p < 1, n < 0, an unknown dtype, NULL algo_out, or a
+ * negative or non-finite link parameter; RA_ERR_UNSUPPORTED for p > RA_MAX_RANKS.
+ */
+int ra_select_algo(int p, int64_t n, int dtype, const ra_options* opt, int* algo_out);
 
 /* Static name of a status code ("RA_OK", ...). */
 const char* ra_status_string(int code);

@@ -75,6 +75,30 @@ def t_tree(p, size_bytes, bandwidth, alpha):
     return tree_steps(p) * (alpha + size_bytes / bandwidth)
 
 
+def choose_ring_or_tree(p, size_bytes, bandwidth, alpha):
+    """The algorithm the cost model favours: "tree" if T_tree < T_ring, else "ring".
+
+    [InDepth] "Trade-offs" and [Derive] "Where it stops scaling": libraries price
+    both algorithms per call and take the ring for large buffers and the tree
+    for small ones.  Ties go to the ring.
+    """
+    return "tree" if t_tree(p, size_bytes, bandwidth, alpha) < t_ring(p, size_bytes, bandwidth, alpha) else "ring"
+
+
+def ring_tree_crossover(p, bandwidth, alpha):
+    """Buffer size S* at which T_ring = T_tree (None if the tree never wins).
+
+    Setting 2(p-1)a + 2(p-1)/p S/B = 2L(a + S/B) with L = ceil(log2 p):
+    S* = B a (2(p-1) - 2L) / (2L - 2(p-1)/p).  The tree wins below S*.
+    """
+    L = math.ceil(math.log2(p)) if p > 1 else 0
+    lat = ring_steps(p) - 2 * L
+    bw = 2 * L - traffic_factor(p)
+    if lat <= 0 or bw <= 0:
+        return None
+    return bandwidth * alpha * lat / bw
+
+
 def one_memory_min_elements(n, p):
     """2pN: each of the p buffers read once and written once."""
     return 2 * p * n

@@ -23,7 +23,8 @@ RA_MAX_RANKS = 64
 RA_FLAG_FORCE_TIMEOUT = 1
 
 ALGOS = {"default": -1, "ring_step": 0, "ring_pipelined": 1, "ring_bidir": 2,
-         "fused": 3, "tree": 4, "ring_channels": 5}
+         "fused": 3, "tree": 4, "ring_channels": 5, "auto": 6}
+ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 DTYPE_NAMES = {"int32": RA_INT32, "float32": RA_FLOAT32, "bfloat16": RA_BFLOAT16}
 
 
@@ -42,7 +43,9 @@ class ra_options(ctypes.Structure):
                 ("flags", ctypes.c_uint32),
                 ("step_ts", ctypes.c_void_p),
                 ("channels", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("reserved", ctypes.c_int32),
+                ("link_alpha_us", ctypes.c_double),
+                ("link_GBps", ctypes.c_double)]
 
 
 _lib = None
@@ -62,6 +65,8 @@ _SIGNATURES = {
     "ra_all_gather_ex": (_int, [ctypes.POINTER(_vp), _int, _i64, _int, _int,
                                 ctypes.POINTER(ra_options), _vp]),
     "ra_stream_status": (_int, [_vp]),
+    "ra_select_algo": (_int, [_int, _i64, _int, ctypes.POINTER(ra_options),
+                              ctypes.POINTER(_int)]),
     "ra_status_string": (ctypes.c_char_p, [_int]),
     "ra_last_error": (ctypes.c_char_p, []),
     "ra_wallclock_hz": (_int, [ctypes.POINTER(ctypes.c_int64)]),
@@ -144,7 +149,8 @@ def _marshal(tensors):
     return ptrs, len(tensors), t0.numel(), dtype_code(t0), t0.device
 
 
-def _options(slice_elems=0, timeout_us=0, grid=0, flags=0, step_ts=None, channels=0):
+def _options(slice_elems=0, timeout_us=0, grid=0, flags=0, step_ts=None, channels=0,
+             link_alpha_us=0.0, link_GBps=0.0):
     o = ra_options()
     o.slice_elems = int(slice_elems)
     o.timeout_us = int(timeout_us)
@@ -153,6 +159,8 @@ def _options(slice_elems=0, timeout_us=0, grid=0, flags=0, step_ts=None, channel
     o.step_ts = None if step_ts is None else int(step_ts.data_ptr())
     o.channels = int(channels)
     o.reserved = 0
+    o.link_alpha_us = float(link_alpha_us)
+    o.link_GBps = float(link_GBps)
     return o
 
 
@@ -209,6 +217,15 @@ def ra_all_gather_ex(tensors, algo="default", stream=None, **opts):
     o = _options(**opts)
     return _check(lib().ra_all_gather_ex(ptrs, p, n, dt, _algo(algo), ctypes.byref(o),
                                          _stream_handle(stream, dev)))
+
+
+def ra_select_algo(p, n, dtype, **opts):
+    """Name of the algorithm RA_ALGO_AUTO would run (host only)."""
+    code = DTYPE_NAMES[dtype] if isinstance(dtype, str) else int(dtype)
+    o = _options(**opts)
+    out = ctypes.c_int(-1)
+    _check(lib().ra_select_algo(int(p), int(n), code, ctypes.byref(o), ctypes.byref(out)))
+    return ALGO_NAMES[out.value]
 
 
 def ra_stream_status(stream=None, device=None):

@@ -45,7 +45,7 @@ bool debug_on() {
   return on != 0;
 }
 
-constexpr int kLastAlgo = RA_ALGO_RING_CHANNELS;
+constexpr int kLastAlgo = RA_ALGO_AUTO;
 
 // Channels of RING_CHANNELS when the caller does not choose: one per XCD.
 constexpr int kDefaultChannels = 8;
@@ -58,6 +58,7 @@ const char* algo_name(int a) {
     case RA_ALGO_FUSED: return "fused";
     case RA_ALGO_TREE: return "tree";
     case RA_ALGO_RING_CHANNELS: return "ring_channels";
+    case RA_ALGO_AUTO: return "auto";
     default: return "?";
   }
 }
@@ -107,6 +108,25 @@ int check_channels(const ra_options* opt) {
   if (opt && (opt->channels < 0 || opt->channels > ra::kMaxChannels))
     return fail(RA_ERR_INVALID_ARG, "channels = %d, need 0..%d", opt->channels, ra::kMaxChannels);
   return RA_OK;
+}
+
+int check_link(const ra_options* opt) {
+  if (!opt) return RA_OK;
+  const double a = opt->link_alpha_us, b = opt->link_GBps;
+  if (!(a >= 0.0) || !(b >= 0.0) || a > 1e300 || b > 1e300)
+    return fail(RA_ERR_INVALID_ARG, "link_alpha_us / link_GBps must be finite and >= 0");
+  return RA_OK;
+}
+
+// The pages' latency-bandwidth model: a ring of 2(p-1) steps, each sending a
+// chunk of S/p bytes, against a binomial tree of 2 ceil(log2 p) steps, each
+// sending the whole buffer.  The ring wins ties.
+int model_choice(int p, double size_bytes, double alpha_s, double bytes_per_s) {
+  int levels = 0;
+  while ((1 << levels) < p) ++levels;
+  const double t_ring = 2.0 * (p - 1) * alpha_s + 2.0 * (p - 1) / p * size_bytes / bytes_per_s;
+  const double t_tree = 2.0 * levels * (alpha_s + size_bytes / bytes_per_s);
+  return t_tree < t_ring ? RA_ALGO_TREE : RA_ALGO_RING_STEP;
 }
 
 bool phase_algo(int algo) {
@@ -318,6 +338,10 @@ int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int 
   if (algo == RA_ALGO_DEFAULT) algo = env_algo(RA_ALGO_FUSED);
   if (algo < RA_ALGO_RING_STEP || algo > kLastAlgo)
     return fail(RA_ERR_INVALID_ARG, "unknown algo %d", algo);
+  if (algo == RA_ALGO_AUTO) {
+    rc = ra_select_algo(p, n, dtype, opt, &algo);
+    if (rc != RA_OK) return rc;
+  }
   if (p == 1 || n == 0) return RA_OK;
   if (phase_algo(algo))
     return run_ring("allreduce", bufs, p, n, dtype, algo, 0, 2 * (p - 1), opt, stream);
@@ -369,6 +393,23 @@ int ra_stream_status(hipStream_t stream) {
   e = hipMemset(hdr, 0, sizeof(ra::WsHeader));
   if (e != hipSuccess) return fail_hip(e, "clearing device status");
   return fail((int)status, "a device-side wait timed out (status %u)", status);
+}
+
+int ra_select_algo(int p, int64_t n, int dtype, const ra_options* opt, int* algo_out) {
+  if (!algo_out) return fail(RA_ERR_INVALID_ARG, "algo_out is NULL");
+  if (p < 1) return fail(RA_ERR_INVALID_ARG, "p = %d, need p >= 1", p);
+  if (p > RA_MAX_RANKS) return fail(RA_ERR_UNSUPPORTED, "p = %d exceeds RA_MAX_RANKS = %d", p, RA_MAX_RANKS);
+  if (n < 0) return fail(RA_ERR_INVALID_ARG, "n = %lld, need n >= 0", (long long)n);
+  if (dtype < RA_INT32 || dtype > RA_BFLOAT16) return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  int rc = check_link(opt);
+  if (rc != RA_OK) return rc;
+  if (opt && opt->link_alpha_us > 0.0 && opt->link_GBps > 0.0) {
+    const double size = (double)n * (double)ra::elem_bytes(dtype);
+    *algo_out = model_choice(p, size, opt->link_alpha_us * 1e-6, opt->link_GBps * 1e9);
+  } else {
+    *algo_out = RA_ALGO_FUSED;
+  }
+  return RA_OK;
 }
 
 const char* ra_status_string(int code) {

@@ -343,12 +343,9 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   // channels: at most one per workgroup.  Each segment is cut C ways; a part of
   // ceil(len / C) elements holds fewer than maxvec / C + 4 whole vectors
   // (len < (maxvec + 2) V)
-  a.channels = std::max(1, std::min(std::min(sc.channels, kMaxChannels), grid));
-  if (a.channels > 1) maxvec = maxvec / a.channels + 4;
   const int64_t tv = (int64_t)kBlock * kStepU;
-  a.T = std::max<int64_t>(1, (maxvec + tv - 1) / tv);
-  // most tiles any step has, per channel
-  int64_t most = 0;
+  // most segments any step has
+  int most_seg = 0;
   for (int st = step_begin; st < step_end; ++st) {
     int nseg;
     if (mode == kModeTree) {
@@ -357,11 +354,17 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
     } else {
       nseg = mode == kModeBidir ? 2 * p : p;
     }
-    most = std::max(most, (int64_t)nseg * a.T);
+    most_seg = std::max(most_seg, nseg);
   }
-  // every channel gets the same number of workgroups, at least one
-  grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, most * a.channels));
-  grid = std::max(a.channels, grid / a.channels * a.channels);
+  // no more workgroups than whole-segment tiles: on small buffers every extra
+  // workgroup only adds to each barrier's cost
+  const int64_t most = (int64_t)most_seg * std::max<int64_t>(1, (maxvec + tv - 1) / tv);
+  grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, most));
+  // channels share that grid, the same number of workgroups each, at least one
+  a.channels = std::max(1, std::min(std::min(sc.channels, kMaxChannels), grid));
+  grid = grid / a.channels * a.channels;
+  if (a.channels > 1) maxvec = maxvec / a.channels + 4;
+  a.T = std::max<int64_t>(1, (maxvec + tv - 1) / tv);
   *grid_used = grid;
   void* args[] = {&a};
   return hipLaunchCooperativeKernel(func, dim3(grid), dim3(kBlock), args, 0, s);

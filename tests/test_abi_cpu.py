@@ -62,7 +62,7 @@ def test_argument_errors_are_reported_before_any_gpu_work():
     assert _call(ok, -1) == B.RA_ERR_INVALID_ARG
     assert _call(ok, 16, dtype=7) == B.RA_ERR_INVALID_ARG
     assert _call(ok, 16, op=1) == B.RA_ERR_UNSUPPORTED
-    assert _call(ok, 16, algo=9) == B.RA_ERR_INVALID_ARG
+    assert _call(ok, 16, algo=99) == B.RA_ERR_INVALID_ARG
     assert _call([base + i * MiB for i in range(65)], 16) == B.RA_ERR_UNSUPPORTED
     assert _call([ok[0], 0, ok[2], ok[3]], 16) == B.RA_ERR_INVALID_ARG
     assert _call([ok[0], ok[1] + 8, ok[2], ok[3]], 16) == B.RA_ERR_MISALIGNED
@@ -96,10 +96,11 @@ def test_status_strings():
 
 
 def test_options_struct_layout():
-    # int64, int64, int32, uint32, pointer, int32, int32: 40 bytes with no padding
-    assert ctypes.sizeof(B.ra_options) == 40
+    # int64, int64, int32, uint32, pointer, int32, int32, double, double: 56 bytes
+    assert ctypes.sizeof(B.ra_options) == 56
     assert B.ra_options.step_ts.offset == 24
     assert B.ra_options.channels.offset == 32
+    assert B.ra_options.link_alpha_us.offset == 40
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
@@ -107,3 +108,38 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         B.lib()
+
+
+@pytest.mark.parametrize("p", [1, 2, 3, 4, 8, 9, 16, 64])
+def test_select_algo_follows_the_cost_model(p):
+    # the library's AUTO choice against the oracle's pricing of the same call
+    for dtype, item in (("int32", 4), ("float32", 4), ("bfloat16", 2)):
+        for n in (0, 1, 1000, 65_536, 524_288, 10**7, 8 * 10**9):
+            for alpha_us in (1.0, 10.0, 20.0):
+                for gbps in (25.0, 50.0, 450.0):
+                    s = n * item
+                    tr = oracle.cost.t_ring(p, s, gbps * 1e9, alpha_us * 1e-6)
+                    tt = oracle.cost.t_tree(p, s, gbps * 1e9, alpha_us * 1e-6)
+                    if tr > 0 and abs(tr - tt) / tr < 1e-9:
+                        continue        # a tie up to rounding: either answer is right
+                    want = oracle.cost.choose_ring_or_tree(p, s, gbps * 1e9, alpha_us * 1e-6)
+                    got = B.ra_select_algo(p, n, dtype, link_alpha_us=alpha_us, link_GBps=gbps)
+                    assert got == {"ring": "ring_step", "tree": "tree"}[want], (p, n, dtype, alpha_us, gbps)
+    # no link model: the one-memory fused pass
+    assert B.ra_select_algo(p, 1 << 20, "bfloat16") == "fused"
+
+
+def test_select_algo_errors():
+    lib = B.lib()
+    out = ctypes.c_int()
+    for args, code in [((0, 16, 1), B.RA_ERR_INVALID_ARG), ((4, -1, 1), B.RA_ERR_INVALID_ARG),
+                       ((4, 16, 9), B.RA_ERR_INVALID_ARG), ((65, 16, 1), B.RA_ERR_UNSUPPORTED)]:
+        assert lib.ra_select_algo(*args, None, ctypes.byref(out)) == code
+    assert lib.ra_select_algo(4, 16, 1, None, None) == B.RA_ERR_INVALID_ARG
+    for a, b in ((-1.0, 50.0), (10.0, -5.0), (float("nan"), 50.0), (float("inf"), 50.0)):
+        o = B._options(link_alpha_us=a, link_GBps=b)
+        assert lib.ra_select_algo(4, 16, 1, ctypes.byref(o), ctypes.byref(out)) == B.RA_ERR_INVALID_ARG
+    # AUTO is an all-reduce choice only
+    base = 0x7f0000000000
+    ptrs = (ctypes.c_void_p * 4)(*[base + i * (1 << 20) for i in range(4)])
+    assert lib.ra_reduce_scatter_ex(ptrs, 4, 16, 1, 0, B.ALGOS["auto"], None, None) == B.RA_ERR_UNSUPPORTED

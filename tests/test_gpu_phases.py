@@ -135,3 +135,26 @@ def test_channels_forced_timeout_and_timestamps():
     assert all(same_bits(g, want, "float32") for g in from_dev(t, "float32"))
     v = ts.cpu().numpy()
     assert np.all(v > 0) and np.all(np.diff(v) >= 0)
+
+
+@pytest.mark.parametrize("p,n,link", [(64, 512, (10.0, 50.0)), (64, 524_288, (10.0, 50.0)),
+                                      (8, 1_000_003, (10.0, 50.0)), (9, 100_003, None),
+                                      (64, 4097, None)])
+def test_auto_runs_what_it_selects(p, n, link):
+    # AUTO picks by the cost model (with a link) or the fused pass (without) and
+    # the result is that algorithm's, bit for bit
+    require_gpu()
+    dtype = "bfloat16"
+    opts = {} if link is None else {"link_alpha_us": link[0], "link_GBps": link[1]}
+    chosen = B.ra_select_algo(p, n, dtype, **opts)
+    xs = inputs.make_inputs(p, n, dtype, seed=p * n % 1000, sigma=1.0)
+    t = to_dev(xs, dtype)
+    print(f"[case] auto p={p} n={n} link={link} -> {chosen}", flush=True)
+    B.ra_allreduce_ex(t, algo="auto", **opts)
+    B.ra_stream_status()
+    want = (oracle.tree_allreduce(xs, dtype)[0][0] if chosen == "tree"
+            else oracle.ring_fold(xs, dtype))
+    for r, g in enumerate(from_dev(t, dtype)):
+        assert same_bits(g, want, dtype), f"rank {r} at {first_diff(g, want, dtype)}"
+    if link is not None and p == 64 and n == 512:
+        assert chosen == "tree"        # 1 KiB per rank at p = 64: latency-bound

@@ -99,3 +99,43 @@ def test_model_is_monotone_and_bounded():
     for p in (2, 8, 64, 1024):
         assert cost.traffic_factor(p) < 2.0
         assert cost.ring_bytes_per_rank(1.0, p) < cost.ring_bytes_per_rank(1.0, 2 * p)
+
+
+def test_ring_tree_choice_printed(golden):
+    g = golden("cost_figures.json")["reversal"]
+    for c in g["cases"]:
+        assert cost.choose_ring_or_tree(c["n"], c["S_bytes"], g["B_Bps"], g["alpha_s"]) == c["winner"]
+
+
+def test_crossover_is_a_few_hundred_kilobytes_per_rank(golden):
+    g = golden("cost_figures.json")["reversal"]
+    lo, hi = g["crossover_S_per_rank_bytes_range"]
+    for p in (64, 1024):
+        for b in (g["B_Bps"], g["also_B_Bps"]):
+            s = cost.ring_tree_crossover(p, b, g["alpha_s"])
+            assert lo <= s / p <= hi
+
+
+@pytest.mark.parametrize("p", [4, 5, 8, 9, 16, 64, 1024])
+def test_crossover_closed_form_matches_bisection(p):
+    # the closed form against a root of T_ring - T_tree found by bisection
+    b, a = 50e9, 1e-5
+    f = lambda s: cost.t_ring(p, s, b, a) - cost.t_tree(p, s, b, a)
+    lo, hi = 0.0, 1e12
+    assert f(lo) > 0 > f(hi)
+    for _ in range(200):
+        mid = (lo + hi) / 2
+        lo, hi = (mid, hi) if f(mid) > 0 else (lo, mid)
+    s = cost.ring_tree_crossover(p, b, a)
+    assert s == pytest.approx(lo, rel=1e-9)
+    assert cost.choose_ring_or_tree(p, s * 0.999, b, a) == "tree"
+    assert cost.choose_ring_or_tree(p, s * 1.001, b, a) == "ring"
+
+
+@pytest.mark.parametrize("p", [2, 3])
+def test_two_or_three_ranks_never_choose_the_tree(p):
+    # p = 2: one tree level costs 2(a + S/B) against the ring's 2a + S/B; p = 3:
+    # both take 4 steps and the tree moves more bytes per step
+    assert cost.ring_tree_crossover(p, 50e9, 1e-5) is None
+    for s in (1.0, 1e3, 1e9):
+        assert cost.choose_ring_or_tree(p, s, 50e9, 1e-5) == "ring"
