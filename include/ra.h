@@ -18,9 +18,15 @@
  *          must not overlap another.  The caller owns the buffers and keeps
  *          them alive until the stream work completes.
  *  n       elements per rank (int64; buffers beyond 2^32 elements are fine).
- *  dtype   RA_INT32, RA_FLOAT32 or RA_BFLOAT16.
- *  op      RA_SUM only ([Deepinsea] "AllReduce 语义" names sum, average and
- *          max; this library implements sum).
+ *  dtype   RA_INT32, RA_FLOAT32, RA_BFLOAT16, RA_FLOAT16, RA_FLOAT64 or RA_INT64.
+ *  op      RA_SUM, RA_MAX or RA_AVG ([Deepinsea] "AllReduce 语义": sum, average,
+ *          maximum).  RA_AVG (floating-point types only) divides every rank's
+ *          contribution by p, rounded to the element type, before it enters
+ *          the sum ([InDepth] "Failure modes": pre-divide so that fp16 sums over
+ *          many ranks do not overflow); the divided terms are then summed in
+ *          exactly the order and rounding of RA_SUM.  RA_MAX is exact: a NaN
+ *          operand gives the type's canonical quiet NaN and +0 counts as larger
+ *          than -0 (IEEE 754-2019 maximum), so every algorithm gives the same bits.
  *  stream  HIP stream the work is enqueued on.  Calls return as soon as the
  *          work is enqueued.  Argument errors are reported synchronously by
  *          the return value, before anything is enqueued; errors that happen
@@ -28,10 +34,11 @@
  *          reported by ra_stream_status().
  *  In place: results overwrite the inputs.  p == 1 or n == 0 is a no-op that
  *  returns RA_OK ([InDepth] "An implementation": a world of one returns at once).
- *  Rounding: every hop's sum is rounded to the buffer type (int32 wraps modulo
- *  2^32, float32 and bfloat16 round to nearest even), which is how an in-place
+ *  Rounding: every hop's sum is rounded to the buffer type (integers wrap
+ *  modulo 2^32 or 2^64, floats round to nearest even), which is how an in-place
  *  add in the buffer's dtype accumulates ([InDepth] "An implementation";
- *  [Derive] "What interviewers probe next").
+ *  [Derive] "What interviewers probe next").  RA_FLAG_WIDE_ACCUM asks for the
+ *  other remedy of [InDepth] "Failure modes": accumulate in a wider type.
  *  Concurrency: calls on different streams may overlap; calls on one stream
  *  are ordered by the stream.  The library keeps a small device workspace per
  *  (device, stream), allocated on first use and kept until process exit.
@@ -55,16 +62,19 @@ typedef enum ra_status {
   RA_OK = 0,
   RA_ERR_INVALID_ARG = 1,  /* p < 1, n < 0, NULL pointer (buffers may be NULL when n == 0),
                               unknown enum value */
-  RA_ERR_UNSUPPORTED = 2,  /* p > RA_MAX_RANKS, op other than RA_SUM, algo not valid for the call */
+  RA_ERR_UNSUPPORTED = 2,  /* p > RA_MAX_RANKS, unknown op, RA_AVG on an integer type, algo or
+                              flag not valid for the call */
   RA_ERR_ALIAS = 3,        /* two rank buffers overlap */
   RA_ERR_MISALIGNED = 4,   /* a buffer does not start on a 16-byte boundary */
   RA_ERR_HIP = 5,          /* a HIP runtime call failed (see ra_last_error) */
   RA_ERR_TIMEOUT = 6       /* a device-side wait exceeded its time budget */
 } ra_status;
 
-typedef enum ra_dtype { RA_INT32 = 0, RA_FLOAT32 = 1, RA_BFLOAT16 = 2 } ra_dtype;
+typedef enum ra_dtype {
+  RA_INT32 = 0, RA_FLOAT32 = 1, RA_BFLOAT16 = 2, RA_FLOAT16 = 3, RA_FLOAT64 = 4, RA_INT64 = 5
+} ra_dtype;
 
-typedef enum ra_op { RA_SUM = 0 } ra_op;
+typedef enum ra_op { RA_SUM = 0, RA_MAX = 1, RA_AVG = 2 } ra_op;
 
 /* Algorithms.  All ring variants give bit-identical results to the step-by-step
  * schedule; the tree sums in a different order. */
@@ -85,6 +95,13 @@ typedef enum ra_algo {
 #define RA_FLAG_FORCE_TIMEOUT 1u  /* test hook: the first device wait expects an
                                      arrival that never comes, so it times out
                                      after timeout_us and every workgroup exits */
+#define RA_FLAG_WIDE_ACCUM 2u     /* RA_ALGO_FUSED, bfloat16 / float16 / float32 only:
+                                     every term is widened exactly to float32
+                                     (float64 for float32 buffers), the ring order
+                                     is folded there, rounding each hop to the wide
+                                     type, and the result is rounded once to the
+                                     element type.  RA_AVG divides the widened terms.
+                                     Other algorithms or dtypes: RA_ERR_UNSUPPORTED. */
 
 typedef struct ra_options {
   int64_t slice_elems;  /* RING_PIPELINED slice length in elements; 0 = library default

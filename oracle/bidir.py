@@ -20,13 +20,13 @@ def bidir_halves(n):
     return chunk_bounds(n, 2)
 
 
-def bidir_allreduce(bufs, dtype):
+def bidir_allreduce(bufs, dtype, op="sum"):
     """Returns (final buffers, buffers after both reduce-scatters)."""
     p = len(bufs)
     n = len(bufs[0])
     (a0, a1), (b0, b1) = bidir_halves(n)
-    fwd, fwd_rs, _ = ring_allreduce([np.asarray(b)[a0:a1] for b in bufs], dtype, 1)
-    rev, rev_rs, _ = ring_allreduce([np.asarray(b)[b0:b1] for b in bufs], dtype, -1)
+    fwd, fwd_rs, _ = ring_allreduce([np.asarray(b)[a0:a1] for b in bufs], dtype, 1, op=op)
+    rev, rev_rs, _ = ring_allreduce([np.asarray(b)[b0:b1] for b in bufs], dtype, -1, op=op)
     final = [np.concatenate([fwd[r], rev[r]]) for r in range(p)]
     after_rs = [np.concatenate([fwd_rs[r], rev_rs[r]]) for r in range(p)]
     return final, after_rs

@@ -18,22 +18,34 @@ reduce-scatter, rank r holds in chunk c the fold of the first ((r - c) * d mod p
 ``ring_fold_window`` evaluates the same order for a window of a buffer too large
 to hold on the host; it only needs the window's elements and their global
 positions.
+
+Other reductions (``arith``): "max" folds with the exact maximum; "avg" folds
+the terms x_q / p (each rounded to the element type) with the rounded sum;
+``wide=True`` folds widened terms in the wide type and rounds once at the end.
 """
 
 import numpy as np
 
-from .arith import add_rounded
+from .arith import combine, pre_divide, wide_term, wide_add, narrow
 from .schedule import chunk_bounds
 
 
-def _fold_terms(terms, dtype):
+def _fold_terms(terms, dtype, op="sum", wide=False):
+    p = len(terms)
+    if wide and op != "max":              # a maximum is exact: nothing to widen
+        acc = wide_term(terms[0], dtype, op, p)
+        for t in terms[1:]:
+            acc = wide_add(acc, wide_term(t, dtype, op, p), dtype)
+        return narrow(acc, dtype)
+    if op == "avg":
+        terms = [pre_divide(t, dtype, p) for t in terms]
     acc = np.array(terms[0], copy=True)
     for t in terms[1:]:
-        acc = add_rounded(acc, t, dtype)
+        acc = combine(acc, t, dtype, op)
     return acc
 
 
-def ring_fold(xs, dtype, direction=1):
+def ring_fold(xs, dtype, direction=1, op="sum", wide=False):
     """All-reduce result (identical on every rank) by folding in ring order."""
     p = len(xs)
     n = len(xs[0])
@@ -42,12 +54,15 @@ def ring_fold(xs, dtype, direction=1):
         if hi == lo:
             continue
         order = [(c + direction * k) % p for k in range(p)]
-        out[lo:hi] = _fold_terms([np.asarray(xs[q])[lo:hi] for q in order], dtype)
+        out[lo:hi] = _fold_terms([np.asarray(xs[q])[lo:hi] for q in order], dtype, op, wide)
     return out
 
 
-def rs_partial(xs, dtype, r, direction=1):
-    """Rank r's whole buffer right after the reduce-scatter, from the closed form."""
+def rs_partial(xs, dtype, r, direction=1, op="sum"):
+    """Rank r's whole buffer right after the reduce-scatter, from the closed form.
+
+    With "avg" every term is x_q / p, chunk r of rank r included (one term).
+    """
     p = len(xs)
     n = len(xs[0])
     out = np.array(xs[r], copy=True)
@@ -56,11 +71,15 @@ def rs_partial(xs, dtype, r, direction=1):
             continue
         m = ((r - c) * direction) % p + 1          # terms folded so far
         order = [(c + direction * k) % p for k in range(m)]
-        out[lo:hi] = _fold_terms([np.asarray(xs[q])[lo:hi] for q in order], dtype)
+        terms = [np.asarray(xs[q])[lo:hi] for q in order]
+        if op == "avg":
+            out[lo:hi] = _fold_terms([pre_divide(t, dtype, p) for t in terms], dtype, "sum")
+        else:
+            out[lo:hi] = _fold_terms(terms, dtype, op)
     return out
 
 
-def rs_owned(xs, dtype, r, direction=1):
+def rs_owned(xs, dtype, r, direction=1, op="sum", wide=False):
     """Rank r's buffer after a reduce-scatter that writes only the owned chunk.
 
     The owned chunk, (r + direction) mod p ([InDepth] "The schedule": rank r ends
@@ -76,11 +95,11 @@ def rs_owned(xs, dtype, r, direction=1):
     lo, hi = chunk_bounds(n, p)[c]
     if hi > lo:
         order = [(c + direction * k) % p for k in range(p)]
-        out[lo:hi] = _fold_terms([np.asarray(xs[q])[lo:hi] for q in order], dtype)
+        out[lo:hi] = _fold_terms([np.asarray(xs[q])[lo:hi] for q in order], dtype, op, wide)
     return out
 
 
-def ring_fold_window(windows, lo, n, dtype, direction=1):
+def ring_fold_window(windows, lo, n, dtype, direction=1, op="sum", wide=False):
     """Ring-order result for elements [lo, lo + len(window)) of n-element buffers.
 
     ``windows[r]`` holds rank r's elements of that window.  Each element's chunk
@@ -98,5 +117,5 @@ def ring_fold_window(windows, lo, n, dtype, direction=1):
             continue
         order = [(c + direction * k) % p for k in range(p)]
         out[a - lo:b - lo] = _fold_terms(
-            [np.asarray(windows[q])[a - lo:b - lo] for q in order], dtype)
+            [np.asarray(windows[q])[a - lo:b - lo] for q in order], dtype, op, wide)
     return out

@@ -17,6 +17,10 @@ that live in one memory (a receive-add reads the incoming chunk and the
 receiver's chunk and writes the receiver's chunk; a receive-copy reads one chunk
 and writes one), and the chunk indices sent at every step.
 
+Reductions other than the sum ([Deepinsea] "AllReduce 语义"): "max" delivers
+with the exact maximum instead of the add; "avg" divides every rank's buffer by
+p before the first step ([InDepth] "Failure modes": pre-divide), then sums.
+
 Failure: [InDepth] "Failure modes" -- a dead rank never sends, its right
 neighbour waits for a message that does not come, and the job should fail fast
 on a timeout instead of hanging.  ``dead_rank=k`` models that: rank k's messages
@@ -26,7 +30,7 @@ its inbox by raising ``RingTimeout``.
 
 import numpy as np
 
-from .arith import add_rounded
+from .arith import combine, pre_divide
 from .schedule import (chunk_bounds, rs_send_chunk, ag_send_chunk, right_of,
                        left_of)
 
@@ -61,7 +65,7 @@ def _deliver(inbox, rank, phase, step, max_polls):
     raise RingTimeout(rank, phase, step)
 
 
-def _phase(bufs, dtype, direction, phase, trace, dead_rank, max_polls):
+def _phase(bufs, dtype, direction, phase, trace, dead_rank, max_polls, op="sum"):
     p = len(bufs)
     n = len(bufs[0])
     bounds = chunk_bounds(n, p)
@@ -90,7 +94,7 @@ def _phase(bufs, dtype, direction, phase, trace, dead_rank, max_polls):
             c, data = _deliver(inbox, dst, phase, s, max_polls)
             lo, hi = bounds[c]
             if phase == "reduce-scatter":
-                bufs[dst][lo:hi] = add_rounded(bufs[dst][lo:hi], data, dtype)
+                bufs[dst][lo:hi] = combine(bufs[dst][lo:hi], data, dtype, op)
                 trace.reads += 2 * (hi - lo)
             else:
                 bufs[dst][lo:hi] = data
@@ -103,15 +107,19 @@ def _phase(bufs, dtype, direction, phase, trace, dead_rank, max_polls):
 
 
 def reduce_scatter(bufs, dtype, direction=1, dead_rank=None, max_polls=3,
-                   trace=None):
+                   trace=None, op="sum"):
     """Run the p - 1 reduce-scatter steps in place on copies of ``bufs``.
 
     Returns (buffers, trace).  Afterwards rank r holds the full sum of chunk
     ``owned_chunk(r, p, direction)``; its other chunks hold ring partial sums.
+    With op "avg" the buffers are divided by p first.
     """
+    p = len(bufs)
     bufs = [np.array(b, copy=True) for b in bufs]
-    trace = trace or Trace(len(bufs))
-    _phase(bufs, dtype, direction, "reduce-scatter", trace, dead_rank, max_polls)
+    if op == "avg":
+        bufs = [pre_divide(b, dtype, p) for b in bufs]
+    trace = trace or Trace(p)
+    _phase(bufs, dtype, direction, "reduce-scatter", trace, dead_rank, max_polls, op)
     return bufs, trace
 
 
@@ -125,7 +133,7 @@ def all_gather(bufs, dtype, direction=1, dead_rank=None, max_polls=3,
 
 
 def ring_allreduce(bufs, dtype, direction=1, dead_rank=None, max_polls=3,
-                   keep_states=False):
+                   keep_states=False, op="sum"):
     """Reduce-scatter then all-gather.
 
     Returns (final buffers, buffers after the reduce-scatter, trace); with
@@ -135,7 +143,7 @@ def ring_allreduce(bufs, dtype, direction=1, dead_rank=None, max_polls=3,
     """
     trace = Trace(len(bufs), keep_states)
     after_rs, _ = reduce_scatter(bufs, dtype, direction, dead_rank, max_polls,
-                                 trace)
+                                 trace, op)
     final, _ = all_gather(after_rs, dtype, direction, dead_rank, max_polls,
                           trace)
     return final, after_rs, trace

@@ -17,7 +17,7 @@ the sum; after the broadcast every rank holds that same value.
 
 import numpy as np
 
-from .arith import add_rounded
+from .arith import combine, pre_divide
 
 
 def tree_levels(p):
@@ -34,15 +34,20 @@ def tree_pairs(p, k):
     return [(r, r + stride) for r in range(0, p, 2 * stride) if r + stride < p]
 
 
-def tree_allreduce(bufs, dtype):
-    """Returns (final buffers, rank 0's buffer after the reduction, step count)."""
+def tree_allreduce(bufs, dtype, op="sum"):
+    """Returns (final buffers, rank 0's buffer after the reduction, step count).
+
+    "max" combines with the exact maximum; "avg" divides every buffer by p first.
+    """
     bufs = [np.array(b, copy=True) for b in bufs]
     p = len(bufs)
+    if op == "avg":
+        bufs = [pre_divide(b, dtype, p) for b in bufs]
     levels = tree_levels(p)
     steps = 0
     for k in range(levels):
         for parent, child in tree_pairs(p, k):
-            bufs[parent] = add_rounded(bufs[parent], bufs[child], dtype)
+            bufs[parent] = combine(bufs[parent], bufs[child], dtype, op)
         steps += 1
     reduced = bufs[0].copy()
     for k in reversed(range(levels)):

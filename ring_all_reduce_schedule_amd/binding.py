@@ -17,15 +17,18 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "ra.h")
 
 RA_OK, RA_ERR_INVALID_ARG, RA_ERR_UNSUPPORTED, RA_ERR_ALIAS = 0, 1, 2, 3
 RA_ERR_MISALIGNED, RA_ERR_HIP, RA_ERR_TIMEOUT = 4, 5, 6
-RA_INT32, RA_FLOAT32, RA_BFLOAT16 = 0, 1, 2
-RA_SUM = 0
+RA_INT32, RA_FLOAT32, RA_BFLOAT16, RA_FLOAT16, RA_FLOAT64, RA_INT64 = 0, 1, 2, 3, 4, 5
+RA_SUM, RA_MAX, RA_AVG = 0, 1, 2
 RA_MAX_RANKS = 64
 RA_FLAG_FORCE_TIMEOUT = 1
+RA_FLAG_WIDE_ACCUM = 2
+OPS = {"sum": RA_SUM, "max": RA_MAX, "avg": RA_AVG}
 
 ALGOS = {"default": -1, "ring_step": 0, "ring_pipelined": 1, "ring_bidir": 2,
          "fused": 3, "tree": 4, "ring_channels": 5, "auto": 6}
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
-DTYPE_NAMES = {"int32": RA_INT32, "float32": RA_FLOAT32, "bfloat16": RA_BFLOAT16}
+DTYPE_NAMES = {"int32": RA_INT32, "float32": RA_FLOAT32, "bfloat16": RA_BFLOAT16,
+               "float16": RA_FLOAT16, "float64": RA_FLOAT64, "int64": RA_INT64}
 
 
 class RaError(RuntimeError):
@@ -120,9 +123,11 @@ def _torch():
 
 def dtype_code(t):
     torch = _torch()
-    codes = {torch.int32: RA_INT32, torch.float32: RA_FLOAT32, torch.bfloat16: RA_BFLOAT16}
+    codes = {torch.int32: RA_INT32, torch.float32: RA_FLOAT32, torch.bfloat16: RA_BFLOAT16,
+             torch.float16: RA_FLOAT16, torch.float64: RA_FLOAT64, torch.int64: RA_INT64}
     if t.dtype not in codes:
-        raise TypeError(f"unsupported dtype {t.dtype} (int32, float32, bfloat16)")
+        raise TypeError(f"unsupported dtype {t.dtype} "
+                        "(int32, int64, float16, bfloat16, float32, float64)")
     return codes[t.dtype]
 
 
@@ -150,12 +155,12 @@ def _marshal(tensors):
 
 
 def _options(slice_elems=0, timeout_us=0, grid=0, flags=0, step_ts=None, channels=0,
-             link_alpha_us=0.0, link_GBps=0.0):
+             link_alpha_us=0.0, link_GBps=0.0, wide=False):
     o = ra_options()
     o.slice_elems = int(slice_elems)
     o.timeout_us = int(timeout_us)
     o.grid = int(grid)
-    o.flags = int(flags)
+    o.flags = int(flags) | (RA_FLAG_WIDE_ACCUM if wide else 0)
     o.step_ts = None if step_ts is None else int(step_ts.data_ptr())
     o.channels = int(channels)
     o.reserved = 0
@@ -169,9 +174,9 @@ def _algo(algo):
 
 
 def _op(op):
-    if op in ("sum", RA_SUM):
-        return RA_SUM
-    return int(op) if isinstance(op, int) else -1
+    if isinstance(op, str):
+        return OPS.get(op, -1)
+    return int(op)
 
 
 # ---------------------------------------------------------------- entry points

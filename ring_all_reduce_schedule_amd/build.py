@@ -2,7 +2,8 @@
 
     python -m ring_all_reduce_schedule_amd.build
 
-Every call compiles from source.  Flags:
+Every call compiles every source from scratch (one hipcc per source, in
+parallel, objects under _build/) and links them.  Flags:
   --offload-arch=gfx950              MI355X only, no other targets
   -Xclang -target-feature -Xclang -packed-fp32-ops
                                      no packed fp32 instructions are generated
@@ -31,27 +32,46 @@ def hipcc():
     return exe
 
 
-def command(out=LIB):
-    return [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-x", "hip", "-ffp-contract=off",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-unused-command-line-argument",
-            "-I", INCLUDE, "-I", CSRC,
-            *[os.path.join(CSRC, s) for s in SOURCES], "-o", out]
+BUILD = os.path.join(ROOT, "_build")
+
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+         "-ffp-contract=off",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wno-unused-command-line-argument"]
+
+
+def compile_command(src, obj):
+    return [hipcc(), *FLAGS, "-x", "hip", "-I", INCLUDE, "-I", CSRC, "-c",
+            os.path.join(CSRC, src), "-o", obj]
+
+
+def link_command(objs, out):
+    return [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", out]
+
+
+def _run(cmd):
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(" ".join(cmd) + "\n" + res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libra.so")
+    # hipcc's host pass warns that it does not know the packed-fp32 feature
+    return [ln for ln in res.stderr.splitlines() if ln.strip()
+            and "packed-fp32-ops" not in ln and "not a recognized feature" not in ln]
 
 
 def build(verbose=False):
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+    """Compile every source (in parallel) and link libra.so; always from scratch."""
+    from concurrent.futures import ThreadPoolExecutor
+    os.makedirs(BUILD, exist_ok=True)
+    objs = [os.path.join(BUILD, os.path.splitext(src)[0] + ".o") for src in SOURCES]
+    cmds = [compile_command(src, obj) for src, obj in zip(SOURCES, objs)]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libra.so")
-    # hipcc's host pass warns that it does not know the packed-fp32 feature
-    noise = [ln for ln in res.stderr.splitlines() if ln.strip()
-             and "packed-fp32-ops" not in ln and "not a recognized feature" not in ln]
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
+        noise = [ln for out in ex.map(_run, cmds) for ln in out]
+    tmp = LIB + ".tmp"
+    noise += _run(link_command(objs, tmp))
     if verbose and noise:
         sys.stderr.write("\n".join(noise) + "\n")
     os.replace(tmp, LIB)

@@ -82,7 +82,7 @@ int check_args(void* const* bufs, int p, int64_t n, int dtype) {
   if (p < 1) return fail(RA_ERR_INVALID_ARG, "p = %d, need p >= 1", p);
   if (p > RA_MAX_RANKS) return fail(RA_ERR_UNSUPPORTED, "p = %d exceeds RA_MAX_RANKS = %d", p, RA_MAX_RANKS);
   if (n < 0) return fail(RA_ERR_INVALID_ARG, "n = %lld, need n >= 0", (long long)n);
-  if (dtype < RA_INT32 || dtype > RA_BFLOAT16) return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (dtype < RA_INT32 || dtype > RA_INT64) return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if (n == 0) return RA_OK;   // nothing is accessed: empty buffers may be NULL
   for (int r = 0; r < p; ++r) {
     if (!bufs[r]) return fail(RA_ERR_INVALID_ARG, "bufs[%d] is NULL", r);
@@ -134,8 +134,27 @@ bool phase_algo(int algo) {
          algo == RA_ALGO_RING_CHANNELS || algo == RA_ALGO_FUSED;
 }
 
-int check_op(int op) {
-  if (op != RA_SUM) return fail(RA_ERR_UNSUPPORTED, "op %d not supported (only RA_SUM)", op);
+bool is_float(int dtype) {
+  return dtype == RA_FLOAT32 || dtype == RA_BFLOAT16 || dtype == RA_FLOAT16 || dtype == RA_FLOAT64;
+}
+
+int check_op(int op, int dtype) {
+  if (op < RA_SUM || op > RA_AVG) return fail(RA_ERR_UNSUPPORTED, "op %d not supported", op);
+  if (op == RA_AVG && !is_float(dtype))
+    return fail(RA_ERR_UNSUPPORTED, "RA_AVG needs a floating-point dtype, not %d", dtype);
+  return RA_OK;
+}
+
+bool wide_requested(const ra_options* opt) { return opt && (opt->flags & RA_FLAG_WIDE_ACCUM); }
+
+// Wider accumulation exists for the one-pass algorithm, for bfloat16, float16
+// and float32 (a maximum is exact, so there it changes nothing).
+int check_wide(const ra_options* opt, int dtype, int algo) {
+  if (!wide_requested(opt)) return RA_OK;
+  if (algo != RA_ALGO_FUSED)
+    return fail(RA_ERR_UNSUPPORTED, "RA_FLAG_WIDE_ACCUM needs RA_ALGO_FUSED");
+  if (dtype != RA_FLOAT32 && dtype != RA_BFLOAT16 && dtype != RA_FLOAT16)
+    return fail(RA_ERR_UNSUPPORTED, "RA_FLAG_WIDE_ACCUM needs bfloat16, float16 or float32");
   return RA_OK;
 }
 
@@ -235,7 +254,7 @@ void debug_line(const char* call, int algo, int p, int64_t n, int dtype, int gri
 
 // Run phases [hop_begin, hop_end) (0..p-2 reduce-scatter, p-1..2p-3 all-gather)
 // with a ring algorithm.
-int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, int algo,
+int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
              int hop_begin, int hop_end, const ra_options* opt, hipStream_t s) {
   if (algo == RA_ALGO_FUSED) {
     // the fused pass covers whole phases only
@@ -243,7 +262,7 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
     ra::RankPtrs P;
     fill_ptrs(bufs, p, &P);
     int grid = 0;
-    hipError_t e = ra::launch_fused(P, p, n, dtype, mode, s, &grid);
+    hipError_t e = ra::launch_fused(P, p, n, dtype, op, wide_requested(opt), mode, s, &grid);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
     debug_line(call, algo, p, n, dtype, grid);
     return RA_OK;
@@ -268,12 +287,12 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
     uint32_t base = 0;
     rc = reserve_flags(w, kmax * p, s, &base);
     if (rc != RA_OK) return rc;
-    e = ra::launch_pipelined(P, p, n, dtype, hop_begin, hop_end, slice, kmax, w->flags, base,
+    e = ra::launch_pipelined(P, p, n, dtype, op, hop_begin, hop_end, slice, kmax, w->flags, base,
                              sc, s, &grid);
   } else {
     if (algo == RA_ALGO_RING_CHANNELS)
       sc.channels = opt && opt->channels > 0 ? opt->channels : kDefaultChannels;
-    e = ra::launch_steps(P, p, n, dtype, ra::kModeRing, hop_begin, hop_end, sc, s, &grid);
+    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeRing, hop_begin, hop_end, sc, s, &grid);
   }
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   debug_line(call, algo, p, n, dtype, grid);
@@ -297,15 +316,17 @@ int ra_chunk_bounds(int64_t n, int p, int64_t* starts) {
 int ra_reduce_scatter_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
                          const ra_options* opt, hipStream_t stream) {
   int rc = check_args(bufs, p, n, dtype);
-  if (rc == RA_OK) rc = check_op(op);
+  if (rc == RA_OK) rc = check_op(op, dtype);
   if (rc == RA_OK) rc = check_channels(opt);
   if (rc != RA_OK) return rc;
   if (algo == RA_ALGO_DEFAULT) algo = RA_ALGO_FUSED;
   if (!phase_algo(algo))
     return fail(RA_ERR_UNSUPPORTED,
                 "reduce-scatter runs RING_STEP, RING_PIPELINED, RING_CHANNELS or FUSED, not %d", algo);
+  rc = check_wide(opt, dtype, algo);
+  if (rc != RA_OK) return rc;
   if (p == 1 || n == 0) return RA_OK;
-  return run_ring("reduce_scatter", bufs, p, n, dtype, algo, 0, p - 1, opt, stream);
+  return run_ring("reduce_scatter", bufs, p, n, dtype, op, algo, 0, p - 1, opt, stream);
 }
 
 int ra_all_gather_ex(void* const* bufs, int p, int64_t n, int dtype, int algo,
@@ -318,7 +339,7 @@ int ra_all_gather_ex(void* const* bufs, int p, int64_t n, int dtype, int algo,
     return fail(RA_ERR_UNSUPPORTED,
                 "all-gather runs RING_STEP, RING_PIPELINED, RING_CHANNELS or FUSED, not %d", algo);
   if (p == 1 || n == 0) return RA_OK;
-  return run_ring("all_gather", bufs, p, n, dtype, algo, p - 1, 2 * (p - 1), opt, stream);
+  return run_ring("all_gather", bufs, p, n, dtype, RA_SUM, algo, p - 1, 2 * (p - 1), opt, stream);
 }
 
 int ra_reduce_scatter(void* const* bufs, int p, int64_t n, int dtype, int op, hipStream_t stream) {
@@ -332,7 +353,7 @@ int ra_all_gather(void* const* bufs, int p, int64_t n, int dtype, hipStream_t st
 int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
                     const ra_options* opt, hipStream_t stream) {
   int rc = check_args(bufs, p, n, dtype);
-  if (rc == RA_OK) rc = check_op(op);
+  if (rc == RA_OK) rc = check_op(op, dtype);
   if (rc == RA_OK) rc = check_channels(opt);
   if (rc != RA_OK) return rc;
   if (algo == RA_ALGO_DEFAULT) algo = env_algo(RA_ALGO_FUSED);
@@ -342,9 +363,11 @@ int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int 
     rc = ra_select_algo(p, n, dtype, opt, &algo);
     if (rc != RA_OK) return rc;
   }
+  rc = check_wide(opt, dtype, algo);
+  if (rc != RA_OK) return rc;
   if (p == 1 || n == 0) return RA_OK;
   if (phase_algo(algo))
-    return run_ring("allreduce", bufs, p, n, dtype, algo, 0, 2 * (p - 1), opt, stream);
+    return run_ring("allreduce", bufs, p, n, dtype, op, algo, 0, 2 * (p - 1), opt, stream);
   // bidirectional rings or tree: one cooperative launch of the step kernel
   Workspace* w = nullptr;
   rc = get_workspace(stream, &w);
@@ -357,11 +380,11 @@ int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int 
   int grid = 0;
   hipError_t e;
   if (algo == RA_ALGO_RING_BIDIR) {
-    e = ra::launch_steps(P, p, n, dtype, ra::kModeBidir, 0, 2 * (p - 1), sc, stream, &grid);
+    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeBidir, 0, 2 * (p - 1), sc, stream, &grid);
   } else {
     int levels = 0;
     while ((1 << levels) < p) ++levels;
-    e = ra::launch_steps(P, p, n, dtype, ra::kModeTree, 0, 2 * levels, sc, stream, &grid);
+    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeTree, 0, 2 * levels, sc, stream, &grid);
   }
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   debug_line("allreduce", algo, p, n, dtype, grid);
@@ -400,7 +423,7 @@ int ra_select_algo(int p, int64_t n, int dtype, const ra_options* opt, int* algo
   if (p < 1) return fail(RA_ERR_INVALID_ARG, "p = %d, need p >= 1", p);
   if (p > RA_MAX_RANKS) return fail(RA_ERR_UNSUPPORTED, "p = %d exceeds RA_MAX_RANKS = %d", p, RA_MAX_RANKS);
   if (n < 0) return fail(RA_ERR_INVALID_ARG, "n = %lld, need n >= 0", (long long)n);
-  if (dtype < RA_INT32 || dtype > RA_BFLOAT16) return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (dtype < RA_INT32 || dtype > RA_INT64) return fail(RA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   int rc = check_link(opt);
   if (rc != RA_OK) return rc;
   if (opt && opt->link_alpha_us > 0.0 && opt->link_GBps > 0.0) {

@@ -49,20 +49,69 @@ __device__ __forceinline__ int mod_p(int x, int p) {
 }
 
 // ---------------------------------------------------------------- element types
-// dtype codes match ra_dtype: 0 int32, 1 float32, 2 bfloat16.
+// dtype codes match ra_dtype: 0 int32, 1 float32, 2 bfloat16, 3 float16,
+// 4 float64, 5 int64.  op codes match ra_op: 0 sum, 1 max, 2 avg.
 
+enum Op { kSum = 0, kMax = 1, kAvg = 2 };
+
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
+// IEEE 754-2019 maximum of two floats given as values and bit patterns: a NaN
+// operand gives the canonical quiet NaN, +0 counts as larger than -0, so the
+// result does not depend on the operand order.
+template <typename B, typename F>
+__device__ __forceinline__ B max_bits(B a, B b, F va, F vb, B qnan, B sign) {
+  if (va != va || vb != vb) return qnan;
+  if (vb > va) return b;
+  if (va > vb) return a;
+  return (a & sign) ? b : a;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  f32x2 v = {f, 0.0f};
+  return (uint16_t)(__builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2)) & 0xffffu);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t x) { return (float)__builtin_bit_cast(_Float16, x); }
+__device__ __forceinline__ uint16_t f32_to_f16(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+// Per element type: V elements per 16-byte vector, storage S, and
+//   add1(a, b)   one hop of the sum, rounded to the type
+//   max1(a, b)   exact maximum
+//   div1(a, p)   a / p rounded to the type (floats: a contribution to an average)
+//   add(a, b)    add1 on every element of a 16-byte vector
+// Floats with a wide accumulation type W also have to_w (exact), from_w (one
+// rounding to nearest even) and divw (a / p rounded to W).
 template <int DT> struct Elem;
 
 template <> struct Elem<0> {                 // int32: wraps modulo 2^32
-  static constexpr int V = 4;                // elements per 16-byte vector
-  typedef uint32_t S;                        // storage of one element
+  static constexpr int V = 4;
+  typedef uint32_t S;
   __device__ static __forceinline__ u32x4 add(u32x4 a, u32x4 b) { return a + b; }
   __device__ static __forceinline__ S add1(S a, S b) { return a + b; }
+  __device__ static __forceinline__ S max1(S a, S b) { return (int32_t)a >= (int32_t)b ? a : b; }
+  __device__ static __forceinline__ S div1(S a, int) { return a; }
+};
+
+template <> struct Elem<5> {                 // int64: wraps modulo 2^64
+  static constexpr int V = 2;
+  typedef uint64_t S;
+  __device__ static __forceinline__ S add1(S a, S b) { return a + b; }
+  __device__ static __forceinline__ u32x4 add(u32x4 a, u32x4 b) {
+    return __builtin_bit_cast(u32x4, __builtin_bit_cast(u64x2, a) + __builtin_bit_cast(u64x2, b));
+  }
+  __device__ static __forceinline__ S max1(S a, S b) { return (int64_t)a >= (int64_t)b ? a : b; }
+  __device__ static __forceinline__ S div1(S a, int) { return a; }
 };
 
 template <> struct Elem<1> {                 // float32: IEEE add, nearest even
   static constexpr int V = 4;
   typedef uint32_t S;
+  typedef double W;
   __device__ static __forceinline__ u32x4 add(u32x4 a, u32x4 b) {
     f32x4 s = __builtin_bit_cast(f32x4, a) + __builtin_bit_cast(f32x4, b);
     return __builtin_bit_cast(u32x4, s);
@@ -70,13 +119,36 @@ template <> struct Elem<1> {                 // float32: IEEE add, nearest even
   __device__ static __forceinline__ S add1(S a, S b) {
     return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
   }
+  __device__ static __forceinline__ S max1(S a, S b) {
+    return max_bits<S, float>(a, b, __uint_as_float(a), __uint_as_float(b), 0x7fc00000u, 0x80000000u);
+  }
+  __device__ static __forceinline__ S div1(S a, int p) { return __float_as_uint(__uint_as_float(a) / (float)p); }
+  __device__ static __forceinline__ W to_w(S a) { return (double)__uint_as_float(a); }
+  __device__ static __forceinline__ S from_w(W w) { return __float_as_uint((float)w); }
+  __device__ static __forceinline__ W divw(W w, int p) { return w / (double)p; }
+};
+
+template <> struct Elem<4> {                 // float64: IEEE add, nearest even
+  static constexpr int V = 2;
+  typedef uint64_t S;
+  __device__ static __forceinline__ double val(S a) { return __builtin_bit_cast(double, a); }
+  __device__ static __forceinline__ S bits(double d) { return __builtin_bit_cast(S, d); }
+  __device__ static __forceinline__ u32x4 add(u32x4 a, u32x4 b) {
+    return __builtin_bit_cast(u32x4, __builtin_bit_cast(f64x2, a) + __builtin_bit_cast(f64x2, b));
+  }
+  __device__ static __forceinline__ S add1(S a, S b) { return bits(val(a) + val(b)); }
+  __device__ static __forceinline__ S max1(S a, S b) {
+    return max_bits<S, double>(a, b, val(a), val(b), 0x7ff8000000000000ull, 0x8000000000000000ull);
+  }
+  __device__ static __forceinline__ S div1(S a, int p) { return bits(val(a) / (double)p); }
 };
 
 // bfloat16: both operands widened exactly to float32 (a bf16 is the top half of
 // a float32), added in float32 (nearest even), narrowed back to bf16 (nearest
 // even) with the gfx950 packed convert.  Rounding through float32 first gives
 // the same result as rounding the exact sum once, because float32 carries more
-// than twice bf16's precision plus two bits.
+// than twice bf16's precision plus two bits.  The same holds for a quotient by
+// p <= 64 (both operands bf16 values), so div1 divides in float32.
 __device__ __forceinline__ uint32_t bf16_pair_add(uint32_t a, uint32_t b) {
   f32x2 s;
   s.x = __uint_as_float(a << 16) + __uint_as_float(b << 16);
@@ -87,6 +159,7 @@ __device__ __forceinline__ uint32_t bf16_pair_add(uint32_t a, uint32_t b) {
 template <> struct Elem<2> {
   static constexpr int V = 8;
   typedef uint16_t S;
+  typedef float W;
   __device__ static __forceinline__ u32x4 add(u32x4 a, u32x4 b) {
     u32x4 r;
     r.x = bf16_pair_add(a.x, b.x);
@@ -98,6 +171,126 @@ template <> struct Elem<2> {
   __device__ static __forceinline__ S add1(S a, S b) {
     return (S)(bf16_pair_add((uint32_t)a, (uint32_t)b) & 0xffffu);
   }
+  __device__ static __forceinline__ S max1(S a, S b) {
+    return max_bits<S, float>(a, b, bf16_to_f32(a), bf16_to_f32(b), (S)0x7fc0, (S)0x8000);
+  }
+  __device__ static __forceinline__ S div1(S a, int p) { return f32_to_bf16(bf16_to_f32(a) / (float)p); }
+  __device__ static __forceinline__ W to_w(S a) { return bf16_to_f32(a); }
+  __device__ static __forceinline__ S from_w(W w) { return f32_to_bf16(w); }
+  __device__ static __forceinline__ W divw(W w, int p) { return w / (float)p; }
+};
+
+// float16: the hardware half add rounds the exact sum once (nearest even); the
+// quotient goes through float32 as for bf16 (24 >= 2 * 11 + 2).
+template <> struct Elem<3> {
+  static constexpr int V = 8;
+  typedef uint16_t S;
+  typedef float W;
+  __device__ static __forceinline__ u32x4 add(u32x4 a, u32x4 b) {
+    return __builtin_bit_cast(u32x4, __builtin_bit_cast(f16x8, a) + __builtin_bit_cast(f16x8, b));
+  }
+  __device__ static __forceinline__ S add1(S a, S b) {
+    return __builtin_bit_cast(S, (_Float16)(__builtin_bit_cast(_Float16, a) + __builtin_bit_cast(_Float16, b)));
+  }
+  __device__ static __forceinline__ S max1(S a, S b) {
+    return max_bits<S, float>(a, b, f16_to_f32(a), f16_to_f32(b), (S)0x7e00, (S)0x8000);
+  }
+  __device__ static __forceinline__ S div1(S a, int p) { return f32_to_f16(f16_to_f32(a) / (float)p); }
+  __device__ static __forceinline__ W to_w(S a) { return f16_to_f32(a); }
+  __device__ static __forceinline__ S from_w(W w) { return f32_to_f16(w); }
+  __device__ static __forceinline__ W divw(W w, int p) { return w / (float)p; }
+};
+
+// Elements of a 16-byte vector as an array of storage words.
+template <int DT> struct Lanes {
+  typename Elem<DT>::S e[Elem<DT>::V];
+};
+template <int DT>
+__device__ __forceinline__ Lanes<DT> unpack(u32x4 v) { return __builtin_bit_cast(Lanes<DT>, v); }
+template <int DT>
+__device__ __forceinline__ u32x4 pack(const Lanes<DT>& l) { return __builtin_bit_cast(u32x4, l); }
+
+// One hop of reduction OP on a whole vector (sum and avg add; max takes the larger).
+template <int DT, int OP>
+__device__ __forceinline__ u32x4 vcomb(u32x4 a, u32x4 b) {
+  typedef Elem<DT> E;
+  if constexpr (OP == kMax) {
+    Lanes<DT> x = unpack<DT>(a), y = unpack<DT>(b);
+#pragma unroll
+    for (int i = 0; i < E::V; ++i) x.e[i] = E::max1(x.e[i], y.e[i]);
+    return pack<DT>(x);
+  } else {
+    return E::add(a, b);
+  }
+}
+template <int DT, int OP>
+__device__ __forceinline__ typename Elem<DT>::S comb1(typename Elem<DT>::S a, typename Elem<DT>::S b) {
+  if constexpr (OP == kMax) return Elem<DT>::max1(a, b);
+  else return Elem<DT>::add1(a, b);
+}
+
+// A contribution to an average: every element divided by p, rounded to the type.
+template <int DT>
+__device__ __forceinline__ u32x4 vdiv(u32x4 a, int p) {
+  Lanes<DT> x = unpack<DT>(a);
+#pragma unroll
+  for (int i = 0; i < Elem<DT>::V; ++i) x.e[i] = Elem<DT>::div1(x.e[i], p);
+  return pack<DT>(x);
+}
+
+// Folding p terms, in the order given, into one result:
+//   WIDE = false: every hop rounds to the element type (avg divides each term first)
+//   WIDE = true:  terms widened exactly to W (avg divides them there), every hop
+//                 rounds to W, the result is rounded once to the element type
+template <int DT, int OP, bool WIDE> struct Fold;
+
+template <int DT, int OP> struct Fold<DT, OP, false> {
+  typedef Elem<DT> E;
+  typedef u32x4 A;
+  typedef typename E::S A1;
+  __device__ static __forceinline__ A start(u32x4 x, int p) { return OP == kAvg ? vdiv<DT>(x, p) : x; }
+  __device__ static __forceinline__ A step(A acc, u32x4 x, int p) {
+    return vcomb<DT, OP>(acc, OP == kAvg ? vdiv<DT>(x, p) : x);
+  }
+  __device__ static __forceinline__ u32x4 finish(A acc) { return acc; }
+  __device__ static __forceinline__ A1 start1(typename E::S x, int p) { return OP == kAvg ? E::div1(x, p) : x; }
+  __device__ static __forceinline__ A1 step1(A1 acc, typename E::S x, int p) {
+    return comb1<DT, OP>(acc, OP == kAvg ? E::div1(x, p) : x);
+  }
+  __device__ static __forceinline__ typename E::S finish1(A1 acc) { return acc; }
+};
+
+template <int DT, int OP> struct Fold<DT, OP, true> {
+  typedef Elem<DT> E;
+  typedef typename E::W W;
+  struct A { W w[E::V]; };
+  typedef W A1;
+  __device__ static __forceinline__ W term(typename E::S x, int p) {
+    const W w = E::to_w(x);
+    return OP == kAvg ? E::divw(w, p) : w;
+  }
+  __device__ static __forceinline__ A start(u32x4 x, int p) {
+    const Lanes<DT> l = unpack<DT>(x);
+    A a;
+#pragma unroll
+    for (int i = 0; i < E::V; ++i) a.w[i] = term(l.e[i], p);
+    return a;
+  }
+  __device__ static __forceinline__ A step(A acc, u32x4 x, int p) {
+    const Lanes<DT> l = unpack<DT>(x);
+#pragma unroll
+    for (int i = 0; i < E::V; ++i) acc.w[i] = acc.w[i] + term(l.e[i], p);
+    return acc;
+  }
+  __device__ static __forceinline__ u32x4 finish(const A& acc) {
+    Lanes<DT> l;
+#pragma unroll
+    for (int i = 0; i < E::V; ++i) l.e[i] = E::from_w(acc.w[i]);
+    return pack<DT>(l);
+  }
+  __device__ static __forceinline__ A1 start1(typename E::S x, int p) { return term(x, p); }
+  __device__ static __forceinline__ A1 step1(A1 acc, typename E::S x, int p) { return acc + term(x, p); }
+  __device__ static __forceinline__ typename E::S finish1(A1 acc) { return E::from_w(acc); }
 };
 
 // ---------------------------------------------------------------- memory access

@@ -27,14 +27,16 @@ namespace ra {
 // "Trade-offs"), each move the least their output needs.
 enum FusedMode { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
 
-// Tile t = (chunk c, tile j of that chunk).  For every element of the tile:
-// acc = x_c; acc = acc + x_{c+1}; ...; acc = acc + x_{c+p-1} (indices mod p,
-// rounding each addition), the order in which the step-by-step ring
-// accumulates chunk c, so the bits match.
-template <int DT, int U, bool NT, int MODE>
+// Tile t = (chunk c, tile j of that chunk), one 16-byte vector per thread.
+// For every element of the tile: acc = x_c; acc = acc + x_{c+1}; ...;
+// acc = acc + x_{c+p-1} (indices mod p, rounding each addition), the order in
+// which the step-by-step ring accumulates chunk c, so the bits match.  OP and
+// WIDE choose the reduction and the accumulation type (Fold in ra_elem.h).
+template <int DT, int OP, bool WIDE, bool NT, int MODE>
 __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p, int64_t T,
                                                   int64_t ntiles) {
   typedef Elem<DT> E;
+  typedef Fold<DT, OP, WIDE> F;
   constexpr int V = E::V;
   constexpr int KB = 8;                     // ranks loaded per batch
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
@@ -43,52 +45,34 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
     const int owner = c == 0 ? p - 1 : c - 1;
     const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
     const Span sp = split_span<V>(lo, hi);
-    const int64_t tv = (int64_t)kBlock * U;
-    const int64_t t0 = sp.v0 + j * tv;
-    const int64_t t1 = t0 + tv < sp.v1 ? t0 + tv : sp.v1;
-    if (t0 < t1) {
-      int64_t v[U];
-      u32x4 acc[U];
-      const void* first = P.b[MODE == kAllGather ? owner : c];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        v[u] = t0 + u * kBlock + threadIdx.x;
-        if (v[u] < t1) acc[u] = ld16<NT>(first, v[u]);
-      }
-      if (MODE != kAllGather) {
+    const int64_t v = sp.v0 + j * kBlock + threadIdx.x;
+    if (v < sp.v1) {
+      u32x4 out;
+      if (MODE == kAllGather) {
+        out = ld16<NT>(P.b[owner], v);
+      } else {
+        typename F::A acc = F::start(ld16<NT>(P.b[c], v), p);
         for (int k0 = 1; k0 < p; k0 += KB) {
-          u32x4 x[KB][U];
+          u32x4 x[KB];
 #pragma unroll
           for (int i = 0; i < KB; ++i) {
             if (k0 + i < p) {
               int r = c + k0 + i;
               r = r >= p ? r - p : r;
-              const void* src = P.b[r];
-#pragma unroll
-              for (int u = 0; u < U; ++u)
-                if (v[u] < t1) x[i][u] = ld16<NT>(src, v[u]);
+              x[i] = ld16<NT>(P.b[r], v);
             }
           }
 #pragma unroll
           for (int i = 0; i < KB; ++i)
-            if (k0 + i < p) {
-#pragma unroll
-              for (int u = 0; u < U; ++u) acc[u] = E::add(acc[u], x[i][u]);
-            }
+            if (k0 + i < p) acc = F::step(acc, x[i], p);
         }
+        out = F::finish(acc);
       }
       if (MODE == kReduceScatter) {
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-          if (v[u] < t1) st16<NT>(P.b[owner], v[u], acc[u]);
+        st16<NT>(P.b[owner], v, out);
       } else {
-        for (int r = 0; r < p; ++r) {
-          if (MODE == kAllGather && r == owner) continue;
-          void* dst = P.b[r];
-#pragma unroll
-          for (int u = 0; u < U; ++u)
-            if (v[u] < t1) st16<NT>(dst, v[u], acc[u]);
-        }
+        for (int r = 0; r < p; ++r)
+          if (!(MODE == kAllGather && r == owner)) st16<NT>(P.b[r], v, out);
       }
     }
     if (j == 0) {
@@ -96,19 +80,23 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
       const int tt = threadIdx.x;
       if (tt < nh + nt) {
         const int64_t i = tt < nh ? lo + tt : sp.tail_lo + (tt - nh);
-        typename E::S acc = ld1<DT>(P.b[MODE == kAllGather ? owner : c], i);
-        if (MODE != kAllGather) {
+        typename E::S out;
+        if (MODE == kAllGather) {
+          out = ld1<DT>(P.b[owner], i);
+        } else {
+          typename F::A1 acc = F::start1(ld1<DT>(P.b[c], i), p);
           for (int k = 1; k < p; ++k) {
             int r = c + k;
             r = r >= p ? r - p : r;
-            acc = E::add1(acc, ld1<DT>(P.b[r], i));
+            acc = F::step1(acc, ld1<DT>(P.b[r], i), p);
           }
+          out = F::finish1(acc);
         }
         if (MODE == kReduceScatter) {
-          st1<DT>(P.b[owner], i, acc);
+          st1<DT>(P.b[owner], i, out);
         } else {
           for (int r = 0; r < p; ++r)
-            if (!(MODE == kAllGather && r == owner)) st1<DT>(P.b[r], i, acc);
+            if (!(MODE == kAllGather && r == owner)) st1<DT>(P.b[r], i, out);
         }
       }
     }
@@ -116,49 +104,70 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
 }
 
 
-// Vectors per thread.  Measured on MI355X at 8 x 16 GiB bf16: one vector per
+// One vector per thread.  Measured on MI355X at 8 x 16 GiB bf16: one vector per
 // thread with the most workgroups in flight streams best (6.40 TB/s on 2pS
 // against 6.35 with two and 6.30 with four).
-static constexpr int kFusedU = 1;
-
-template <int DT, int MODE>
-static hipError_t fused_dt(const RankPtrs& P, int p, int64_t n, hipStream_t s, int* grid_used) {
+template <int DT, int OP, bool WIDE, int MODE>
+static hipError_t fused_launch(const RankPtrs& P, int p, int64_t n, hipStream_t s, int* grid_used) {
   const int V = Elem<DT>::V;
   const ChunkGeo g = make_geo(0, n, p);
   int64_t T = 1;
   for (int c = 0; c < p; ++c) {
     const int64_t lo = host_chunk_lo(0, n, p, c), hi = host_chunk_lo(0, n, p, c + 1);
-    T = std::max<int64_t>(T, (vecs_in(lo, hi, V) + (int64_t)kBlock * kFusedU - 1) /
-                                 ((int64_t)kBlock * kFusedU));
+    T = std::max<int64_t>(T, (vecs_in(lo, hi, V) + kBlock - 1) / kBlock);
   }
   const int64_t ntiles = (int64_t)p * T;
   const int grid = (int)std::min<int64_t>(ntiles, kMaxGrid);
   *grid_used = grid;
   if (streaming(p, n, DT))
-    hipLaunchKernelGGL((k_fused<DT, kFusedU, true, MODE>), dim3(grid), dim3(kBlock), 0, s, P, g,
+    hipLaunchKernelGGL((k_fused<DT, OP, WIDE, true, MODE>), dim3(grid), dim3(kBlock), 0, s, P, g,
                        p, T, ntiles);
   else
-    hipLaunchKernelGGL((k_fused<DT, kFusedU, false, MODE>), dim3(grid), dim3(kBlock), 0, s, P, g,
+    hipLaunchKernelGGL((k_fused<DT, OP, WIDE, false, MODE>), dim3(grid), dim3(kBlock), 0, s, P, g,
                        p, T, ntiles);
   return hipGetLastError();
 }
 
+// (dtype, op, wide) combinations that exist: avg needs a float type, wide needs
+// bfloat16, float16 or float32 and a sum or an average (a maximum is exact).
+template <int DT, int MODE>
+static hipError_t fused_op(const RankPtrs& P, int p, int64_t n, int op, bool wide, hipStream_t s,
+                           int* grid_used) {
+  constexpr bool kFloat = DT == 1 || DT == 2 || DT == 3 || DT == 4;
+  constexpr bool kWide = DT == 1 || DT == 2 || DT == 3;
+  if (MODE == kAllGather) return fused_launch<DT, kSum, false, MODE>(P, p, n, s, grid_used);
+  if (op == kMax) return fused_launch<DT, kMax, false, MODE>(P, p, n, s, grid_used);
+  if constexpr (kWide) {
+    if (wide) {
+      if (op == kAvg) return fused_launch<DT, kAvg, true, MODE>(P, p, n, s, grid_used);
+      return fused_launch<DT, kSum, true, MODE>(P, p, n, s, grid_used);
+    }
+  }
+  if constexpr (kFloat) {
+    if (op == kAvg) return fused_launch<DT, kAvg, false, MODE>(P, p, n, s, grid_used);
+  }
+  return fused_launch<DT, kSum, false, MODE>(P, p, n, s, grid_used);
+}
+
 template <int MODE>
-static hipError_t fused_mode(const RankPtrs& P, int p, int64_t n, int dtype, hipStream_t s,
-                             int* grid_used) {
+static hipError_t fused_mode(const RankPtrs& P, int p, int64_t n, int dtype, int op, bool wide,
+                             hipStream_t s, int* grid_used) {
   switch (dtype) {
-    case 0: return fused_dt<0, MODE>(P, p, n, s, grid_used);
-    case 1: return fused_dt<1, MODE>(P, p, n, s, grid_used);
-    default: return fused_dt<2, MODE>(P, p, n, s, grid_used);
+    case 0: return fused_op<0, MODE>(P, p, n, op, wide, s, grid_used);
+    case 1: return fused_op<1, MODE>(P, p, n, op, wide, s, grid_used);
+    case 2: return fused_op<2, MODE>(P, p, n, op, wide, s, grid_used);
+    case 3: return fused_op<3, MODE>(P, p, n, op, wide, s, grid_used);
+    case 4: return fused_op<4, MODE>(P, p, n, op, wide, s, grid_used);
+    default: return fused_op<5, MODE>(P, p, n, op, wide, s, grid_used);
   }
 }
 
-hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, int mode, hipStream_t s,
-                        int* grid_used) {
+hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, int op, bool wide,
+                        int mode, hipStream_t s, int* grid_used) {
   switch (mode) {
-    case kReduceScatter: return fused_mode<kReduceScatter>(P, p, n, dtype, s, grid_used);
-    case kAllGather: return fused_mode<kAllGather>(P, p, n, dtype, s, grid_used);
-    default: return fused_mode<kAllReduce>(P, p, n, dtype, s, grid_used);
+    case kReduceScatter: return fused_mode<kReduceScatter>(P, p, n, dtype, op, wide, s, grid_used);
+    case kAllGather: return fused_mode<kAllGather>(P, p, n, dtype, op, wide, s, grid_used);
+    default: return fused_mode<kAllReduce>(P, p, n, dtype, op, wide, s, grid_used);
   }
 }
 

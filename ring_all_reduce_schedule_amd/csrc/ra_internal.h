@@ -29,23 +29,24 @@ struct SyncCfg {
 
 // Launch descriptions return the number of workgroups used through *grid_used.
 
-// One pass: each element folded in its chunk's ring order.  mode 0 stores the
-// result to all ranks (all-reduce), 1 only to the chunk's owner (reduce-scatter),
-// 2 copies each owner's chunk to the other ranks (all-gather).
-hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, int mode, hipStream_t s,
-                        int* grid_used);
+// One pass: each element folded in its chunk's ring order with reduction `op`
+// (wide: accumulated in the wider type).  mode 0 stores the result to all ranks
+// (all-reduce), 1 only to the chunk's owner (reduce-scatter), 2 copies each
+// owner's chunk to the other ranks (all-gather; op and wide unused).
+hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, int op, bool wide,
+                        int mode, hipStream_t s, int* grid_used);
 
 // Steps [step_begin, step_end) of a step-by-step schedule, one cooperative launch,
 // a grid barrier between steps.  Ring/bidir: steps 0..p-2 reduce-scatter,
 // p-1..2p-3 all-gather.  Tree: L reduce levels then L broadcast levels.
-hipError_t launch_steps(const RankPtrs& P, int p, int64_t n, int dtype, StepMode mode,
+hipError_t launch_steps(const RankPtrs& P, int p, int64_t n, int dtype, int op, StepMode mode,
                         int step_begin, int step_end, const SyncCfg& sc, hipStream_t s,
                         int* grid_used);
 
 // Hops [hop_begin, hop_end) of the forward ring with chunks cut into slices of
 // `slice` elements and per-slice ready counters in `flags` (p * kmax entries,
 // all <= `base` on entry).
-hipError_t launch_pipelined(const RankPtrs& P, int p, int64_t n, int dtype, int hop_begin,
+hipError_t launch_pipelined(const RankPtrs& P, int p, int64_t n, int dtype, int op, int hop_begin,
                             int hop_end, int64_t slice, int64_t kmax, uint32_t* flags,
                             uint32_t base, const SyncCfg& sc, hipStream_t s, int* grid_used);
 
@@ -60,7 +61,13 @@ hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s)
 
 // ---------------------------------------------------------------- host helpers
 
-inline int elem_bytes(int dtype) { return dtype == 2 ? 2 : 4; }
+inline int elem_bytes(int dtype) {
+  switch (dtype) {
+    case 2: case 3: return 2;
+    case 4: case 5: return 8;
+    default: return 4;
+  }
+}
 
 inline int elems_per_vec(int dtype) { return 16 / elem_bytes(dtype); }
 

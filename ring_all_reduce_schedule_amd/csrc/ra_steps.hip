@@ -26,14 +26,25 @@ namespace ra {
 
 // ================================================================ hop on one tile
 
-// Tile j of the segment [lo, hi): dst[i] = dst[i] + src[i] (ADD) or dst[i] = src[i].
-// A tile covers kBlock*U consecutive vectors; tile 0 also takes the scalar
-// head and tail of the segment.
-template <int DT, int U, bool ADD, bool NT>
-__device__ __forceinline__ void hop_tile(const void* __restrict__ src, void* __restrict__ dst,
-                                         int64_t lo, int64_t hi, int64_t j) {
+// Tile j of the segment [lo, hi): dst[i] = dst[i] (op) src[i] (ADD) or
+// dst[i] = src[i].  A tile covers kBlock*U consecutive vectors; tile 0 also takes
+// the scalar head and tail of the segment.
+//
+// Averages ([InDepth] "Failure modes": pre-divide) divide every rank's
+// contribution by p exactly once, at the first hop that reads it: div_src and
+// div_dst say whether the incoming or the receiving value is still an undivided
+// input, and keep_src writes the divided first term back over its input, so
+// that the reduce-scatter leaves the same states as dividing every buffer first.
+struct HopFlags {
+  bool div_src, div_dst, keep_src;
+};
+
+template <int DT, int OP, int U, bool ADD, bool NT>
+__device__ __forceinline__ void hop_tile(void* __restrict__ src, void* __restrict__ dst,
+                                         int64_t lo, int64_t hi, int64_t j, int p, HopFlags f) {
   typedef Elem<DT> E;
   constexpr int V = E::V;
+  constexpr bool kDiv = OP == kAvg && ADD;
   const Span sp = split_span<V>(lo, hi);
   const int64_t tv = (int64_t)kBlock * U;
   const int64_t t0 = sp.v0 + j * tv;
@@ -49,9 +60,21 @@ __device__ __forceinline__ void hop_tile(const void* __restrict__ src, void* __r
         if (ADD) b[u] = ld16<NT>(dst, v[u]);
       }
     }
+    if (kDiv) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (f.div_src) a[u] = vdiv<DT>(a[u], p);
+        if (f.div_dst) b[u] = vdiv<DT>(b[u], p);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (v[u] < t1) st16<NT>(dst, v[u], ADD ? E::add(b[u], a[u]) : a[u]);
+      if (v[u] < t1) st16<NT>(dst, v[u], ADD ? vcomb<DT, OP>(b[u], a[u]) : a[u]);
+    if (kDiv && f.keep_src) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (v[u] < t1) st16<NT>(src, v[u], a[u]);
+    }
   }
   if (j == 0) {
     const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
@@ -59,7 +82,17 @@ __device__ __forceinline__ void hop_tile(const void* __restrict__ src, void* __r
     if (t < nh + nt) {
       const int64_t i = t < nh ? lo + t : sp.tail_lo + (t - nh);
       typename E::S x = ld1<DT>(src, i);
-      st1<DT>(dst, i, ADD ? E::add1(ld1<DT>(dst, i), x) : x);
+      if (ADD) {
+        typename E::S y = ld1<DT>(dst, i);
+        if (kDiv) {
+          if (f.div_src) x = E::div1(x, p);
+          if (f.div_dst) y = E::div1(y, p);
+        }
+        st1<DT>(dst, i, comb1<DT, OP>(y, x));
+        if (kDiv && f.keep_src) st1<DT>(src, i, x);
+      } else {
+        st1<DT>(dst, i, x);
+      }
     }
   }
 }
@@ -84,6 +117,7 @@ struct Seg {
   int64_t lo, hi;
   int src, dst;
   bool add;
+  HopFlags f;           // averages: which operands are still undivided inputs
 };
 
 // Number of segments (independent chunk transfers) in a step.
@@ -103,6 +137,11 @@ __device__ __forceinline__ int step_segments(const StepArgs& a, int step) {
 //       (forward: rank r sends chunk r + 1 - s; mirrored: chunk r - 1 + s)
 //   Tree level k, pair q, r = q * 2^(k+1): reduce adds rank r + 2^k into rank r;
 //     broadcast copies rank r over rank r + 2^k; whole buffers.
+// Averages: in the ring, the receiver's chunk is always an undivided input and
+// the sender's only at step 0 (it leaves its first sender then).  In the tree,
+// level 0 reads two inputs; at a later level k the receiver was already a
+// receiver at level 0, and the sender r + 2^k (even) was one exactly when it had
+// a level-0 partner, r + 2^k + 1 < p.
 __device__ __forceinline__ Seg step_segment(const StepArgs& a, int step, int seg) {
   Seg g;
   const int p = a.p;
@@ -115,6 +154,9 @@ __device__ __forceinline__ Seg step_segment(const StepArgs& a, int step, int seg
     g.add = reduce;
     g.src = reduce ? r + (1 << k) : r;
     g.dst = reduce ? r : r + (1 << k);
+    g.f.div_dst = k == 0;
+    g.f.div_src = k == 0 || g.src + 1 >= p;
+    g.f.keep_src = false;
     return g;
   }
   const int h = seg >= p ? 1 : 0;
@@ -127,11 +169,14 @@ __device__ __forceinline__ Seg step_segment(const StepArgs& a, int step, int seg
     g.src = mod_p(c + d * s, p);
     g.dst = mod_p(c + d * (s + 1), p);
     g.add = true;
+    g.f.div_dst = true;
+    g.f.div_src = g.f.keep_src = s == 0;
   } else {
     const int s = step - (p - 1);
     g.src = mod_p(c + d * (s - 1), p);
     g.dst = mod_p(c + d * s, p);
     g.add = false;
+    g.f.div_dst = g.f.div_src = g.f.keep_src = false;
   }
   return g;
 }
@@ -142,7 +187,7 @@ __device__ __forceinline__ Seg step_segment(const StepArgs& a, int step, int seg
 // lo + h*floor(len/C) + min(h, len mod C) -- and its workgroups wait only for
 // each other between steps.  Every element still takes the same hops in the same
 // order, so the result does not depend on C; C = 1 is the plain step-by-step ring.
-template <int DT, int U, bool NT>
+template <int DT, int OP, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
   if (ws_failed(a.ws)) return;
   const int C = a.channels;
@@ -163,9 +208,9 @@ __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
       const int64_t lo = g.lo + h * q + (h < rem ? h : rem);
       const int64_t hi = lo + q + (h < rem ? 1 : 0);
       if (g.add)
-        hop_tile<DT, U, true, NT>(a.P.b[g.src], a.P.b[g.dst], lo, hi, j);
+        hop_tile<DT, OP, U, true, NT>(a.P.b[g.src], a.P.b[g.dst], lo, hi, j, a.p, g.f);
       else
-        hop_tile<DT, U, false, NT>(a.P.b[g.src], a.P.b[g.dst], lo, hi, j);
+        hop_tile<DT, OP, U, false, NT>(a.P.b[g.src], a.P.b[g.dst], lo, hi, j, a.p, g.f);
     }
     const bool last = step + 1 == a.step_end;
     if (!last || a.step_ts || extra) {
@@ -210,7 +255,7 @@ __device__ __forceinline__ int64_t n_slices(int64_t lo, int64_t hi, int64_t slic
 // points to an earlier hop of the same slice, handled by workgroup (d-1, w), and
 // every workgroup takes its hops in increasing order, so with all workgroups
 // resident the chain always progresses.
-template <int DT, int U, bool NT>
+template <int DT, int OP, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void k_pipelined(PipeArgs a) {
   typedef Elem<DT> E;
   constexpr int V = E::V;
@@ -219,7 +264,7 @@ __global__ __launch_bounds__(kBlock) void k_pipelined(PipeArgs a) {
   const int d = blockIdx.x / a.workers;
   const int w = blockIdx.x - d * a.workers;
   const int left = d == 0 ? p - 1 : d - 1;
-  const void* src = a.P.b[left];
+  void* src = a.P.b[left];
   void* dst = a.P.b[d];
   uint32_t extra = a.expect_extra;
   for (int h = a.hop_begin; h < a.hop_end; ++h) {
@@ -242,11 +287,16 @@ __global__ __launch_bounds__(kBlock) void k_pipelined(PipeArgs a) {
       const int64_t shi = k == K - 1 ? hi : A + (k + 1) * a.slice;
       const Span sp = split_span<V>(slo, shi);
       const int64_t tv = (int64_t)kBlock * U;
+      // averages: the receiver's chunk is always an input, the sender's only
+      // at the first hop (see step_segment)
+      HopFlags hf;
+      hf.div_dst = rs;
+      hf.div_src = hf.keep_src = rs && s == 0;
       for (int64_t j = 0; sp.v0 + j * tv < sp.v1 || j == 0; ++j) {
         if (rs)
-          hop_tile<DT, U, true, NT>(src, dst, slo, shi, j);
+          hop_tile<DT, OP, U, true, NT>(src, dst, slo, shi, j, p, hf);
         else
-          hop_tile<DT, U, false, NT>(src, dst, slo, shi, j);
+          hop_tile<DT, OP, U, false, NT>(src, dst, slo, shi, j, p, hf);
       }
       post_flag(f, done + 1);
     }
@@ -299,7 +349,7 @@ static hipError_t resident_blocks(const void* func, int* out) {
 static constexpr int kStepU = 4;
 static constexpr int kPipeU = 4;
 
-template <int DT>
+template <int DT, int OP>
 static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, int step_begin,
                            int step_end, const SyncCfg& sc, hipStream_t s, int* grid_used) {
   const int V = Elem<DT>::V;
@@ -334,8 +384,9 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
                                           host_chunk_lo(off, len, p, c + 1), V));
     }
   }
-  const void* func = streaming(p, n, DT) ? reinterpret_cast<const void*>(&k_steps<DT, kStepU, true>)
-                                         : reinterpret_cast<const void*>(&k_steps<DT, kStepU, false>);
+  const void* func = streaming(p, n, DT)
+                         ? reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, true>)
+                         : reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, false>);
   int resident = 0;
   hipError_t e = resident_blocks(func, &resident);
   if (e != hipSuccess) return e;
@@ -370,13 +421,30 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   return hipLaunchCooperativeKernel(func, dim3(grid), dim3(kBlock), args, 0, s);
 }
 
-hipError_t launch_steps(const RankPtrs& P, int p, int64_t n, int dtype, StepMode mode,
+// (dtype, op) pairs that exist: avg needs a float type.
+template <int DT>
+static hipError_t steps_op(const RankPtrs& P, int p, int64_t n, int op, StepMode mode,
+                           int step_begin, int step_end, const SyncCfg& sc, hipStream_t s,
+                           int* grid_used) {
+  constexpr bool kFloat = DT == 1 || DT == 2 || DT == 3 || DT == 4;
+  if (op == kMax) return steps_dt<DT, kMax>(P, p, n, mode, step_begin, step_end, sc, s, grid_used);
+  if constexpr (kFloat) {
+    if (op == kAvg)
+      return steps_dt<DT, kAvg>(P, p, n, mode, step_begin, step_end, sc, s, grid_used);
+  }
+  return steps_dt<DT, kSum>(P, p, n, mode, step_begin, step_end, sc, s, grid_used);
+}
+
+hipError_t launch_steps(const RankPtrs& P, int p, int64_t n, int dtype, int op, StepMode mode,
                         int step_begin, int step_end, const SyncCfg& sc, hipStream_t s,
                         int* grid_used) {
   switch (dtype) {
-    case 0: return steps_dt<0>(P, p, n, mode, step_begin, step_end, sc, s, grid_used);
-    case 1: return steps_dt<1>(P, p, n, mode, step_begin, step_end, sc, s, grid_used);
-    default: return steps_dt<2>(P, p, n, mode, step_begin, step_end, sc, s, grid_used);
+    case 0: return steps_op<0>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used);
+    case 1: return steps_op<1>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used);
+    case 2: return steps_op<2>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used);
+    case 3: return steps_op<3>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used);
+    case 4: return steps_op<4>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used);
+    default: return steps_op<5>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used);
   }
 }
 
@@ -414,7 +482,7 @@ int64_t pipelined_slices_per_chunk(int p, int64_t n, int dtype, int64_t slice) {
   return kmax;
 }
 
-template <int DT>
+template <int DT, int OP>
 static hipError_t pipelined_dt(const RankPtrs& P, int p, int64_t n, int hop_begin, int hop_end,
                                int64_t slice, int64_t kmax, uint32_t* flags, uint32_t base,
                                const SyncCfg& sc, hipStream_t s, int* grid_used) {
@@ -432,8 +500,8 @@ static hipError_t pipelined_dt(const RankPtrs& P, int p, int64_t n, int hop_begi
   a.base = base;
   a.expect_extra = sc.expect_extra;
   const void* func = streaming(p, n, DT)
-                         ? reinterpret_cast<const void*>(&k_pipelined<DT, kPipeU, true>)
-                         : reinterpret_cast<const void*>(&k_pipelined<DT, kPipeU, false>);
+                         ? reinterpret_cast<const void*>(&k_pipelined<DT, OP, kPipeU, true>)
+                         : reinterpret_cast<const void*>(&k_pipelined<DT, OP, kPipeU, false>);
   int resident = 0;
   hipError_t e = resident_blocks(func, &resident);
   if (e != hipSuccess) return e;
@@ -447,14 +515,37 @@ static hipError_t pipelined_dt(const RankPtrs& P, int p, int64_t n, int hop_begi
                                     dim3(kBlock), args, 0, s);
 }
 
-hipError_t launch_pipelined(const RankPtrs& P, int p, int64_t n, int dtype, int hop_begin,
+template <int DT>
+static hipError_t pipelined_op(const RankPtrs& P, int p, int64_t n, int op, int hop_begin,
+                               int hop_end, int64_t slice, int64_t kmax, uint32_t* flags,
+                               uint32_t base, const SyncCfg& sc, hipStream_t s, int* grid_used) {
+  constexpr bool kFloat = DT == 1 || DT == 2 || DT == 3 || DT == 4;
+  if (op == kMax)
+    return pipelined_dt<DT, kMax>(P, p, n, hop_begin, hop_end, slice, kmax, flags, base, sc, s,
+                                  grid_used);
+  if constexpr (kFloat) {
+    if (op == kAvg)
+      return pipelined_dt<DT, kAvg>(P, p, n, hop_begin, hop_end, slice, kmax, flags, base, sc, s,
+                                    grid_used);
+  }
+  return pipelined_dt<DT, kSum>(P, p, n, hop_begin, hop_end, slice, kmax, flags, base, sc, s,
+                                grid_used);
+}
+
+hipError_t launch_pipelined(const RankPtrs& P, int p, int64_t n, int dtype, int op, int hop_begin,
                             int hop_end, int64_t slice, int64_t kmax, uint32_t* flags,
                             uint32_t base, const SyncCfg& sc, hipStream_t s, int* grid_used) {
+#define RA_PIPE(D) \
+  pipelined_op<D>(P, p, n, op, hop_begin, hop_end, slice, kmax, flags, base, sc, s, grid_used)
   switch (dtype) {
-    case 0: return pipelined_dt<0>(P, p, n, hop_begin, hop_end, slice, kmax, flags, base, sc, s, grid_used);
-    case 1: return pipelined_dt<1>(P, p, n, hop_begin, hop_end, slice, kmax, flags, base, sc, s, grid_used);
-    default: return pipelined_dt<2>(P, p, n, hop_begin, hop_end, slice, kmax, flags, base, sc, s, grid_used);
+    case 0: return RA_PIPE(0);
+    case 1: return RA_PIPE(1);
+    case 2: return RA_PIPE(2);
+    case 3: return RA_PIPE(3);
+    case 4: return RA_PIPE(4);
+    default: return RA_PIPE(5);
   }
+#undef RA_PIPE
 }
 
 

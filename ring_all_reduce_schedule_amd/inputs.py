@@ -37,7 +37,8 @@ WORKLOADS = {
                          sigma=1e-3, seed=3, on_device=True),
 }
 
-ITEMSIZE = {"int32": 4, "float32": 4, "bfloat16": 2}
+ITEMSIZE = {"int32": 4, "float32": 4, "bfloat16": 2, "float16": 2, "float64": 8, "int64": 8}
+INTS = ("int32", "int64")
 
 
 def f32_to_bf16_bits_torch(x):
@@ -53,17 +54,31 @@ def trace_inputs():
     return [np.float32(r + 1) * base for r in range(4)]
 
 
-def uniform_int(p, n, lo, hi, seed):
+def uniform_int(p, n, lo, hi, seed, dtype="int32"):
     rng = np.random.default_rng(seed)
-    return [rng.integers(lo, hi, n, endpoint=True, dtype=np.int32) for _ in range(p)]
+    t = np.int64 if dtype == "int64" else np.int32
+    return [rng.integers(lo, hi, n, endpoint=True, dtype=t) for _ in range(p)]
+
+
+def _store(x32, dtype):
+    """float32 draws in the storage of ``dtype`` (bf16 as bit patterns)."""
+    if dtype == "bfloat16":
+        return f32_to_bf16_bits_torch(x32)
+    if dtype == "float16":
+        return x32.astype(np.float16)
+    return x32
 
 
 def normal(p, n, sigma, seed, dtype):
+    """normal(0, sigma) draws: float64 drawn in float64, the rest as float32
+    draws narrowed to the element type (round to nearest even)."""
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(p):
-        x = rng.standard_normal(n, dtype=np.float32) * np.float32(sigma)
-        out.append(f32_to_bf16_bits_torch(x) if dtype == "bfloat16" else x)
+        if dtype == "float64":
+            out.append(rng.standard_normal(n) * float(sigma))
+        else:
+            out.append(_store(rng.standard_normal(n, dtype=np.float32) * np.float32(sigma), dtype))
     return out
 
 
@@ -72,13 +87,13 @@ def small_int_valued(p, n, dtype, lo, hi, seed):
     rng = np.random.default_rng(seed)
     out = []
     for _ in range(p):
-        v = rng.integers(lo, hi, n, endpoint=True).astype(np.float32)
-        if dtype == "int32":
-            out.append(v.astype(np.int32))
-        elif dtype == "float32":
-            out.append(v)
+        v = rng.integers(lo, hi, n, endpoint=True)
+        if dtype in INTS:
+            out.append(v.astype(np.int64 if dtype == "int64" else np.int32))
+        elif dtype == "float64":
+            out.append(v.astype(np.float64))
         else:
-            out.append(f32_to_bf16_bits_torch(v))
+            out.append(_store(v.astype(np.float32), dtype))
     return out
 
 
@@ -86,8 +101,8 @@ def make_inputs(p, n, dtype, seed, kind="normal", sigma=1.0, lo=-1000, hi=1000):
     """Generic host inputs for a (p, n, dtype) case."""
     if kind == "trace":
         return trace_inputs()
-    if dtype == "int32" or kind == "uniform_int":
-        return uniform_int(p, n, lo, hi, seed)
+    if dtype in INTS or kind == "uniform_int":
+        return uniform_int(p, n, lo, hi, seed, dtype if dtype in INTS else "int32")
     if kind == "small_int":
         return small_int_valued(p, n, dtype, lo, hi, seed)
     return normal(p, n, sigma, seed, dtype)

@@ -3,8 +3,10 @@
 import numpy as np
 import torch
 
-TORCH_DTYPE = {"int32": torch.int32, "float32": torch.float32, "bfloat16": torch.bfloat16}
-UINT_VIEW = {"int32": np.uint32, "float32": np.uint32, "bfloat16": np.uint16}
+TORCH_DTYPE = {"int32": torch.int32, "float32": torch.float32, "bfloat16": torch.bfloat16,
+               "float16": torch.float16, "float64": torch.float64, "int64": torch.int64}
+UINT_VIEW = {"int32": np.uint32, "float32": np.uint32, "bfloat16": np.uint16,
+             "float16": np.uint16, "float64": np.uint64, "int64": np.uint64}
 
 
 def require_gpu():

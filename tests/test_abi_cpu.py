@@ -61,7 +61,16 @@ def test_argument_errors_are_reported_before_any_gpu_work():
     assert _call(ok, 16, p=0) == B.RA_ERR_INVALID_ARG
     assert _call(ok, -1) == B.RA_ERR_INVALID_ARG
     assert _call(ok, 16, dtype=7) == B.RA_ERR_INVALID_ARG
-    assert _call(ok, 16, op=1) == B.RA_ERR_UNSUPPORTED
+    assert _call(ok, 16, op=7) == B.RA_ERR_UNSUPPORTED
+    # averages need a floating-point type
+    for dt in (B.RA_INT32, B.RA_INT64):
+        assert _call(ok, 16, dtype=dt, op=B.RA_AVG) == B.RA_ERR_UNSUPPORTED
+    # wide accumulation: the fused pass on bf16 / fp16 / fp32 only
+    lib = B.lib()
+    o = B._options(wide=True)
+    for algo, dt in ((B.ALGOS["ring_step"], B.RA_BFLOAT16), (B.ALGOS["tree"], B.RA_FLOAT32),
+                     (B.ALGOS["fused"], B.RA_INT32), (B.ALGOS["fused"], B.RA_FLOAT64)):
+        assert lib.ra_allreduce_ex(_ptrs(ok), 4, 16, dt, 0, algo, ctypes.byref(o), None) == B.RA_ERR_UNSUPPORTED
     assert _call(ok, 16, algo=99) == B.RA_ERR_INVALID_ARG
     assert _call([base + i * MiB for i in range(65)], 16) == B.RA_ERR_UNSUPPORTED
     assert _call([ok[0], 0, ok[2], ok[3]], 16) == B.RA_ERR_INVALID_ARG

@@ -194,7 +194,7 @@ def test_binding_rejects_mismatched_tensors():
     with pytest.raises(ValueError):
         B.ra_allreduce([a, torch.zeros(16, device="cuda", dtype=torch.int32)])
     with pytest.raises(TypeError):
-        B.ra_allreduce([torch.zeros(16, device="cuda", dtype=torch.float16)] * 2)
+        B.ra_allreduce([torch.zeros(16, device="cuda", dtype=torch.uint8) for _ in range(2)])
     with pytest.raises(B.RaError) as e:
         B.ra_allreduce([a, a])
     assert e.value.code == B.RA_ERR_ALIAS
