@@ -99,6 +99,17 @@ def ring_tree_crossover(p, bandwidth, alpha):
     return bandwidth * alpha * lat / bw
 
 
+def t_hier(p, g, size_bytes, b_intra, b_inter, alpha=0.0):
+    """Two-level ring ([InDepth] "What real libraries add", hierarchy, and the
+    worked example "flat versus hierarchical"): reduce-scatter over the g ranks of
+    a node, ring all-reduce of the S/g shard over the m = p/g nodes, all-gather
+    over the node; each phase priced like the flat ring's."""
+    m = p // g
+    intra = (g - 1) * alpha + phase_time(g, size_bytes, b_intra)
+    inter = t_ring(m, size_bytes / g, b_inter, alpha)
+    return 2 * intra + inter
+
+
 def one_memory_min_elements(n, p):
     """2pN: each of the p buffers read once and written once."""
     return 2 * p * n

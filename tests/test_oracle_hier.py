@@ -1,0 +1,95 @@
+"""Pins for the oracle's two-level (hierarchical) ring (CPU only).
+
+* The lock-step composition of ring phases equals the per-element closed form,
+  for every element type and reduction (two independent formulations).
+* g = p and g = 1 reduce to the flat ring (a single node; nodes of one rank).
+* Integer sums equal a brute-force sum.
+* A hand-derived float32 case separates the hierarchical order from the flat ring.
+* Cross-node traffic per rank is 2(m-1)/m * N/g: the flat ring's shrunk by g
+  ([InDepth] "What real libraries add", hierarchy).
+* The cost of the three phases reproduces [InDepth] "Worked example: flat
+  versus hierarchical" (0.1225 s each).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import arith, cost
+from ring_all_reduce_schedule_amd import inputs
+
+CASES = [(4, 2, 9), (6, 3, 100), (8, 4, 1003), (8, 2, 777), (9, 3, 1000), (16, 4, 257),
+         (64, 8, 4097)]
+
+
+@pytest.mark.parametrize("dtype", ["int32", "int64", "float16", "bfloat16", "float32", "float64"])
+@pytest.mark.parametrize("op", ["sum", "max", "avg"])
+@pytest.mark.parametrize("p,g,n", CASES)
+def test_simulator_matches_closed_form(dtype, op, p, g, n):
+    if op == "avg" and dtype in ("int32", "int64"):
+        pytest.skip("avg is defined for floating-point types only")
+    xs = inputs.make_inputs(p, n, dtype, seed=p * g + n, sigma=3.0)
+    final, _, _ = oracle.hier_allreduce(xs, dtype, g, op=op)
+    want = oracle.hier_fold(xs, dtype, g, op=op)
+    bits = arith.BITS[dtype]
+    for f in final:
+        assert np.array_equal(f.view(bits), want.view(bits))
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
+@pytest.mark.parametrize("p,n", [(4, 9), (8, 1003), (9, 100)])
+def test_one_node_or_one_rank_per_node_is_the_flat_ring(dtype, p, n):
+    xs = inputs.make_inputs(p, n, dtype, seed=p + n, sigma=3.0)
+    flat = oracle.ring_fold(xs, dtype)
+    for g in (1, p):
+        assert np.array_equal(oracle.hier_fold(xs, dtype, g), flat)
+        final, _, _ = oracle.hier_allreduce(xs, dtype, g)
+        assert all(np.array_equal(f, flat) for f in final)
+
+
+@pytest.mark.parametrize("p,g,n", CASES)
+def test_int32_brute_force(p, g, n):
+    rng = np.random.default_rng(p * 31 + n)
+    xs = [rng.integers(-2**31, 2**31, n, dtype=np.int64).astype(np.int32) for _ in range(p)]
+    want = np.sum(np.stack(xs).astype(np.int64), axis=0).astype(np.int32)
+    assert np.array_equal(oracle.hier_fold(xs, "int32", g), want)
+
+
+def test_hand_derived_order():
+    # p = 4, g = 2, one element: node partials are 1 + 2^-24 -> 1 (tie, even) and
+    # 2^-24 + (-1) = -(1 - 2^-24) (exact); across nodes 1 + (-(1 - 2^-24)) = 2^-24.
+    # The flat ring folds ((1 + 2^-24) + 2^-24) + (-1) = (1 + 2^-24) - 1 -> 0.
+    e = np.float32(2.0 ** -24)
+    xs = [np.array([v], np.float32) for v in (1.0, e, e, -1.0)]
+    assert oracle.hier_fold(xs, "float32", 2)[0] == e
+    assert oracle.ring_fold(xs, "float32")[0] == 0.0
+
+
+@pytest.mark.parametrize("p,g", [(8, 2), (8, 4), (16, 4), (64, 8)])
+def test_cross_node_traffic_shrinks_by_g(p, g):
+    m = p // g
+    n = p * m * 12          # g | n and m | n / g: every chunk and sub-chunk even
+    xs = inputs.make_inputs(p, n, "int32", seed=1)
+    _, cross, inner = oracle.hier_allreduce(xs, "int32", g)
+    assert cross == [2 * (m - 1) * (n // g) // m] * p
+    assert inner == [2 * (g - 1) * n // g] * p
+    # the flat ring over m nodes, each sending its whole buffer: g times more
+    assert cost.ring_sends_per_rank(n, m)[0] == g * cross[0]
+
+
+def test_worked_example_hierarchical_cost(golden):
+    g = golden("cost_figures.json")["hierarchical_phase"]
+    a, b = g["intra_rs"], g["cross_ar"]
+    nodes = b["p"]
+    per_node = a["p"]
+    total = cost.t_hier(nodes * per_node, per_node, a["S_GB"] * 1e9,
+                        a["B_GBps"] * 1e9, b["B_GBps"] * 1e9)
+    assert total == pytest.approx(3 * a["seconds"])
+    assert a["S_GB"] / per_node == pytest.approx(b["S_GB"])      # the 1.75 GB shard
+
+
+def test_layout_rejects_groups_that_do_not_divide():
+    with pytest.raises(ValueError):
+        oracle.hier_layout(8, 3)
+    m, nodes, loc = oracle.hier_layout(8, 4)
+    assert m == 2 and nodes == [[0, 1, 2, 3], [4, 5, 6, 7]] and loc[1] == [1, 5]
