@@ -88,7 +88,11 @@ typedef enum ra_algo {
   RA_ALGO_TREE = 4,           /* binomial tree: reduce to rank 0, broadcast back */
   RA_ALGO_RING_CHANNELS = 5,  /* RING_STEP split into independent channels: channel h takes
                                  part h of every chunk and synchronises only with itself */
-  RA_ALGO_AUTO = 6            /* chosen per call by ra_select_algo (all-reduce only) */
+  RA_ALGO_AUTO = 6,           /* chosen per call by ra_select_algo (all-reduce only) */
+  RA_ALGO_HIER = 7,           /* two-level ring on g ranks per node (ra_options.group): in-node
+                                 reduce-scatter, cross-node ring all-reduce of each 1/g shard,
+                                 in-node all-gather; one launch, 2(g-1) + 2(p/g-1) steps */
+  RA_ALGO_HIER_FUSED = 8      /* one pass in the same two-level order (the same bits as HIER) */
 } ra_algo;
 
 /* ra_options.flags bits */
@@ -116,7 +120,8 @@ typedef struct ra_options {
                            NULL = not recorded. */
   int32_t channels;     /* RING_CHANNELS: number of channels, 1..64; 0 = 8 (one per XCD).
                            Capped at the number of workgroups.  Other algorithms ignore it. */
-  int32_t reserved;     /* set to 0 */
+  int32_t group;        /* HIER, HIER_FUSED: ranks per node g, dividing p; 0 = the largest
+                           divisor of p that is at most 8.  Other algorithms ignore it. */
   double link_alpha_us; /* AUTO: per-step latency alpha of the link the schedule is priced
                            for, in microseconds; 0 = no link model (see ra_select_algo) */
   double link_GBps;     /* AUTO: per-direction link bandwidth B, in 10^9 bytes/s; 0 = none */
@@ -177,6 +182,13 @@ int ra_allreduce(void* const* bufs, int p, int64_t n, int dtype, int op,
  *         level k adds rank r + 2^k into rank r for r a multiple of 2^(k+1)).
  *         RING_CHANNELS: [InDepth] "What real libraries add", multiple rings or
  *         channels -- the result is the same bits as RING_STEP for any channel count.
+ *         HIER, HIER_FUSED: [InDepth] "What real libraries add", hierarchy;
+ *         [Deepinsea] "Ring vs Hierarchical".  Rank r = q*g + l is local rank l of
+ *         node q.  Element i of chunk c of the g-way partition, in piece d of that
+ *         chunk cut p/g ways, is summed over local ranks c, c+1, ... of each node
+ *         and those node sums over nodes d, d+1, ..., rounding every hop.  g = 1
+ *         and g = p give the flat ring's bits.  A group that does not divide p:
+ *         RA_ERR_INVALID_ARG.  RA_FLAG_WIDE_ACCUM is not available here.
  *   opt   may be NULL (all defaults).
  */
 int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,

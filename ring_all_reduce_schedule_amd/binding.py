@@ -25,7 +25,8 @@ RA_FLAG_WIDE_ACCUM = 2
 OPS = {"sum": RA_SUM, "max": RA_MAX, "avg": RA_AVG}
 
 ALGOS = {"default": -1, "ring_step": 0, "ring_pipelined": 1, "ring_bidir": 2,
-         "fused": 3, "tree": 4, "ring_channels": 5, "auto": 6}
+         "fused": 3, "tree": 4, "ring_channels": 5, "auto": 6, "hier": 7,
+         "hier_fused": 8}
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 DTYPE_NAMES = {"int32": RA_INT32, "float32": RA_FLOAT32, "bfloat16": RA_BFLOAT16,
                "float16": RA_FLOAT16, "float64": RA_FLOAT64, "int64": RA_INT64}
@@ -46,7 +47,7 @@ class ra_options(ctypes.Structure):
                 ("flags", ctypes.c_uint32),
                 ("step_ts", ctypes.c_void_p),
                 ("channels", ctypes.c_int32),
-                ("reserved", ctypes.c_int32),
+                ("group", ctypes.c_int32),
                 ("link_alpha_us", ctypes.c_double),
                 ("link_GBps", ctypes.c_double)]
 
@@ -155,7 +156,7 @@ def _marshal(tensors):
 
 
 def _options(slice_elems=0, timeout_us=0, grid=0, flags=0, step_ts=None, channels=0,
-             link_alpha_us=0.0, link_GBps=0.0, wide=False):
+             link_alpha_us=0.0, link_GBps=0.0, wide=False, group=0):
     o = ra_options()
     o.slice_elems = int(slice_elems)
     o.timeout_us = int(timeout_us)
@@ -163,7 +164,7 @@ def _options(slice_elems=0, timeout_us=0, grid=0, flags=0, step_ts=None, channel
     o.flags = int(flags) | (RA_FLAG_WIDE_ACCUM if wide else 0)
     o.step_ts = None if step_ts is None else int(step_ts.data_ptr())
     o.channels = int(channels)
-    o.reserved = 0
+    o.group = int(group)
     o.link_alpha_us = float(link_alpha_us)
     o.link_GBps = float(link_GBps)
     return o

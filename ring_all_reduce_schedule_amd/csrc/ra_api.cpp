@@ -45,7 +45,7 @@ bool debug_on() {
   return on != 0;
 }
 
-constexpr int kLastAlgo = RA_ALGO_AUTO;
+constexpr int kLastAlgo = RA_ALGO_HIER_FUSED;
 
 // Channels of RING_CHANNELS when the caller does not choose: one per XCD.
 constexpr int kDefaultChannels = 8;
@@ -59,6 +59,8 @@ const char* algo_name(int a) {
     case RA_ALGO_TREE: return "tree";
     case RA_ALGO_RING_CHANNELS: return "ring_channels";
     case RA_ALGO_AUTO: return "auto";
+    case RA_ALGO_HIER: return "hier";
+    case RA_ALGO_HIER_FUSED: return "hier_fused";
     default: return "?";
   }
 }
@@ -107,6 +109,22 @@ int check_args(void* const* bufs, int p, int64_t n, int dtype) {
 int check_channels(const ra_options* opt) {
   if (opt && (opt->channels < 0 || opt->channels > ra::kMaxChannels))
     return fail(RA_ERR_INVALID_ARG, "channels = %d, need 0..%d", opt->channels, ra::kMaxChannels);
+  return RA_OK;
+}
+
+// Ranks per node of the hierarchical algorithms: the caller's, or the largest
+// divisor of p that is at most 8 (eight GPUs to a node).
+int hier_group(const ra_options* opt, int p) {
+  if (opt && opt->group > 0) return opt->group;
+  for (int g = std::min(p, 8); g > 1; --g)
+    if (p % g == 0) return g;
+  return 1;
+}
+
+int check_group(const ra_options* opt, int p) {
+  if (!opt || opt->group == 0) return RA_OK;
+  if (opt->group < 0 || opt->group > p || p % opt->group != 0)
+    return fail(RA_ERR_INVALID_ARG, "group = %d must divide p = %d", opt->group, p);
   return RA_OK;
 }
 
@@ -237,6 +255,7 @@ int sync_cfg(const ra_options* opt, Workspace* w, ra::SyncCfg* sc) {
   sc->step_ts = opt ? opt->step_ts : nullptr;
   sc->grid = opt && opt->grid > 0 ? opt->grid : 0;
   sc->channels = 1;
+  sc->group = 1;
   return RA_OK;
 }
 
@@ -364,10 +383,20 @@ int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int 
     if (rc != RA_OK) return rc;
   }
   rc = check_wide(opt, dtype, algo);
+  if (rc == RA_OK) rc = check_group(opt, p);
   if (rc != RA_OK) return rc;
   if (p == 1 || n == 0) return RA_OK;
   if (phase_algo(algo))
     return run_ring("allreduce", bufs, p, n, dtype, op, algo, 0, 2 * (p - 1), opt, stream);
+  if (algo == RA_ALGO_HIER_FUSED) {
+    ra::RankPtrs P;
+    fill_ptrs(bufs, p, &P);
+    int grid = 0;
+    hipError_t e = ra::launch_fused_hier(P, p, n, dtype, op, hier_group(opt, p), stream, &grid);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    debug_line("allreduce", algo, p, n, dtype, grid);
+    return RA_OK;
+  }
   // bidirectional rings or tree: one cooperative launch of the step kernel
   Workspace* w = nullptr;
   rc = get_workspace(stream, &w);
@@ -381,6 +410,11 @@ int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int 
   hipError_t e;
   if (algo == RA_ALGO_RING_BIDIR) {
     e = ra::launch_steps(P, p, n, dtype, op, ra::kModeBidir, 0, 2 * (p - 1), sc, stream, &grid);
+  } else if (algo == RA_ALGO_HIER) {
+    sc.group = hier_group(opt, p);
+    const int m = p / sc.group;
+    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeHier, 0, 2 * (sc.group - 1) + 2 * (m - 1), sc,
+                         stream, &grid);
   } else {
     int levels = 0;
     while ((1 << levels) < p) ++levels;

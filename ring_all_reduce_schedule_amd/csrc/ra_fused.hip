@@ -162,6 +162,130 @@ static hipError_t fused_mode(const RankPtrs& P, int p, int64_t n, int dtype, int
   }
 }
 
+// ---------------------------------------------------------------- two-level order
+
+// The hierarchical ring ("Ring All-Reduce, in depth", section "What real
+// libraries add", hierarchy) in one pass.  With g ranks per node and m = p / g
+// nodes, element i lies in chunk c of the g-way partition (the shard that local
+// rank c - 1 owns after the in-node reduce-scatter) and in sub-chunk d of that
+// shard cut m ways (the piece whose cross-node ring starts at node d).  Its
+// result is
+//   A_q = x[q*g + c] (op) x[q*g + c+1] (op) ... (op) x[q*g + c+g-1]   (local indices mod g)
+//   out = A_d (op) A_{d+1} (op) ... (op) A_{d+m-1}                   (nodes mod m)
+// with every hop rounded to the element type: the order in which the in-node
+// reduce-scatter and the cross-node ring accumulate it.  Tile t = (segment
+// (c, d), tile j), one 16-byte vector per thread.
+template <int DT, int OP, bool NT>
+__global__ __launch_bounds__(kBlock) void k_fused_hier(RankPtrs P, ChunkGeo gi, int p, int G,
+                                                       int M, int64_t T, int64_t ntiles) {
+  typedef Elem<DT> E;
+  typedef Fold<DT, OP, false> F;
+  constexpr int V = E::V;
+  constexpr int KB = 8;                     // ranks loaded per batch
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int seg = (int)(t / T);
+    const int64_t j = t - (int64_t)seg * T;
+    const int c = seg / M, d = seg - c * M;
+    const int64_t clo = chunk_lo(gi, c), chi = chunk_hi(gi, c);
+    const ChunkGeo sg = {clo, (chi - clo) / M, (chi - clo) % M};
+    const int64_t lo = chunk_lo(sg, d), hi = chunk_hi(sg, d);
+    const Span sp = split_span<V>(lo, hi);
+    const int64_t v = sp.v0 + j * kBlock + threadIdx.x;
+    if (v < sp.v1) {
+      u32x4 total;
+      for (int k2 = 0; k2 < M; ++k2) {
+        const int q = d + k2 < M ? d + k2 : d + k2 - M;
+        const int base = q * G;
+        u32x4 acc = F::start(ld16<NT>(P.b[base + c], v), p);
+        for (int k0 = 1; k0 < G; k0 += KB) {
+          u32x4 x[KB];
+#pragma unroll
+          for (int i = 0; i < KB; ++i) {
+            if (k0 + i < G) {
+              int l = c + k0 + i;
+              l = l >= G ? l - G : l;
+              x[i] = ld16<NT>(P.b[base + l], v);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < KB; ++i)
+            if (k0 + i < G) acc = F::step(acc, x[i], p);
+        }
+        total = k2 == 0 ? acc : vcomb<DT, OP>(total, acc);
+      }
+      for (int r = 0; r < p; ++r) st16<NT>(P.b[r], v, total);
+    }
+    if (j == 0) {
+      const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
+      const int tt = threadIdx.x;
+      if (tt < nh + nt) {
+        const int64_t i = tt < nh ? lo + tt : sp.tail_lo + (tt - nh);
+        typename E::S total = 0;
+        for (int k2 = 0; k2 < M; ++k2) {
+          const int q = d + k2 < M ? d + k2 : d + k2 - M;
+          typename E::S acc = F::start1(ld1<DT>(P.b[q * G + c], i), p);
+          for (int k1 = 1; k1 < G; ++k1) {
+            int l = c + k1;
+            l = l >= G ? l - G : l;
+            acc = F::step1(acc, ld1<DT>(P.b[q * G + l], i), p);
+          }
+          total = k2 == 0 ? acc : comb1<DT, OP>(total, acc);
+        }
+        for (int r = 0; r < p; ++r) st1<DT>(P.b[r], i, total);
+      }
+    }
+  }
+}
+
+template <int DT, int OP>
+static hipError_t fused_hier_launch(const RankPtrs& P, int p, int64_t n, int G, hipStream_t s,
+                                    int* grid_used) {
+  const int V = Elem<DT>::V;
+  const int M = p / G;
+  const ChunkGeo gi = make_geo(0, n, G);
+  int64_t T = 1;
+  for (int c = 0; c < G; ++c) {
+    const int64_t clo = host_chunk_lo(0, n, G, c), len = host_chunk_lo(0, n, G, c + 1) - clo;
+    for (int d = 0; d < M; ++d) {
+      const int64_t lo = host_chunk_lo(clo, len, M, d), hi = host_chunk_lo(clo, len, M, d + 1);
+      T = std::max<int64_t>(T, (vecs_in(lo, hi, V) + kBlock - 1) / kBlock);
+    }
+  }
+  const int64_t ntiles = (int64_t)G * M * T;
+  const int grid = (int)std::min<int64_t>(ntiles, kMaxGrid);
+  *grid_used = grid;
+  if (streaming(p, n, DT))
+    hipLaunchKernelGGL((k_fused_hier<DT, OP, true>), dim3(grid), dim3(kBlock), 0, s, P, gi, p, G,
+                       M, T, ntiles);
+  else
+    hipLaunchKernelGGL((k_fused_hier<DT, OP, false>), dim3(grid), dim3(kBlock), 0, s, P, gi, p, G,
+                       M, T, ntiles);
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t fused_hier_op(const RankPtrs& P, int p, int64_t n, int op, int G, hipStream_t s,
+                                int* grid_used) {
+  constexpr bool kFloat = DT == 1 || DT == 2 || DT == 3 || DT == 4;
+  if (op == kMax) return fused_hier_launch<DT, kMax>(P, p, n, G, s, grid_used);
+  if constexpr (kFloat) {
+    if (op == kAvg) return fused_hier_launch<DT, kAvg>(P, p, n, G, s, grid_used);
+  }
+  return fused_hier_launch<DT, kSum>(P, p, n, G, s, grid_used);
+}
+
+hipError_t launch_fused_hier(const RankPtrs& P, int p, int64_t n, int dtype, int op, int g,
+                             hipStream_t s, int* grid_used) {
+  switch (dtype) {
+    case 0: return fused_hier_op<0>(P, p, n, op, g, s, grid_used);
+    case 1: return fused_hier_op<1>(P, p, n, op, g, s, grid_used);
+    case 2: return fused_hier_op<2>(P, p, n, op, g, s, grid_used);
+    case 3: return fused_hier_op<3>(P, p, n, op, g, s, grid_used);
+    case 4: return fused_hier_op<4>(P, p, n, op, g, s, grid_used);
+    default: return fused_hier_op<5>(P, p, n, op, g, s, grid_used);
+  }
+}
+
 hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, int op, bool wide,
                         int mode, hipStream_t s, int* grid_used) {
   switch (mode) {

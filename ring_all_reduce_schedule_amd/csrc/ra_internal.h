@@ -15,7 +15,7 @@ namespace ra {
 struct WsHeader;
 
 // Kernel families of the step-by-step schedule run by launch_steps().
-enum StepMode { kModeRing = 0, kModeBidir = 1, kModeTree = 2 };
+enum StepMode { kModeRing = 0, kModeBidir = 1, kModeTree = 2, kModeHier = 3 };
 
 // What every persistent (grid-synchronised) launch needs besides the data.
 struct SyncCfg {
@@ -25,6 +25,7 @@ struct SyncCfg {
   uint64_t* step_ts;      // optional device array of step timestamps
   int grid;               // 0 = as many workgroups as are co-resident
   int channels;           // step kernels: independent channels (1 = whole grid)
+  int group;              // kModeHier: ranks per node g (g divides p)
 };
 
 // Launch descriptions return the number of workgroups used through *grid_used.
@@ -39,9 +40,16 @@ hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, int op, 
 // Steps [step_begin, step_end) of a step-by-step schedule, one cooperative launch,
 // a grid barrier between steps.  Ring/bidir: steps 0..p-2 reduce-scatter,
 // p-1..2p-3 all-gather.  Tree: L reduce levels then L broadcast levels.
+// Hier (g = sc.group, m = p / g): g-1 intra-node reduce-scatter steps, 2(m-1)
+// inter-node all-reduce steps on the shards, g-1 intra-node all-gather steps.
 hipError_t launch_steps(const RankPtrs& P, int p, int64_t n, int dtype, int op, StepMode mode,
                         int step_begin, int step_end, const SyncCfg& sc, hipStream_t s,
                         int* grid_used);
+
+// One pass in the two-level order: node partials folded over local ranks,
+// then folded over nodes (g ranks per node), stored to every rank.
+hipError_t launch_fused_hier(const RankPtrs& P, int p, int64_t n, int dtype, int op, int g,
+                             hipStream_t s, int* grid_used);
 
 // Hops [hop_begin, hop_end) of the forward ring with chunks cut into slices of
 // `slice` elements and per-slice ready counters in `flags` (p * kmax entries,

@@ -110,6 +110,7 @@ struct StepArgs {
   uint64_t limit;
   int p, mode, step_begin, step_end, levels;
   int channels;         // C: workgroup b serves channel b mod C
+  int g, m;             // hier: ranks per node, nodes (half[0] = the g-way intra partition)
   uint32_t expect_extra;
 };
 
@@ -122,6 +123,7 @@ struct Seg {
 
 // Number of segments (independent chunk transfers) in a step.
 __device__ __forceinline__ int step_segments(const StepArgs& a, int step) {
+  if (a.mode == kModeHier) return a.p;
   if (a.mode == kModeTree) {
     const int k = step < a.levels ? step : 2 * a.levels - 1 - step;
     return (a.p - 1 - (1 << k)) / (2 << k) + 1;
@@ -142,9 +144,63 @@ __device__ __forceinline__ int step_segments(const StepArgs& a, int step) {
 // level 0 reads two inputs; at a later level k the receiver was already a
 // receiver at level 0, and the sender r + 2^k (even) was one exactly when it had
 // a level-0 partner, r + 2^k + 1 < p.
+//   Hier ("Ring All-Reduce, in depth", section "What real libraries add",
+//     hierarchy), rank = node * g + local:
+//     intra steps: segment = (node, chunk cc of the g-way partition); the node's
+//       ring over local ranks, reduce-scatter then (after the inter steps)
+//       all-gather, with the ring's rules on local indices;
+//     inter steps: segment = (local l, sub-chunk dd of l's shard), the shard
+//       being intra chunk (l + 1) mod g, which local rank l owns after the
+//       intra reduce-scatter, cut m ways; the ring over nodes on ranks
+//       node * g + l, reduce-scatter then all-gather.
+//     Averages: every input is divided during the intra reduce-scatter, so
+//     the inter steps move divided partials -- unless g = 1, when there is no
+//     intra step and the inter ring is the first to read the inputs.
+__device__ __forceinline__ Seg hier_segment(const StepArgs& a, int step, int seg) {
+  Seg g;
+  const int G = a.g, M = a.m;
+  const int inter0 = G - 1, ag0 = G - 1 + 2 * (M - 1);
+  g.f.div_dst = g.f.div_src = g.f.keep_src = false;
+  if (step < inter0 || step >= ag0) {
+    const bool rs = step < inter0;
+    const int s = rs ? step : step - ag0;
+    const int node = seg / G, cc = seg - node * G;
+    g.lo = chunk_lo(a.half[0], cc);
+    g.hi = chunk_hi(a.half[0], cc);
+    const int from = rs ? cc + s : cc + s - 1;
+    g.src = node * G + mod_p(from, G);
+    g.dst = node * G + mod_p(from + 1, G);
+    g.add = rs;
+    if (rs) {
+      g.f.div_dst = true;
+      g.f.div_src = g.f.keep_src = s == 0;
+    }
+    return g;
+  }
+  const int s2 = step - inter0;
+  const bool rs = s2 < M - 1;
+  const int s = rs ? s2 : s2 - (M - 1);
+  const int l = seg / M, dd = seg - l * M;
+  const int c = l + 1 == G ? 0 : l + 1;
+  const int64_t slo = chunk_lo(a.half[0], c), shi = chunk_hi(a.half[0], c);
+  const ChunkGeo sg = {slo, (shi - slo) / M, (shi - slo) % M};
+  g.lo = chunk_lo(sg, dd);
+  g.hi = chunk_hi(sg, dd);
+  const int from = rs ? dd + s : dd + s - 1;
+  g.src = mod_p(from, M) * G + l;
+  g.dst = mod_p(from + 1, M) * G + l;
+  g.add = rs;
+  if (rs && G == 1) {
+    g.f.div_dst = true;
+    g.f.div_src = g.f.keep_src = s == 0;
+  }
+  return g;
+}
+
 __device__ __forceinline__ Seg step_segment(const StepArgs& a, int step, int seg) {
   Seg g;
   const int p = a.p;
+  if (a.mode == kModeHier) return hier_segment(a, step, seg);
   if (a.mode == kModeTree) {
     const bool reduce = step < a.levels;
     const int k = reduce ? step : 2 * a.levels - 1 - step;
@@ -365,11 +421,18 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   a.step_end = step_end;
   a.expect_extra = sc.expect_extra;
   a.channels = 1;
+  a.g = sc.group > 0 ? sc.group : p;
+  a.m = p / a.g;
   a.levels = 0;
   while ((1 << a.levels) < p) ++a.levels;
   // segment geometry and the widest segment in vectors
   int64_t maxvec = 0;
-  if (mode == kModeTree) {
+  if (mode == kModeHier) {
+    // intra chunks are the widest segments (inter sub-chunks cut them m ways)
+    a.half[0] = a.half[1] = make_geo(0, n, a.g);
+    for (int c = 0; c < a.g; ++c)
+      maxvec = std::max(maxvec, vecs_in(host_chunk_lo(0, n, a.g, c), host_chunk_lo(0, n, a.g, c + 1), V));
+  } else if (mode == kModeTree) {
     a.half[0] = a.half[1] = make_geo(0, n, p);
     maxvec = vecs_in(0, n, V);
   } else {
@@ -399,7 +462,9 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   int most_seg = 0;
   for (int st = step_begin; st < step_end; ++st) {
     int nseg;
-    if (mode == kModeTree) {
+    if (mode == kModeHier) {
+      nseg = p;
+    } else if (mode == kModeTree) {
       const int k = st < a.levels ? st : 2 * a.levels - 1 - st;
       nseg = (p - 1 - (1 << k)) / (2 << k) + 1;
     } else {

@@ -109,6 +109,7 @@ def test_options_struct_layout():
     assert ctypes.sizeof(B.ra_options) == 56
     assert B.ra_options.step_ts.offset == 24
     assert B.ra_options.channels.offset == 32
+    assert B.ra_options.group.offset == 36
     assert B.ra_options.link_alpha_us.offset == 40
 
 
@@ -152,3 +153,17 @@ def test_select_algo_errors():
     base = 0x7f0000000000
     ptrs = (ctypes.c_void_p * 4)(*[base + i * (1 << 20) for i in range(4)])
     assert lib.ra_reduce_scatter_ex(ptrs, 4, 16, 1, 0, B.ALGOS["auto"], None, None) == B.RA_ERR_UNSUPPORTED
+
+
+def test_hier_group_errors():
+    lib = B.lib()
+    base = 0x7f0000000000
+    ptrs = (ctypes.c_void_p * 8)(*[base + i * (1 << 20) for i in range(8)])
+    for bad in (-1, 3, 9):
+        o = B._options(group=bad)
+        for algo in ("hier", "hier_fused"):
+            assert lib.ra_allreduce_ex(ptrs, 8, 16, 1, 0, B.ALGOS[algo], ctypes.byref(o),
+                                       None) == B.RA_ERR_INVALID_ARG
+    o = B._options(wide=True, group=4)
+    assert lib.ra_allreduce_ex(ptrs, 8, 16, 2, 0, B.ALGOS["hier_fused"], ctypes.byref(o),
+                               None) == B.RA_ERR_UNSUPPORTED
