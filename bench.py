@@ -181,7 +181,7 @@ def per_workload(torch, B, inputs):
         S = n * inputs.ITEMSIZE[dtype]
         two_ps = 2 * p * S
         rec = {"p": p, "n_per_rank": n, "dtype": dtype, "bytes_per_rank": S, "bytes_2pS": two_ps}
-        for algo in ("fused", "ring_step", "ring_channels", "tree"):
+        for algo in ("fused", "ring_step", "ring_channels", "tree", "hier", "hier_fused"):
             fn = lambda a=algo: B.ra_allreduce_ex(bufs, algo=a)
             fn()
             B.ra_stream_status()
@@ -249,7 +249,7 @@ def alpha_measure(torch, B, inputs):
     # the same with 8 channels: each barrier spans an eighth of the grid
     steps = []
     for _ in range(5):
-        B.ra_allreduce_ex(bufs, algo="ring_channels", step_ts=ts)
+        B.ra_allreduce_ex(bufs, algo="ring_channels", channels=8, step_ts=ts)
         B.ra_stream_status()
         v = ts.cpu().numpy().astype(np.float64)
         steps.append(np.diff(v) / hz * 1e6)
@@ -388,14 +388,19 @@ def main():
         log("variants")
         fill_workload(args.workload, bufs, torch, inputs)
         variants = {}
-        for algo in ("ring_step", "ring_pipelined", "ring_bidir", "ring_channels", "tree"):
-            fn = lambda a=algo: B.ra_allreduce_ex(bufs, algo=a)
+        runs = [(a, a, {}) for a in ("ring_step", "ring_pipelined", "ring_bidir", "ring_channels",
+                                     "tree", "hier", "hier_fused")]
+        runs += [("fused_wide_fp32_accumulate", "fused", {"wide": True}),
+                 ("fused_avg", "fused", {"op": "avg"}), ("fused_max", "fused", {"op": "max"})]
+        for name, algo, kw in runs:
+            fn = lambda a=algo, k=kw: B.ra_allreduce_ex(bufs, algo=a, **k)
+            fill_workload(args.workload, bufs, torch, inputs)
             fn()
             B.ra_stream_status()
             vper, _ = time_calls(fn, 3, torch)
             B.ra_stream_status()
             t = sum(vper) / len(vper)
-            variants[algo] = {"ms": round(t, 3), "GBps_on_2pS": round(min_bytes / (t * 1e-3) / 1e9, 1)}
+            variants[name] = {"ms": round(t, 3), "GBps_on_2pS": round(min_bytes / (t * 1e-3) / 1e9, 1)}
         result["variants"] = variants
         log("standalone phases")
         fill_workload(args.workload, bufs, torch, inputs)

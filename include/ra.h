@@ -118,8 +118,10 @@ typedef struct ra_options {
                            ticks at kernel start and as each step's barrier releases
                            (RING_STEP, RING_BIDIR, TREE, RING_CHANNELS: channel 0).
                            NULL = not recorded. */
-  int32_t channels;     /* RING_CHANNELS: number of channels, 1..64; 0 = 8 (one per XCD).
-                           Capped at the number of workgroups.  Other algorithms ignore it. */
+  int32_t channels;     /* RING_CHANNELS: number of channels, 1..64; 0 = automatic (up to
+                           8, one per XCD, while every segment of a channel still gets a
+                           workgroup).  Capped at the number of workgroups.  Other
+                           algorithms ignore it. */
   int32_t group;        /* HIER, HIER_FUSED: ranks per node g, dividing p; 0 = the largest
                            divisor of p that is at most 8.  Other algorithms ignore it. */
   double link_alpha_us; /* AUTO: per-step latency alpha of the link the schedule is priced

@@ -47,9 +47,6 @@ bool debug_on() {
 
 constexpr int kLastAlgo = RA_ALGO_HIER_FUSED;
 
-// Channels of RING_CHANNELS when the caller does not choose: one per XCD.
-constexpr int kDefaultChannels = 8;
-
 const char* algo_name(int a) {
   switch (a) {
     case RA_ALGO_RING_STEP: return "ring_step";
@@ -309,8 +306,7 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
     e = ra::launch_pipelined(P, p, n, dtype, op, hop_begin, hop_end, slice, kmax, w->flags, base,
                              sc, s, &grid);
   } else {
-    if (algo == RA_ALGO_RING_CHANNELS)
-      sc.channels = opt && opt->channels > 0 ? opt->channels : kDefaultChannels;
+    if (algo == RA_ALGO_RING_CHANNELS) sc.channels = opt ? opt->channels : 0;   // 0: automatic
     e = ra::launch_steps(P, p, n, dtype, op, ra::kModeRing, hop_begin, hop_end, sc, s, &grid);
   }
   if (e != hipSuccess) return fail_hip(e, "kernel launch");

@@ -24,7 +24,7 @@ struct SyncCfg {
   uint32_t expect_extra;  // 1 = first wait expects an arrival that never comes (test hook)
   uint64_t* step_ts;      // optional device array of step timestamps
   int grid;               // 0 = as many workgroups as are co-resident
-  int channels;           // step kernels: independent channels (1 = whole grid)
+  int channels;           // step kernels: independent channels (1 = whole grid, 0 = automatic)
   int group;              // kModeHier: ranks per node g (g divides p)
 };
 

@@ -403,6 +403,9 @@ static hipError_t resident_blocks(const void* func, int* out) {
 // (see kPersistentPerCU), so each thread keeps more bytes in flight: measured at
 // 8 x 16 GB bf16, four vectors per thread ran 103.8 ms against 107.3 with two.
 static constexpr int kStepU = 4;
+
+// Most channels chosen when the caller leaves the count open: one per XCD.
+static constexpr int kAutoChannels = 8;
 static constexpr int kPipeU = 4;
 
 template <int DT, int OP>
@@ -476,8 +479,13 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   // workgroup only adds to each barrier's cost
   const int64_t most = (int64_t)most_seg * std::max<int64_t>(1, (maxvec + tv - 1) / tv);
   grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, most));
-  // channels share that grid, the same number of workgroups each, at least one
-  a.channels = std::max(1, std::min(std::min(sc.channels, kMaxChannels), grid));
+  // channels share that grid, the same number of workgroups each, at least one.
+  // Unspecified (0): as many as give every segment of a channel a workgroup of
+  // its own, at most kAutoChannels -- fewer would leave a channel's workgroups
+  // walking segments one after another on small buffers
+  int want = sc.channels;
+  if (want == 0) want = std::max(1, std::min(kAutoChannels, grid / std::max(1, most_seg)));
+  a.channels = std::max(1, std::min(std::min(want, kMaxChannels), grid));
   grid = grid / a.channels * a.channels;
   if (a.channels > 1) maxvec = maxvec / a.channels + 4;
   a.T = std::max<int64_t>(1, (maxvec + tv - 1) / tv);
