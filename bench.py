@@ -229,8 +229,10 @@ def alpha_measure(torch, B, inputs):
 
     (1) in-kernel: device wall-clock stamps as each step's grid barrier
         releases, tiny buffers (p=64, 1 KiB per rank): median step time.
-    (2) fit: T(S) = 2(p-1) a + 2(p-1)/p * S / B over S/p from 4 KiB to 4 MiB at
-        p=8 and p=64 (bf16), least squares per p.
+    (2) fit: T(S) = 2(p-1) a + 2(p-1)/p * S / B over S from 4 KiB to 16 MiB per
+        rank, p = 2 .. 64 (bf16), least squares per p; the tree under the same
+        model (2 ceil(log2 p) steps of a + S / B) and the fused pass (a + 2pS/BW);
+        the ring/tree crossover measured and from the fitted model.
     """
     import numpy as np
     hz = B.ra_wallclock_hz()
@@ -256,9 +258,11 @@ def alpha_measure(torch, B, inputs):
     out["in_kernel_step_us_p64_1KiB_8channels"] = round(float(np.median(np.concatenate(steps))), 3)
     fits = {}
     algos = ("ring_step", "ring_channels", "tree", "fused")
-    for p in (8, 64):
+    sizes = [4 << 10, 16 << 10, 64 << 10, 256 << 10, 1 << 20, 4 << 20, 16 << 20]
+    for p in (2, 4, 8, 9, 16, 32, 64):
+        levels = max(1, (p - 1).bit_length())
         rows = []
-        for per_rank in (4 << 10, 64 << 10, 1 << 20, 4 << 20):
+        for per_rank in sizes:
             n = per_rank // 2
             bufs = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
             row = {"S_per_rank": per_rank}
@@ -268,19 +272,38 @@ def alpha_measure(torch, B, inputs):
             rows.append(row)
             del bufs
         rec = {"sizes": rows}
-        # T = 2(p-1) a + 2(p-1)/p * S / B, least squares over the sizes
-        x = np.array([2 * (p - 1) / p * r["S_per_rank"] for r in rows])
-        A = np.stack([np.full(len(x), 2.0 * (p - 1)), x], axis=1)
+        S = np.array([r["S_per_rank"] for r in rows], dtype=np.float64)
+        # ring: T = 2(p-1) a + 2(p-1)/p * S / B ([Derive] Where it stops scaling)
+        A = np.stack([np.full(len(S), 2.0 * (p - 1)), 2 * (p - 1) / p * S], axis=1)
         for algo in ("ring_step", "ring_channels"):
             y = np.array([r[f"{algo}_ms"] * 1e-3 for r in rows])
             (a, inv_b), *_ = np.linalg.lstsq(A, y, rcond=None)
             rec[algo] = {"alpha_us": round(a * 1e6, 3),
                          "B_GBps_per_rank": round(1.0 / inv_b / 1e9, 2) if inv_b > 0 else None}
+        # tree under the same model: 2L steps, each alpha + S / B
+        At = np.stack([np.full(len(S), 2.0 * levels), 2.0 * levels * S], axis=1)
+        y = np.array([r["tree_ms"] * 1e-3 for r in rows])
+        (at, inv_bt), *_ = np.linalg.lstsq(At, y, rcond=None)
+        rec["tree"] = {"alpha_us": round(at * 1e6, 3),
+                       "B_GBps_per_rank": round(1.0 / inv_bt / 1e9, 2) if inv_bt > 0 else None}
+        # fused: one launch, T = a + 2pS / BW
+        Af = np.stack([np.ones(len(S)), 2.0 * p * S], axis=1)
+        y = np.array([r["fused_ms"] * 1e-3 for r in rows])
+        (af, inv_bf), *_ = np.linalg.lstsq(Af, y, rcond=None)
+        rec["fused"] = {"fixed_us": round(af * 1e6, 3),
+                        "GBps": round(1.0 / inv_bf / 1e9, 1) if inv_bf > 0 else None}
+        # crossovers: measured (largest size where the tree wins) and the pages'
+        # model with the ring's fitted alpha and B: S* = B a (2(p-1) - 2L) / (2L - 2(p-1)/p)
         cross = None
         for r in rows:
             if r["tree_ms"] < r["ring_step_ms"]:
                 cross = r["S_per_rank"]
         rec["largest_S_per_rank_where_tree_beats_ring"] = cross
+        a_r = rec["ring_step"]["alpha_us"] * 1e-6
+        b_r = (rec["ring_step"]["B_GBps_per_rank"] or 0) * 1e9
+        lat, bw = 2.0 * (p - 1) - 2.0 * levels, 2.0 * levels - 2.0 * (p - 1) / p
+        rec["model_crossover_S_per_rank"] = (round(b_r * a_r * lat / bw)
+                                             if lat > 0 and bw > 0 and b_r > 0 and a_r > 0 else None)
         rec["fused_fastest_at_every_size"] = all(
             r["fused_ms"] <= min(r[f"{a}_ms"] for a in algos) for r in rows)
         fits[f"p{p}"] = rec

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ra {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -201,6 +203,37 @@ template <> struct Elem<3> {
   __device__ static __forceinline__ W divw(W w, int p) { return w / (float)p; }
 };
 
+// Maximum of 16-bit floats (bfloat16: infinity 0x7f80, quiet NaN 0x7fc0;
+// float16: 0x7c00, 0x7e00), two lanes per 32-bit word, through integer keys.
+// For a value that is not NaN, x ^ (x's sign ? 0x7fff : 0), read as a signed
+// 16-bit integer, orders like the value itself, with -0 (key -1) below +0
+// (key 0), so one packed signed maximum takes the larger of two lanes.  NaN
+// lanes are tracked apart: adding 0x7fff - infinity to a lane's magnitude sets
+// its bit 15 exactly when the magnitude exceeds infinity's.  The result lane is
+// the canonical quiet NaN wherever any operand lane was NaN.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+template <uint32_t kInf, uint32_t kQNaN>
+struct Max16 {
+  __device__ static __forceinline__ uint32_t key(uint32_t w) {   // an involution
+    return w ^ (((w >> 15) & 0x00010001u) * 0x7fffu);
+  }
+  __device__ static __forceinline__ uint32_t nan_bits(uint32_t w) {
+    return ((w & 0x7fff7fffu) + (0x7fffu - kInf) * 0x00010001u) & 0x80008000u;
+  }
+  __device__ static __forceinline__ uint32_t kmax(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(s16x2, a),
+                                                                 __builtin_bit_cast(s16x2, b)));
+  }
+  // keys and NaN bits back to values
+  __device__ static __forceinline__ uint32_t finish(uint32_t k, uint32_t nan) {
+    const uint32_t m = ((nan >> 15) & 0x00010001u) * 0xffffu;
+    return (key(k) & ~m) | (kQNaN * 0x00010001u & m);
+  }
+};
+typedef Max16<0x7f80u, 0x7fc0u> MaxBf16;
+typedef Max16<0x7c00u, 0x7e00u> MaxF16;
+
 // Elements of a 16-byte vector as an array of storage words.
 template <int DT> struct Lanes {
   typename Elem<DT>::S e[Elem<DT>::V];
@@ -214,7 +247,14 @@ __device__ __forceinline__ u32x4 pack(const Lanes<DT>& l) { return __builtin_bit
 template <int DT, int OP>
 __device__ __forceinline__ u32x4 vcomb(u32x4 a, u32x4 b) {
   typedef Elem<DT> E;
-  if constexpr (OP == kMax) {
+  if constexpr (OP == kMax && (DT == 2 || DT == 3)) {
+    typedef typename std::conditional<DT == 2, MaxBf16, MaxF16>::type M;
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = M::finish(M::kmax(M::key(a[i]), M::key(b[i])), M::nan_bits(a[i]) | M::nan_bits(b[i]));
+    return r;
+  } else if constexpr (OP == kMax) {
     Lanes<DT> x = unpack<DT>(a), y = unpack<DT>(b);
 #pragma unroll
     for (int i = 0; i < E::V; ++i) x.e[i] = E::max1(x.e[i], y.e[i]);
@@ -243,6 +283,44 @@ __device__ __forceinline__ u32x4 vdiv(u32x4 a, int p) {
 //   WIDE = true:  terms widened exactly to W (avg divides them there), every hop
 //                 rounds to W, the result is rounded once to the element type
 template <int DT, int OP, bool WIDE> struct Fold;
+
+// Maximum of 16-bit floats: keys and NaN bits accumulate, values come back once.
+template <int DT> struct Fold16Max {
+  typedef typename std::conditional<DT == 2, MaxBf16, MaxF16>::type M;
+  typedef typename Elem<DT>::S S;
+  struct A {
+    u32x4 k, nan;
+  };
+  typedef S A1;
+  __device__ static __forceinline__ A start(u32x4 x, int) {
+    A a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a.k[i] = M::key(x[i]);
+      a.nan[i] = M::nan_bits(x[i]);
+    }
+    return a;
+  }
+  __device__ static __forceinline__ A step(A a, u32x4 x, int) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a.k[i] = M::kmax(a.k[i], M::key(x[i]));
+      a.nan[i] |= M::nan_bits(x[i]);
+    }
+    return a;
+  }
+  __device__ static __forceinline__ u32x4 finish(const A& a) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = M::finish(a.k[i], a.nan[i]);
+    return r;
+  }
+  __device__ static __forceinline__ A1 start1(S x, int) { return x; }
+  __device__ static __forceinline__ A1 step1(A1 acc, S x, int) { return Elem<DT>::max1(acc, x); }
+  __device__ static __forceinline__ S finish1(A1 acc) { return acc; }
+};
+template <> struct Fold<2, kMax, false> : Fold16Max<2> {};
+template <> struct Fold<3, kMax, false> : Fold16Max<3> {};
 
 template <int DT, int OP> struct Fold<DT, OP, false> {
   typedef Elem<DT> E;

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kBlock) void k_fused_hier(RankPtrs P, ChunkGeo gi, 
       for (int k2 = 0; k2 < M; ++k2) {
         const int q = d + k2 < M ? d + k2 : d + k2 - M;
         const int base = q * G;
-        u32x4 acc = F::start(ld16<NT>(P.b[base + c], v), p);
+        typename F::A acc = F::start(ld16<NT>(P.b[base + c], v), p);
         for (int k0 = 1; k0 < G; k0 += KB) {
           u32x4 x[KB];
 #pragma unroll
@@ -211,7 +211,8 @@ __global__ __launch_bounds__(kBlock) void k_fused_hier(RankPtrs P, ChunkGeo gi, 
           for (int i = 0; i < KB; ++i)
             if (k0 + i < G) acc = F::step(acc, x[i], p);
         }
-        total = k2 == 0 ? acc : vcomb<DT, OP>(total, acc);
+        const u32x4 node = F::finish(acc);
+        total = k2 == 0 ? node : vcomb<DT, OP>(total, node);
       }
       for (int r = 0; r < p; ++r) st16<NT>(P.b[r], v, total);
     }

@@ -111,6 +111,7 @@ struct StepArgs {
   int p, mode, step_begin, step_end, levels;
   int channels;         // C: workgroup b serves channel b mod C
   int g, m;             // hier: ranks per node, nodes (half[0] = the g-way intra partition)
+  int sync;             // SyncScope of the barriers between steps
   uint32_t expect_extra;
 };
 
@@ -270,7 +271,14 @@ __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
     }
     const bool last = step + 1 == a.step_end;
     if (!last || a.step_ts || extra) {
-      if (!grid_barrier(a.ws, bar, leader, nbh, extra, a.limit)) return;
+      bool ok;
+      if (a.sync == kSyncXcdGroups)
+        ok = xcd_barrier(a.ws, bar, extra, a.limit);
+      else if (a.sync == kSyncOneXcd)
+        ok = xcd_local_barrier(a.ws, bar, leader, nbh, extra, a.limit);
+      else
+        ok = grid_barrier(a.ws, bar, leader, nbh, extra, a.limit);
+      if (!ok) return;
       extra = 0;
       if (a.step_ts && blockIdx.x == 0 && threadIdx.x == 0)
         a.step_ts[step - a.step_begin + 1] = now_ticks();
@@ -303,15 +311,17 @@ __device__ __forceinline__ int64_t n_slices(int64_t lo, int64_t hi, int64_t slic
   return k < 1 ? 1 : k;
 }
 
-// Workgroup (d, w) plays rank d: for each hop h it receives chunk c from rank
+// Workgroup (d, w) = block d * W + w plays rank d: for each hop h it receives chunk c from rank
 // d-1 (reduce-scatter hop s: c = d-1-s, add; all-gather hop s: c = d-s, copy),
 // slice by slice (slices k = w, w + W, ...).  Slice k of chunk c may take hop h
 // once its counter says hops 0..h-1 are done, i.e. once rank d-1 has finished
 // with it; afterwards the counter is advanced for rank d+1.  Every dependency
 // points to an earlier hop of the same slice, handled by workgroup (d-1, w), and
 // every workgroup takes its hops in increasing order, so with all workgroups
-// resident the chain always progresses.
-template <int DT, int OP, int U, bool NT>
+// resident the chain always progresses.  When W is a multiple of 8, workgroups
+// (d, w) of every rank d sit on XCD w mod 8, so each slice lives in one XCD's L2
+// and publishing a slice needs no L2 write-back (LOCAL).
+template <int DT, int OP, int U, bool NT, bool LOCAL>
 __global__ __launch_bounds__(kBlock) void k_pipelined(PipeArgs a) {
   typedef Elem<DT> E;
   constexpr int V = E::V;
@@ -354,7 +364,7 @@ __global__ __launch_bounds__(kBlock) void k_pipelined(PipeArgs a) {
         else
           hop_tile<DT, OP, U, false, NT>(src, dst, slo, shi, j, p, hf);
       }
-      post_flag(f, done + 1);
+      post_flag<LOCAL>(f, done + 1);
     }
   }
 }
@@ -374,6 +384,51 @@ static hipError_t device_cus(int* cus) {
   e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess) cache[dev] = *cus;
   return e;
+}
+
+// ---------------------------------------------------------------- placement
+
+// Reads the XCC_ID hardware register: the XCD this workgroup runs on.
+__global__ void k_xcc_probe(uint32_t* out) {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  if (threadIdx.x == 0) out[blockIdx.x] = v & 0xfu;
+}
+
+// Whether the dispatcher puts workgroup b on XCD b mod 8 on the current device:
+// checked once per device with 1024 one-wave workgroups (every b must share the
+// XCD of b mod 8, and blocks 0..7 must cover 8 distinct XCDs).  The two-level
+// and XCD-local synchronisation rely on it; without it everything stays on the
+// device-wide barrier.
+static hipError_t xcd_placement(bool* ok) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::unordered_map<int, bool> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) { *ok = it->second; return hipSuccess; }
+  constexpr int kProbe = 1024;
+  uint32_t* d = nullptr;
+  e = hipMalloc(&d, kProbe * sizeof(uint32_t));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_xcc_probe, dim3(kProbe), dim3(64), 0, 0, d);
+  e = hipGetLastError();
+  uint32_t h[kProbe];
+  if (e == hipSuccess) e = hipMemcpy(h, d, sizeof h, hipMemcpyDeviceToHost);
+  (void)hipFree(d);
+  if (e != hipSuccess) return e;
+  bool good = true;
+  uint32_t seen = 0;
+  for (int b = 0; b < kXcds; ++b) {
+    if (h[b] >= 32 || (seen >> h[b] & 1u)) good = false;
+    else seen |= 1u << h[b];
+  }
+  for (int b = kXcds; b < kProbe && good; ++b) good = h[b] == h[b % kXcds];
+  cache[dev] = good;
+  *ok = good;
+  return hipSuccess;
 }
 
 // Workgroups per CU that persistent kernels rely on being co-resident.  The
@@ -487,6 +542,12 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   if (want == 0) want = std::max(1, std::min(kAutoChannels, grid / std::max(1, most_seg)));
   a.channels = std::max(1, std::min(std::min(want, kMaxChannels), grid));
   grid = grid / a.channels * a.channels;
+  bool placed = false;
+  e = xcd_placement(&placed);
+  if (e != hipSuccess) return e;
+  a.sync = !placed ? kSyncDevice
+           : a.channels == 1 ? kSyncXcdGroups
+           : a.channels % kXcds == 0 ? kSyncOneXcd : kSyncDevice;
   if (a.channels > 1) maxvec = maxvec / a.channels + 4;
   a.T = std::max<int64_t>(1, (maxvec + tv - 1) / tv);
   *grid_used = grid;
@@ -572,15 +633,21 @@ static hipError_t pipelined_dt(const RankPtrs& P, int p, int64_t n, int hop_begi
   a.hop_end = hop_end;
   a.base = base;
   a.expect_extra = sc.expect_extra;
-  const void* func = streaming(p, n, DT)
-                         ? reinterpret_cast<const void*>(&k_pipelined<DT, OP, kPipeU, true>)
-                         : reinterpret_cast<const void*>(&k_pipelined<DT, OP, kPipeU, false>);
+  const bool nt = streaming(p, n, DT);
+  const void* func = nt ? reinterpret_cast<const void*>(&k_pipelined<DT, OP, kPipeU, true, false>)
+                        : reinterpret_cast<const void*>(&k_pipelined<DT, OP, kPipeU, false, false>);
   int resident = 0;
   hipError_t e = resident_blocks(func, &resident);
   if (e != hipSuccess) return e;
   int budget = sc.grid > 0 ? std::min(sc.grid, resident) : resident;
   int workers = (int)std::max<int64_t>(1, std::min<int64_t>(budget / p, kmax));
   if (workers * p > resident) return hipErrorCooperativeLaunchTooLarge;
+  bool placed = false;
+  e = xcd_placement(&placed);
+  if (e != hipSuccess) return e;
+  if (placed && workers % kXcds == 0)
+    func = nt ? reinterpret_cast<const void*>(&k_pipelined<DT, OP, kPipeU, true, true>)
+              : reinterpret_cast<const void*>(&k_pipelined<DT, OP, kPipeU, false, true>);
   a.workers = workers;
   *grid_used = workers * p;
   void* args[] = {&a};

@@ -148,3 +148,41 @@ def test_binding_accepts_new_dtypes():
         B.ra_allreduce(x)
         B.ra_stream_status()
         assert all(torch.equal(v, torch.full_like(v, 3)) for v in x)
+
+
+def special_values(p, n, dtype, seed):
+    """Normals mixed with +-0, +-inf and NaNs of both signs and several payloads."""
+    rng = np.random.default_rng(seed)
+    xs = make(p, n, dtype, seed)
+    bits_t = {"float16": np.uint16, "bfloat16": np.uint16, "float32": np.uint32,
+              "float64": np.uint64}[dtype]
+    width = 8 * np.dtype(bits_t).itemsize
+    exp_mask = {"float16": 0x7C00, "bfloat16": 0x7F80, "float32": 0x7F800000,
+                "float64": 0x7FF0000000000000}[dtype]
+    sign = 1 << (width - 1)
+    pool = [0, sign, exp_mask, exp_mask | sign, exp_mask | 1, exp_mask | 1 | sign,
+            exp_mask | (exp_mask >> 1 & ~exp_mask), (1 << (width - 1)) - 1]
+    out = []
+    for x in xs:
+        b = np.array(x, copy=True).view(bits_t)
+        idx = rng.random(n) < 0.2
+        b[idx] = np.array(pool, dtype=np.uint64).astype(bits_t)[rng.integers(0, len(pool), idx.sum())]
+        out.append(b.view(x.dtype))
+    return out
+
+
+@pytest.mark.parametrize("dtype", FLOATS)
+def test_max_with_nan_signed_zero_and_infinity(dtype):
+    # every algorithm's maximum equals the oracle's bit for bit on inputs full of
+    # +-0, +-inf and NaNs (any NaN gives the canonical quiet NaN; +0 > -0)
+    require_gpu()
+    p, n = 9, 20_011
+    xs = special_values(p, n, dtype, seed=5)
+    for algo in ALGOS + ["hier", "hier_fused"]:
+        t = to_dev(xs, dtype)
+        print(f"[case] max specials algo={algo} dtype={dtype}", flush=True)
+        B.ra_allreduce_ex(t, algo=algo, op="max", group=3)
+        B.ra_stream_status()
+        want = oracle.ring_fold(xs, dtype, op="max")
+        for r, g in enumerate(from_dev(t, dtype)):
+            assert same_bits(g, want, dtype), f"{algo} rank {r} first diff {first_diff(g, want, dtype)}"
