@@ -41,7 +41,14 @@
  *  other remedy of [InDepth] "Failure modes": accumulate in a wider type.
  *  Concurrency: calls on different streams may overlap; calls on one stream
  *  are ordered by the stream.  The library keeps a small device workspace per
- *  (device, stream), allocated on first use and kept until process exit.
+ *  (device, stream), allocated on first use and kept until process exit.  The
+ *  step-by-step and pipelined algorithms run persistent grids whose workgroups
+ *  must all be resident at once; by default one grid fills the GPU, so
+ *  overlapping such calls should each set ra_options.grid to their share (a
+ *  call that cannot get all its workgroups resident times out instead of
+ *  hanging).  The one-pass algorithms (FUSED, HIER_FUSED) launch ordinary
+ *  grids, use no workspace, and can be captured in a HIP graph; the pipelined
+ *  algorithm cannot (its ready counters are numbered per call on the host).
  *
  * Return codes are ra_status values; ra_status_string() names them and
  * ra_last_error() gives the calling thread's last error message.
@@ -118,10 +125,11 @@ typedef struct ra_options {
                            ticks at kernel start and as each step's barrier releases
                            (RING_STEP, RING_BIDIR, TREE, RING_CHANNELS: channel 0).
                            NULL = not recorded. */
-  int32_t channels;     /* RING_CHANNELS: number of channels, 1..64; 0 = automatic (up to
-                           8, one per XCD, while every segment of a channel still gets a
-                           workgroup).  Capped at the number of workgroups.  Other
-                           algorithms ignore it. */
+  int32_t channels;     /* RING_CHANNELS: number of channels, 1..64; 0 = automatic (8, one
+                           per XCD, when every segment of a channel still gets a
+                           workgroup, else 1).  Capped at the number of workgroups.
+                           Counts that are multiples of 8 keep each channel on one XCD.
+                           Other algorithms ignore it. */
   int32_t group;        /* HIER, HIER_FUSED: ranks per node g, dividing p; 0 = the largest
                            divisor of p that is at most 8.  Other algorithms ignore it. */
   double link_alpha_us; /* AUTO: per-step latency alpha of the link the schedule is priced

@@ -59,8 +59,24 @@ def _run(cmd):
             and "packed-fp32-ops" not in ln and "not a recognized feature" not in ln]
 
 
+C_CHECK_SRC = os.path.join(ROOT, "tests", "c", "abi_check.c")
+C_CHECK_BIN = os.path.join(ROOT, "tests", "c", "abi_check")
+
+
+def c_check_command(out=C_CHECK_BIN):
+    """The plain-C user of the ABI: gcc, no HIP compiler, linked against libra.so
+    (found next to the package through an rpath relative to the binary)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    return ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+            "-I", INCLUDE, "-I", os.path.join(rocm, "include"), C_CHECK_SRC,
+            "-L", PKG, "-lra", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+            "-Wl,-rpath,$ORIGIN/../../ring_all_reduce_schedule_amd",
+            "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", out]
+
+
 def build(verbose=False):
-    """Compile every source (in parallel) and link libra.so; always from scratch."""
+    """Compile every source (in parallel) and link libra.so; always from scratch.
+    Then build the plain-C ABI check against it."""
     from concurrent.futures import ThreadPoolExecutor
     os.makedirs(BUILD, exist_ok=True)
     objs = [os.path.join(BUILD, os.path.splitext(src)[0] + ".o") for src in SOURCES]
@@ -75,6 +91,9 @@ def build(verbose=False):
     if verbose and noise:
         sys.stderr.write("\n".join(noise) + "\n")
     os.replace(tmp, LIB)
+    noise += _run(c_check_command())
+    if verbose and noise:
+        sys.stderr.write("\n".join(noise) + "\n")
     return LIB
 
 

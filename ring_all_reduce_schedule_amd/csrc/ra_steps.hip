@@ -20,6 +20,8 @@
 #include "ra_internal.h"
 
 #include <mutex>
+#include <utility>
+#include <vector>
 #include <unordered_map>
 
 namespace ra {
@@ -459,8 +461,11 @@ static hipError_t resident_blocks(const void* func, int* out) {
 // 8 x 16 GB bf16, four vectors per thread ran 103.8 ms against 107.3 with two.
 static constexpr int kStepU = 4;
 
-// Most channels chosen when the caller leaves the count open: one per XCD.
+// Channels chosen when the caller leaves the count open: one per XCD.
 static constexpr int kAutoChannels = 8;
+
+// Smallest grid that synchronises through the two-level barrier.
+static constexpr int kTwoLevelMinGrid = 128;
 static constexpr int kPipeU = 4;
 
 template <int DT, int OP>
@@ -484,15 +489,20 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   a.levels = 0;
   while ((1 << a.levels) < p) ++a.levels;
   // segment geometry and the widest segment in vectors
-  int64_t maxvec = 0;
+  // every element range a step may work on (chunks of the ring's halves, whole
+  // buffers for the tree, intra chunks and their inter pieces for the hierarchy)
+  std::vector<std::pair<int64_t, int64_t>> ranges;
   if (mode == kModeHier) {
-    // intra chunks are the widest segments (inter sub-chunks cut them m ways)
     a.half[0] = a.half[1] = make_geo(0, n, a.g);
-    for (int c = 0; c < a.g; ++c)
-      maxvec = std::max(maxvec, vecs_in(host_chunk_lo(0, n, a.g, c), host_chunk_lo(0, n, a.g, c + 1), V));
+    for (int c = 0; c < a.g; ++c) {
+      const int64_t lo = host_chunk_lo(0, n, a.g, c), hi = host_chunk_lo(0, n, a.g, c + 1);
+      ranges.emplace_back(lo, hi);
+      for (int d = 0; d < a.m; ++d)
+        ranges.emplace_back(host_chunk_lo(lo, hi - lo, a.m, d), host_chunk_lo(lo, hi - lo, a.m, d + 1));
+    }
   } else if (mode == kModeTree) {
     a.half[0] = a.half[1] = make_geo(0, n, p);
-    maxvec = vecs_in(0, n, V);
+    ranges.emplace_back(0, n);
   } else {
     const int64_t len0 = mode == kModeBidir ? (n + 1) / 2 : n;
     a.half[0] = make_geo(0, len0, p);
@@ -501,10 +511,23 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
     for (int h = 0; h < nh; ++h) {
       const int64_t off = h ? len0 : 0, len = h ? n - len0 : len0;
       for (int c = 0; c < p; ++c)
-        maxvec = std::max(maxvec, vecs_in(host_chunk_lo(off, len, p, c),
-                                          host_chunk_lo(off, len, p, c + 1), V));
+        ranges.emplace_back(host_chunk_lo(off, len, p, c), host_chunk_lo(off, len, p, c + 1));
     }
   }
+  // whole vectors of the widest part of any range cut C ways (the kernel's rule:
+  // part h of [lo, hi) starts at lo + h*floor(len/C) + min(h, len mod C))
+  auto widest = [&](int C) {
+    int64_t w = 0;
+    for (const auto& r : ranges) {
+      const int64_t len = r.second - r.first, q = len / C, rem = len % C;
+      for (int h = 0; h < C; ++h) {
+        const int64_t lo = r.first + h * q + std::min<int64_t>(h, rem);
+        w = std::max(w, vecs_in(lo, lo + q + (h < rem ? 1 : 0), V));
+      }
+    }
+    return w;
+  };
+  const int64_t maxvec = widest(1);
   const void* func = streaming(p, n, DT)
                          ? reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, true>)
                          : reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, false>);
@@ -512,9 +535,6 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   hipError_t e = resident_blocks(func, &resident);
   if (e != hipSuccess) return e;
   int grid = sc.grid > 0 ? std::min(sc.grid, resident) : resident;
-  // channels: at most one per workgroup.  Each segment is cut C ways; a part of
-  // ceil(len / C) elements holds fewer than maxvec / C + 4 whole vectors
-  // (len < (maxvec + 2) V)
   const int64_t tv = (int64_t)kBlock * kStepU;
   // most segments any step has
   int most_seg = 0;
@@ -535,21 +555,23 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   const int64_t most = (int64_t)most_seg * std::max<int64_t>(1, (maxvec + tv - 1) / tv);
   grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, most));
   // channels share that grid, the same number of workgroups each, at least one.
-  // Unspecified (0): as many as give every segment of a channel a workgroup of
-  // its own, at most kAutoChannels -- fewer would leave a channel's workgroups
-  // walking segments one after another on small buffers
+  // Unspecified (0): 8, one per XCD (each channel then lives in one XCD's L2 and
+  // its barrier needs no write-back), when that still gives every segment of a
+  // channel a workgroup of its own; otherwise 1 -- on small buffers a channel's
+  // workgroups would walk segments one after another
   int want = sc.channels;
-  if (want == 0) want = std::max(1, std::min(kAutoChannels, grid / std::max(1, most_seg)));
+  if (want == 0) want = grid / std::max(1, most_seg) >= kAutoChannels ? kAutoChannels : 1;
   a.channels = std::max(1, std::min(std::min(want, kMaxChannels), grid));
   grid = grid / a.channels * a.channels;
   bool placed = false;
   e = xcd_placement(&placed);
   if (e != hipSuccess) return e;
+  // the two-level barrier pays from about 128 workgroups (measured: 4.2 against
+  // 10 us at 256, 2.8 against 2.5 us at 64)
   a.sync = !placed ? kSyncDevice
-           : a.channels == 1 ? kSyncXcdGroups
+           : a.channels == 1 ? (grid >= kTwoLevelMinGrid ? kSyncXcdGroups : kSyncDevice)
            : a.channels % kXcds == 0 ? kSyncOneXcd : kSyncDevice;
-  if (a.channels > 1) maxvec = maxvec / a.channels + 4;
-  a.T = std::max<int64_t>(1, (maxvec + tv - 1) / tv);
+  a.T = std::max<int64_t>(1, (widest(a.channels) + tv - 1) / tv);
   *grid_used = grid;
   void* args[] = {&a};
   return hipLaunchCooperativeKernel(func, dim3(grid), dim3(kBlock), args, 0, s);

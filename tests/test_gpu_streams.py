@@ -1,0 +1,93 @@
+"""Streams and graphs (through the C ABI).
+
+* Two streams run all-reduces at the same time on different buffers: the
+  library keeps one workspace (barrier words, status) per (device, stream), so
+  the grid barriers of concurrent step-by-step calls never mix.  Each call is
+  given 64 workgroups so that both persistent grids are resident together.
+* The one-pass algorithms launch ordinary kernels and use no workspace, so they
+  can be captured into a HIP graph; every replay (with eager work and
+  synchronisation in between) must equal the eager result.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ring_all_reduce_schedule_amd import binding as B
+from ring_all_reduce_schedule_amd import inputs
+from tests.gpu_util import require_gpu, to_dev, from_dev, same_bits, first_diff
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("algo", ["ring_step", "tree", "hier", "ring_channels", "ring_pipelined"])
+def test_two_streams_at_once(algo):
+    require_gpu()
+    p, n, dtype = 8, 300_007, "float32"
+    xa = inputs.make_inputs(p, n, dtype, seed=1)
+    xb = inputs.make_inputs(p, n, dtype, seed=2)
+    want = {"tree": lambda x: oracle.tree_allreduce(x, dtype)[0][0],
+            "hier": lambda x: oracle.hier_fold(x, dtype, 8)}.get(algo, lambda x: oracle.ring_fold(x, dtype))
+    ta, tb = to_dev(xa, dtype), to_dev(xb, dtype)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    print(f"[case] two streams algo={algo}", flush=True)
+    for _ in range(3):
+        # 64 workgroups each: both persistent grids fit on the GPU together
+        with torch.cuda.stream(sa):
+            B.ra_allreduce_ex(ta, algo=algo, grid=64)
+        with torch.cuda.stream(sb):
+            B.ra_allreduce_ex(tb, algo=algo, grid=64)
+        B.ra_stream_status(stream=sa)
+        B.ra_stream_status(stream=sb)
+        # the next round starts from this round's result on both streams
+        xa = [want(xa)] * p
+        xb = [want(xb)] * p
+        for r, g in enumerate(from_dev(ta, dtype)):
+            assert same_bits(g, xa[0], dtype), f"stream a rank {r} at {first_diff(g, xa[0], dtype)}"
+        for r, g in enumerate(from_dev(tb, dtype)):
+            assert same_bits(g, xb[0], dtype), f"stream b rank {r} at {first_diff(g, xb[0], dtype)}"
+
+
+@pytest.mark.parametrize("call", ["allreduce_fused", "allreduce_hier_fused", "rs_then_ag_fused"])
+def test_graph_capture_and_replay(call):
+    require_gpu()
+    p, n, dtype = 9, 100_003, "bfloat16"
+    xs = inputs.make_inputs(p, n, dtype, seed=3)
+    src = to_dev(xs, dtype)
+    bufs = [torch.empty_like(s) for s in src]
+
+    def run():
+        if call == "allreduce_fused":
+            B.ra_allreduce_ex(bufs, algo="fused")
+        elif call == "allreduce_hier_fused":
+            B.ra_allreduce_ex(bufs, algo="hier_fused", group=3)
+        else:
+            B.ra_reduce_scatter_ex(bufs, algo="fused")
+            B.ra_all_gather_ex(bufs, algo="fused")
+
+    # eager reference (also warms the library up before capture)
+    for b, s in zip(bufs, src):
+        b.copy_(s)
+    run()
+    B.ra_stream_status()
+    eager = from_dev(bufs, dtype)
+    want = oracle.hier_fold(xs, dtype, 3) if call == "allreduce_hier_fused" else oracle.ring_fold(xs, dtype)
+    assert all(same_bits(e, want, dtype) for e in eager)
+
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    print(f"[case] graph capture {call}", flush=True)
+    with torch.cuda.graph(g, stream=cap):
+        run()
+    torch.cuda.synchronize()
+    for k in range(4):
+        for b, s in zip(bufs, src):           # eager work between replays
+            b.copy_(s)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for r, got in enumerate(from_dev(bufs, dtype)):
+            assert same_bits(got, eager[r], dtype), f"replay {k} rank {r} at {first_diff(got, eager[r], dtype)}"
