@@ -375,6 +375,8 @@ template <int DT, int OP> struct Fold<DT, OP, true> {
 
 // NT = true marks the access non-temporal (streaming): used when the buffers are
 // far larger than the 256 MB Infinity Cache, so nothing would be re-read from it.
+// kNtPolicy is the same hint as an instruction cache-policy operand.
+constexpr int kNtPolicy = 2;
 template <bool NT = false>
 __device__ __forceinline__ u32x4 ld16(const void* base, int64_t vec) {
   const u32x4* p = reinterpret_cast<const u32x4*>(base) + vec;

@@ -100,6 +100,138 @@ __device__ __forceinline__ void hop_tile(void* __restrict__ src, void* __restric
 }
 
 
+// ================================================================ slice through LDS
+
+// Vectors per thread of one LDS stage, and the stage's size in vectors.
+constexpr int kStageU = 2;
+constexpr int kStageV = kBlock * kStageU;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (gfx9 encoding; export and LDS counters left free).
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+
+// One hop over the whole slice [lo, hi), staged through LDS and double-buffered
+// ("Ring All-Reduce, in depth", section "What real libraries add", pipelining:
+// the next piece is already arriving while this one is reduced and forwarded).
+// Stage t holds kStageV vectors of the incoming (src) and the receiving (dst)
+// chunk; while stage t is combined out of LDS and stored, stage t+1 is being
+// copied into the other LDS buffer by global_load_lds_dwordx4, which lands each
+// lane's 16 bytes at the wave's LDS base without passing through registers.
+// Every wave reads back only the LDS its own lanes filled, so the stages need
+// no workgroup barrier: a wave waits on its own memory counter.  Averages as in
+// hop_tile; the slice's unaligned head and tail go element by element.
+// Issue the asynchronous copies of stage t into one LDS buffer (src and dst halves).
+template <bool ADD, bool NT>
+__device__ __forceinline__ void stage_fill(const u32x4* gsrc, const u32x4* gdst, int64_t v0,
+                                           int64_t v1, u32x4* __restrict__ lsrc,
+                                           u32x4* __restrict__ ldst) {
+  const int wave = threadIdx.x / 64;
+#pragma unroll
+  for (int u = 0; u < kStageU; ++u) {
+    const int64_t v = v0 + u * kBlock + threadIdx.x;
+    const int base = u * kBlock + wave * 64;           // this wave's 64 slots
+    if (v < v1) {
+      __builtin_amdgcn_global_load_lds(gsrc + v, lsrc + base, 16, 0, NT ? kNtPolicy : 0);
+      if (ADD) __builtin_amdgcn_global_load_lds(gdst + v, ldst + base, 16, 0, NT ? kNtPolicy : 0);
+    }
+  }
+}
+
+// One double-buffered step: start filling the next stage, wait for the current
+// one, combine it out of LDS and store.  The four LDS pointers are restrict:
+// once inlined, the copies into the next stage carry their own alias scope, so
+// the compiler's wait-count pass can tell that reading the current stage does
+// not depend on them and waits only for the current stage's copies.
+template <int DT, int OP, bool ADD, bool NT>
+__device__ __forceinline__ void stage_step(void* src, void* dst, int64_t v0, int64_t v1,
+                                           int64_t n0, int64_t n1, int p, HopFlags f,
+                                           u32x4* __restrict__ cur_src, u32x4* __restrict__ cur_dst,
+                                           u32x4* __restrict__ nxt_src, u32x4* __restrict__ nxt_dst) {
+  constexpr bool kDiv = OP == kAvg && ADD;
+  constexpr int kLoads = ADD ? 2 * kStageU : kStageU;    // copies per thread per stage
+  if (n0 < n1) {
+    stage_fill<ADD, NT>(reinterpret_cast<const u32x4*>(src), reinterpret_cast<const u32x4*>(dst),
+                        n0, n1, nxt_src, nxt_dst);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));       // the current stage has landed
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+#pragma unroll
+  for (int u = 0; u < kStageU; ++u) {
+    const int64_t v = v0 + u * kBlock + threadIdx.x;
+    if (v < v1) {
+      const int i = u * kBlock + threadIdx.x;
+      u32x4 a = cur_src[i];
+      if (ADD) {
+        u32x4 y = cur_dst[i];
+        if (kDiv) {
+          if (f.div_src) a = vdiv<DT>(a, p);
+          if (f.div_dst) y = vdiv<DT>(y, p);
+        }
+        st16<NT>(dst, v, vcomb<DT, OP>(y, a));
+        if (kDiv && f.keep_src) st16<NT>(src, v, a);
+      } else {
+        st16<NT>(dst, v, a);
+      }
+    }
+  }
+}
+
+// One hop over the whole slice [lo, hi), staged through LDS and double-buffered
+// ("Ring All-Reduce, in depth", section "What real libraries add", pipelining:
+// the next piece is already arriving while this one is reduced and forwarded).
+// Stage t holds kStageV vectors of the incoming (src) and the receiving (dst)
+// chunk; while stage t is combined out of LDS and stored, stage t+1 is being
+// copied into the other LDS buffer by global_load_lds_dwordx4, which lands each
+// lane's 16 bytes at the wave's LDS base without passing through registers.
+// Every wave reads back only the LDS its own lanes filled, so the stages need
+// no workgroup barrier: a wave waits on its own memory counter.  Averages as in
+// hop_tile; the slice's unaligned head and tail go element by element.
+template <int DT, int OP, bool ADD, bool NT>
+__device__ __forceinline__ void hop_slice_lds(void* __restrict__ src, void* __restrict__ dst,
+                                              int64_t lo, int64_t hi, int p, HopFlags f,
+                                              u32x4 (*stage)[2][kStageV]) {
+  typedef Elem<DT> E;
+  constexpr int V = E::V;
+  constexpr bool kDiv = OP == kAvg && ADD;
+  const Span sp = split_span<V>(lo, hi);
+  const int64_t nst = (sp.v1 - sp.v0 + kStageV - 1) / kStageV;
+  auto first = [&](int64_t t) { return sp.v0 + t * kStageV; };
+  auto last = [&](int64_t t) { return first(t) + kStageV < sp.v1 ? first(t) + kStageV : sp.v1; };
+  if (nst > 0)
+    stage_fill<ADD, NT>(reinterpret_cast<const u32x4*>(src), reinterpret_cast<const u32x4*>(dst),
+                        first(0), last(0), stage[0][0], stage[0][1]);
+  // stages alternate between buffer 0 and 1: two steps per trip so that each
+  // step names its current and next buffer explicitly
+  for (int64_t t = 0; t < nst; t += 2) {
+    stage_step<DT, OP, ADD, NT>(src, dst, first(t), last(t), first(t + 1),
+                                t + 1 < nst ? last(t + 1) : first(t + 1), p, f,
+                                stage[0][0], stage[0][1], stage[1][0], stage[1][1]);
+    if (t + 1 < nst)
+      stage_step<DT, OP, ADD, NT>(src, dst, first(t + 1), last(t + 1), first(t + 2),
+                                  t + 2 < nst ? last(t + 2) : first(t + 2), p, f,
+                                  stage[1][0], stage[1][1], stage[0][0], stage[0][1]);
+  }
+  const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
+  const int t = threadIdx.x;
+  if (t < nh + nt) {
+    const int64_t i = t < nh ? lo + t : sp.tail_lo + (t - nh);
+    typename E::S x = ld1<DT>(src, i);
+    if (ADD) {
+      typename E::S y = ld1<DT>(dst, i);
+      if (kDiv) {
+        if (f.div_src) x = E::div1(x, p);
+        if (f.div_dst) y = E::div1(y, p);
+      }
+      st1<DT>(dst, i, comb1<DT, OP>(y, x));
+      if (kDiv && f.keep_src) st1<DT>(src, i, x);
+    } else {
+      st1<DT>(dst, i, x);
+    }
+  }
+}
+
+
 // ================================================================ step by step
 
 struct StepArgs {
@@ -327,6 +459,7 @@ template <int DT, int OP, int U, bool NT, bool LOCAL>
 __global__ __launch_bounds__(kBlock) void k_pipelined(PipeArgs a) {
   typedef Elem<DT> E;
   constexpr int V = E::V;
+  __shared__ u32x4 stage[2][2][kStageV];                   // 32 KiB: 2 stages x (src, dst)
   if (ws_failed(a.ws)) return;
   const int p = a.p;
   const int d = blockIdx.x / a.workers;
@@ -353,19 +486,15 @@ __global__ __launch_bounds__(kBlock) void k_pipelined(PipeArgs a) {
       }
       const int64_t slo = k == 0 ? lo : A + k * a.slice;
       const int64_t shi = k == K - 1 ? hi : A + (k + 1) * a.slice;
-      const Span sp = split_span<V>(slo, shi);
-      const int64_t tv = (int64_t)kBlock * U;
       // averages: the receiver's chunk is always an input, the sender's only
       // at the first hop (see step_segment)
       HopFlags hf;
       hf.div_dst = rs;
       hf.div_src = hf.keep_src = rs && s == 0;
-      for (int64_t j = 0; sp.v0 + j * tv < sp.v1 || j == 0; ++j) {
-        if (rs)
-          hop_tile<DT, OP, U, true, NT>(src, dst, slo, shi, j, p, hf);
-        else
-          hop_tile<DT, OP, U, false, NT>(src, dst, slo, shi, j, p, hf);
-      }
+      if (rs)
+        hop_slice_lds<DT, OP, true, NT>(src, dst, slo, shi, p, hf, stage);
+      else
+        hop_slice_lds<DT, OP, false, NT>(src, dst, slo, shi, p, hf, stage);
       post_flag<LOCAL>(f, done + 1);
     }
   }
