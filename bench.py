@@ -76,6 +76,7 @@ def log(msg):
 
 
 def alloc_workload(name, torch, B, inputs):
+    """The p rank buffers of a workload (one allocation per rank), filled."""
     w = inputs.WORKLOADS[name]
     p, n, dtype = w["p"], w["n"], w["dtype"]
     tdt = {"int32": torch.int32, "float32": torch.float32, "bfloat16": torch.bfloat16}[dtype]
