@@ -106,6 +106,11 @@ typedef enum ra_algo {
 #define RA_FLAG_FORCE_TIMEOUT 1u  /* test hook: the first device wait expects an
                                      arrival that never comes, so it times out
                                      after timeout_us and every workgroup exits */
+#define RA_FLAG_STRESS 4u         /* test hook: every workgroup of the step-by-step and
+                                     pipelined kernels sleeps a pseudo-random 0-25 us
+                                     before each barrier arrival and each slice hop,
+                                     shuffling arrival orders so that a missing fence
+                                     or wait shows up as a wrong result */
 #define RA_FLAG_WIDE_ACCUM 2u     /* RA_ALGO_FUSED, bfloat16 / float16 / float32 only:
                                      every term is widened exactly to float32
                                      (float64 for float32 buffers), the ring order

@@ -22,6 +22,7 @@ RA_SUM, RA_MAX, RA_AVG = 0, 1, 2
 RA_MAX_RANKS = 64
 RA_FLAG_FORCE_TIMEOUT = 1
 RA_FLAG_WIDE_ACCUM = 2
+RA_FLAG_STRESS = 4
 OPS = {"sum": RA_SUM, "max": RA_MAX, "avg": RA_AVG}
 
 ALGOS = {"default": -1, "ring_step": 0, "ring_pipelined": 1, "ring_bidir": 2,

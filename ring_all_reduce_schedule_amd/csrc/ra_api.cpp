@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -249,6 +250,9 @@ int sync_cfg(const ra_options* opt, Workspace* w, ra::SyncCfg* sc) {
   sc->ws = w->hdr;
   sc->limit_ticks = (uint64_t)us * (uint64_t)khz / 1000u;
   sc->expect_extra = opt && (opt->flags & RA_FLAG_FORCE_TIMEOUT) ? 1u : 0u;
+  // a different delay pattern on every call
+  static std::atomic<uint32_t> calls{0};
+  sc->stress = opt && (opt->flags & RA_FLAG_STRESS) ? 1u + calls.fetch_add(1u) : 0u;
   sc->step_ts = opt ? opt->step_ts : nullptr;
   sc->grid = opt && opt->grid > 0 ? opt->grid : 0;
   sc->channels = 1;

@@ -22,6 +22,7 @@ struct SyncCfg {
   WsHeader* ws;           // device workspace of this (device, stream)
   uint64_t limit_ticks;   // bound of one device-side wait, device clock ticks
   uint32_t expect_extra;  // 1 = first wait expects an arrival that never comes (test hook)
+  uint32_t stress;        // nonzero: pseudo-random delays before arrivals and hops (test hook)
   uint64_t* step_ts;      // optional device array of step timestamps
   int grid;               // 0 = as many workgroups as are co-resident
   int channels;           // step kernels: independent channels (1 = whole grid, 0 = automatic)

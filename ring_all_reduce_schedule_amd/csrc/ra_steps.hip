@@ -247,6 +247,7 @@ struct StepArgs {
   int g, m;             // hier: ranks per node, nodes (half[0] = the g-way intra partition)
   int sync;             // SyncScope of the barriers between steps
   uint32_t expect_extra;
+  uint32_t stress;      // test hook: delays before arrivals (stress_delay)
 };
 
 struct Seg {
@@ -405,6 +406,7 @@ __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
     }
     const bool last = step + 1 == a.step_end;
     if (!last || a.step_ts || extra) {
+      stress_delay(a.stress, (uint32_t)step);
       bool ok;
       if (a.sync == kSyncXcdGroups)
         ok = xcd_barrier(a.ws, bar, extra, a.limit);
@@ -433,6 +435,7 @@ struct PipeArgs {
   uint64_t limit;
   int p, workers, hop_begin, hop_end;
   uint32_t base, expect_extra;
+  uint32_t stress;      // test hook: delays before slice hops (stress_delay)
 };
 
 // Slices of chunk [lo, hi): slice 0 starts at lo, later slices start at
@@ -480,6 +483,7 @@ __global__ __launch_bounds__(kBlock) void k_pipelined(PipeArgs a) {
       uint32_t* f = a.flags + (int64_t)c * a.kmax + k;
       // the first hop reads untouched inputs and depends on nothing; counters
       // left by earlier calls are all below `base`, so it must not wait
+      stress_delay(a.stress, (uint32_t)(h * 4096 + k));
       if (h > a.hop_begin || extra) {
         if (!wait_flag(a.ws, f, done + extra, a.limit)) return;
         extra = 0;
@@ -612,6 +616,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   a.step_begin = step_begin;
   a.step_end = step_end;
   a.expect_extra = sc.expect_extra;
+  a.stress = sc.stress;
   a.channels = 1;
   a.g = sc.group > 0 ? sc.group : p;
   a.m = p / a.g;
@@ -784,6 +789,7 @@ static hipError_t pipelined_dt(const RankPtrs& P, int p, int64_t n, int hop_begi
   a.hop_end = hop_end;
   a.base = base;
   a.expect_extra = sc.expect_extra;
+  a.stress = sc.stress;
   const bool nt = streaming(p, n, DT);
   const void* func = nt ? reinterpret_cast<const void*>(&k_pipelined<DT, OP, kPipeU, true, false>)
                         : reinterpret_cast<const void*>(&k_pipelined<DT, OP, kPipeU, false, false>);

@@ -236,6 +236,22 @@ __device__ __forceinline__ void post_flag(uint32_t* flag, uint32_t value) {
     __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Test hook: when `seed` is nonzero, hold this workgroup for a pseudo-random
+// 0-23 x 2048 clocks (about 0-25 us), different for every workgroup, point and
+// call.  Arrival orders at barriers and flags get shuffled; a correct protocol
+// gives the same bits whatever the order.
+__device__ __forceinline__ void stress_delay(uint32_t seed, uint32_t point) {
+  if (seed == 0) return;
+  if (threadIdx.x == 0) {
+    uint32_t h = (blockIdx.x + 1u) * 2654435761u ^ (point + 1u) * 40503u ^ seed * 2246822519u;
+    h ^= h >> 15;
+    h *= 2246822519u;
+    h ^= h >> 13;
+    for (uint32_t i = (h >> 8) % 24u; i > 0; --i) __builtin_amdgcn_s_sleep(32);
+  }
+  __syncthreads();
+}
+
 __device__ __forceinline__ bool ws_failed(WsHeader* ws) {
   __shared__ int bad;
   if (threadIdx.x == 0) bad = ld_relaxed(&ws->status) != 0;
