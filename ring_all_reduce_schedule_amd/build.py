@@ -74,6 +74,29 @@ def c_check_command(out=C_CHECK_BIN):
             "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", out]
 
 
+HOST_CHECK_SRC = os.path.join(ROOT, "tests", "c", "host_check.cpp")
+HOST_CHECK_BIN = os.path.join(ROOT, "tests", "c", "host_check")
+
+
+def host_check_commands(objs, out=HOST_CHECK_BIN):
+    """The host side of the ABI under AddressSanitizer: ra_api.cpp again with the
+    sanitizer on its host code only (each -fsanitize= right after -Xarch_host),
+    linked by g++ with the kernels' objects into a program that needs no GPU."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    api = os.path.join(BUILD, "ra_api_asan.o")
+    main = os.path.join(BUILD, "host_check.o")
+    kernels = [o for o in objs if not o.endswith("ra_api.o")]
+    return [
+        [hipcc(), *FLAGS, "-x", "hip", "-I", INCLUDE, "-I", CSRC, "-Xarch_host", "-fsanitize=address",
+         "-Xarch_host", "-fno-omit-frame-pointer", "-c", os.path.join(CSRC, "ra_api.cpp"), "-o", api],
+        ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address", "-fno-omit-frame-pointer",
+         "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-I", os.path.join(rocm, "include"), "-c",
+         HOST_CHECK_SRC, "-o", main],
+        ["g++", "-fsanitize=address", main, api, *kernels, "-L", os.path.join(rocm, "lib"),
+         "-lamdhip64", "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", out],
+    ]
+
+
 def build(verbose=False):
     """Compile every source (in parallel) and link libra.so; always from scratch.
     Then build the plain-C ABI check against it."""
@@ -92,6 +115,8 @@ def build(verbose=False):
         sys.stderr.write("\n".join(noise) + "\n")
     os.replace(tmp, LIB)
     noise += _run(c_check_command())
+    for cmd in host_check_commands(objs):
+        noise += _run(cmd)
     if verbose and noise:
         sys.stderr.write("\n".join(noise) + "\n")
     return LIB
