@@ -49,7 +49,7 @@ from .ring import (RingTimeout, reduce_scatter, all_gather, ring_allreduce)
 from .fold import ring_fold, ring_fold_window, rs_partial, rs_owned
 from .tree import tree_allreduce
 from .bidir import bidir_allreduce, bidir_halves
-from .hier import hier_allreduce, hier_fold, hier_layout
+from .hier import hier_allreduce, hier_fold, hier_fold_window, hier_layout
 from .exact import exact_sum, normwise_error
 from . import cost
 
@@ -59,5 +59,5 @@ __all__ = [
     "bf16_bits_to_f32", "f32_to_bf16_bits", "as_values", "RingTimeout",
     "reduce_scatter", "all_gather", "ring_allreduce", "ring_fold",
     "ring_fold_window", "rs_partial", "rs_owned", "tree_allreduce", "bidir_allreduce",
-    "bidir_halves", "hier_allreduce", "hier_fold", "hier_layout", "exact_sum", "normwise_error", "cost",
+    "bidir_halves", "hier_allreduce", "hier_fold", "hier_fold_window", "hier_layout", "exact_sum", "normwise_error", "cost",
 ]

@@ -106,3 +106,40 @@ def hier_fold(xs, dtype, g, op="sum"):
                 total = acc if total is None else combine(total, acc, dtype, op)
             out[s0:s1] = total
     return out
+
+
+def hier_fold_window(windows, lo, n, dtype, g, op="sum"):
+    """The hierarchical order for elements [lo, lo + len(window)) of n-element buffers.
+
+    ``windows[r]`` holds rank r's elements of that window; every element's intra
+    chunk and inter piece follow from the global partition, so windows may
+    straddle either kind of edge.
+    """
+    p = len(windows)
+    m = p // g
+    if g < 1 or p % g:
+        raise ValueError(f"group size {g} must divide p = {p}")
+    w = len(windows[0])
+    hi = lo + w
+    if not 0 <= lo <= hi <= n:
+        raise ValueError("window outside the buffer")
+    terms = [np.asarray(x) for x in windows]
+    if op == "avg":
+        terms = [pre_divide(x, dtype, p) for x in terms]
+        op = "sum"
+    out = np.empty_like(terms[0])
+    for c, (clo, chi) in enumerate(chunk_bounds(n, g)):
+        for d, (a, b) in enumerate(chunk_bounds(chi - clo, m)):
+            s0, s1 = max(lo, clo + a), min(hi, clo + b)
+            if s0 >= s1:
+                continue
+            total = None
+            for k2 in range(m):
+                q = (d + k2) % m
+                acc = None
+                for k1 in range(g):
+                    x = terms[q * g + (c + k1) % g][s0 - lo:s1 - lo]
+                    acc = x.copy() if acc is None else combine(acc, x, dtype, op)
+                total = acc if total is None else combine(total, acc, dtype, op)
+            out[s0 - lo:s1 - lo] = total
+    return out

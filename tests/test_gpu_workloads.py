@@ -16,7 +16,23 @@ import oracle
 from ring_all_reduce_schedule_amd import binding as B
 from ring_all_reduce_schedule_amd import inputs
 from tests.gpu_util import require_gpu, to_dev, from_dev, same_bits, first_diff
-from tests.test_gpu_parity import ALL, RING, expected, TOL
+from tests.test_gpu_parity import ALL, RING, expected as _expected, TOL
+
+# every all-reduce algorithm and the order the oracle folds it in
+WIDE_ALL = ALL + ["ring_channels", "hier", "hier_fused"]
+
+
+def expected(xs, dtype, algo):
+    if algo == "ring_channels":
+        return oracle.ring_fold(xs, dtype)
+    if algo in ("hier", "hier_fused"):
+        return oracle.hier_fold(xs, dtype, _group(len(xs)))
+    return _expected(xs, dtype, algo)
+
+
+def _group(p):
+    """The library's default ranks per node: the largest divisor of p up to 8."""
+    return next(g for g in range(min(p, 8), 0, -1) if p % g == 0)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +56,7 @@ def _run_full(name, algo):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("algo", ALL)
+@pytest.mark.parametrize("algo", WIDE_ALL)
 def test_p9_int32(algo):
     require_gpu()
     _run_full("p9_int32_n1000003", algo)
@@ -50,13 +66,13 @@ def test_p9_int32(algo):
                           np.sum(np.stack(xs).astype(np.int64), axis=0).astype(np.int32))
 
 
-@pytest.mark.parametrize("algo", ALL)
+@pytest.mark.parametrize("algo", WIDE_ALL)
 def test_p64_bf16(algo):
     require_gpu()
     _run_full("p64_bf16_1MiB", algo)
 
 
-@pytest.mark.parametrize("algo", ALL)
+@pytest.mark.parametrize("algo", WIDE_ALL)
 def test_p8_fp32(algo):
     require_gpu()
     _run_full("p8_fp32_256MiB", algo)
@@ -77,7 +93,7 @@ def _windows(n, p, seed):
     return sorted(set((max(0, a), min(n, b)) for a, b in wins))
 
 
-@pytest.mark.parametrize("algo", ["fused"])
+@pytest.mark.parametrize("algo", ["fused", "hier_fused", "ring_step", "tree"])
 def test_p8_bf16_16GB_windowed(algo):
     dev = require_gpu()
     w = inputs.WORKLOADS["p8_bf16_16GB"]
@@ -97,7 +113,13 @@ def test_p8_bf16_16GB_windowed(algo):
     for r in range(1, p):
         assert torch.equal(t[0].view(torch.int16), t[r].view(torch.int16)), f"rank {r} != rank 0"
     for (a, b), xw in zip(wins, before):
-        want = oracle.ring_fold_window(xw, a, n, "bfloat16")
+        if algo == "hier_fused":
+            want = oracle.hier_fold_window(xw, a, n, "bfloat16", _group(p))
+        elif algo == "tree":
+            # the tree's order is the same for every element: fold whole windows
+            want = oracle.tree_allreduce(xw, "bfloat16")[0][0]
+        else:
+            want = oracle.ring_fold_window(xw, a, n, "bfloat16")
         got = t[0][a:b].view(torch.int16).cpu().numpy().view(np.uint16)
         assert same_bits(got, want, "bfloat16"), f"window {a}:{b} first diff {first_diff(got, want, 'bfloat16')}"
     del t

@@ -93,3 +93,12 @@ def test_layout_rejects_groups_that_do_not_divide():
         oracle.hier_layout(8, 3)
     m, nodes, loc = oracle.hier_layout(8, 4)
     assert m == 2 and nodes == [[0, 1, 2, 3], [4, 5, 6, 7]] and loc[1] == [1, 5]
+
+
+def test_fold_window_matches_whole():
+    p, g, n = 8, 4, 1003
+    xs = inputs.make_inputs(p, n, "bfloat16", seed=9)
+    whole = oracle.hier_fold(xs, "bfloat16", g)
+    for lo, hi in [(0, 5), (100, 300), (120, 130), (245, 260), (998, 1003), (0, 1003)]:
+        got = oracle.hier_fold_window([x[lo:hi] for x in xs], lo, n, "bfloat16", g)
+        assert np.array_equal(got, whole[lo:hi])
