@@ -99,13 +99,40 @@ def fill_workload(name, bufs, torch, inputs):
     torch.cuda.synchronize()
 
 
+_SPIN = {}
+
+
+def run_ahead(torch, k):
+    """Hold the stream in a device-side spin while the host enqueues k calls.
+
+    A start event that reaches the GPU before the host has enqueued its call
+    times the host's enqueue rate instead of the kernel (a small all-reduce takes
+    less GPU time than its Python call).  The spin, enqueued before the first
+    start event, lets the host run ahead, so every event pair brackets work that
+    is already queued.  0.1 ms of spin per call covers the host cost of a call
+    and its flush many times over."""
+    if not hasattr(torch.cuda, "_sleep"):
+        return
+    if "cycles_per_ms" not in _SPIN:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(4_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SPIN["cycles_per_ms"] = 4_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    torch.cuda._sleep(int(_SPIN["cycles_per_ms"] * (1.0 + 0.1 * k)))
+
+
 def time_calls(fn, k, torch, flush=None):
     """Per-call durations (ms) from HIP events on the current stream, plus the
     span from the first start to the last end.  `flush`, if given, runs before
-    each call, outside its events (to evict the Infinity Cache)."""
+    each call, outside its events (to evict the Infinity Cache).  The calls are
+    queued behind a short device spin (run_ahead), so the events time the GPU."""
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(k)]
     torch.cuda.synchronize()
+    run_ahead(torch, k)
     for i in range(k):
         if flush is not None:
             flush()
@@ -164,16 +191,20 @@ def cpu_baseline(bufs, w, sample, torch):
 
 def per_workload(torch, B, inputs):
     """Effective GB/s and % of HBM peak for every workload that fits comfortably,
-    per algorithm: fused (on its own 2pS), ring_step and tree (rated on 2pS too).
+    per algorithm, all rated on 2pS.
 
-    Workloads whose 2pS is below the 256 MB Infinity Cache are timed twice: with
-    a 1 GiB scratch write before every call (cold, HBM-bound) and back to back
-    (warm, partly cache-resident)."""
+    Each algorithm is timed twice: with a 1 GiB scratch buffer read before every
+    call (cold: the read replaces the Infinity Cache's contents with clean lines,
+    so nothing of the workload is cached and no write-back competes with the
+    timed call) and back to back (warm: workloads whose 2pS is below the 256 MB
+    cache are then partly cache-resident).  The rank tensors are marshalled once
+    (RankBuffers), as a caller that all-reduces the same buffers every step would."""
     import numpy as np
-    scratch = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+    sink = torch.empty((), dtype=torch.int64, device="cuda")
 
     def flush():
-        scratch.fill_(1)
+        torch.sum(scratch, dim=0, dtype=torch.int64, out=sink)
 
     out = {}
     for name in ("p9_int32_n1000003", "p64_bf16_1MiB", "p8_fp32_256MiB"):
@@ -182,8 +213,9 @@ def per_workload(torch, B, inputs):
         S = n * inputs.ITEMSIZE[dtype]
         two_ps = 2 * p * S
         rec = {"p": p, "n_per_rank": n, "dtype": dtype, "bytes_per_rank": S, "bytes_2pS": two_ps}
+        ranks = B.RankBuffers(bufs)
         for algo in ("fused", "ring_step", "ring_channels", "tree", "hier", "hier_fused"):
-            fn = lambda a=algo: B.ra_allreduce_ex(bufs, algo=a)
+            fn = lambda a=algo: B.ra_allreduce_ex(ranks, algo=a)
             fn()
             B.ra_stream_status()
             cold, _ = time_calls(fn, 9, torch, flush=flush)
@@ -195,9 +227,9 @@ def per_workload(torch, B, inputs):
                          "pct_peak_cold": round(100 * two_ps / (tc * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
                          "ms_warm": round(tw, 4), "GBps_warm": round(two_ps / (tw * 1e-3) / 1e9, 1)}
         out[name] = rec
-        del bufs
+        del bufs, ranks
         torch.cuda.empty_cache()
-    del scratch
+    del scratch, sink
     torch.cuda.empty_cache()
     return out
 
@@ -240,7 +272,7 @@ def alpha_measure(torch, B, inputs):
     out = {}
     p = 64
     n = 512
-    bufs = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+    bufs = B.RankBuffers([torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(p)])
     ts = torch.zeros(2 * (p - 1) + 1, dtype=torch.int64, device="cuda")
     steps = []
     for _ in range(5):
@@ -265,7 +297,8 @@ def alpha_measure(torch, B, inputs):
         rows = []
         for per_rank in sizes:
             n = per_rank // 2
-            bufs = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+            bufs = B.RankBuffers([torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+                                  for _ in range(p)])
             row = {"S_per_rank": per_rank}
             for algo in algos:
                 per, _ = time_calls(lambda a=algo: B.ra_allreduce_ex(bufs, algo=a), 7, torch)
@@ -351,9 +384,10 @@ def main():
     item = inputs.ITEMSIZE[dtype]
     S = n * item
     min_bytes = 2 * p * S
+    ranks = B.RankBuffers(bufs)   # checked and marshalled once; refills are in place
 
     def step():
-        B.ra_allreduce_ex(bufs, algo=args.algo)
+        B.ra_allreduce_ex(ranks, algo=args.algo)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -417,7 +451,7 @@ def main():
         runs += [("fused_wide_fp32_accumulate", "fused", {"wide": True}),
                  ("fused_avg", "fused", {"op": "avg"}), ("fused_max", "fused", {"op": "max"})]
         for name, algo, kw in runs:
-            fn = lambda a=algo, k=kw: B.ra_allreduce_ex(bufs, algo=a, **k)
+            fn = lambda a=algo, k=kw: B.ra_allreduce_ex(ranks, algo=a, **k)
             fill_workload(args.workload, bufs, torch, inputs)
             fn()
             B.ra_stream_status()
@@ -428,7 +462,7 @@ def main():
         result["variants"] = variants
         log("standalone phases")
         fill_workload(args.workload, bufs, torch, inputs)
-        result["phases"] = phase_measure(bufs, S, p, torch, B)
+        result["phases"] = phase_measure(ranks, S, p, torch, B)
         log("copy ceiling")
         # the same byte count as the all-reduce, read + write, through a plain copy
         half = min_bytes // 2
@@ -447,7 +481,7 @@ def main():
         result["cpu_baseline"] = cpu_baseline(bufs, w, args.cpu_sample, torch)
 
     if not args.no_extras:
-        del bufs
+        del bufs, ranks
         torch.cuda.empty_cache()
         log("per-workload rates")
         result["per_workload"] = per_workload(torch, B, inputs)

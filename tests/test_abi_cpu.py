@@ -167,3 +167,14 @@ def test_hier_group_errors():
     o = B._options(wide=True, group=4)
     assert lib.ra_allreduce_ex(ptrs, 8, 16, 2, 0, B.ALGOS["hier_fused"], ctypes.byref(o),
                                None) == B.RA_ERR_UNSUPPORTED
+
+
+def test_rank_buffers_rejects_host_tensors_and_empty_lists():
+    """The binding's marshalling checks run before any library call."""
+    import torch
+    with pytest.raises(ValueError):
+        B.RankBuffers([])
+    with pytest.raises(ValueError):
+        B.RankBuffers([torch.zeros(4), torch.zeros(4)])
+    with pytest.raises(ValueError):
+        B.ra_allreduce([torch.zeros(4)])

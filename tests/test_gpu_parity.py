@@ -200,6 +200,57 @@ def test_binding_rejects_mismatched_tensors():
     assert e.value.code == B.RA_ERR_ALIAS
 
 
+def test_rank_buffers_match_lists_on_every_entry_point():
+    """A RankBuffers (checked and marshalled once) gives the same bits as the list
+    it was made from, through every entry point, and is reused across calls."""
+    require_gpu()
+    p, n = 9, 10_007
+    xs = inputs.make_inputs(p, n, "float32", seed=11)
+    want = oracle.ring_fold(xs, "float32")
+    t = to_dev(xs, "float32")
+    ranks = B.RankBuffers(t)
+    assert len(ranks) == p and ranks.n == n
+    for call in (lambda: B.ra_allreduce(ranks), lambda: B.ra_allreduce_ex(ranks, algo="ring_step")):
+        for r in range(p):
+            t[r].copy_(torch.from_numpy(xs[r]))
+        call()
+        B.ra_stream_status()
+        got = from_dev(t, "float32")
+        for r in range(p):
+            assert same_bits(got[r], want, "float32"), r
+    # reduce-scatter then all-gather through the same object
+    for r in range(p):
+        t[r].copy_(torch.from_numpy(xs[r]))
+    B.ra_reduce_scatter(ranks)
+    B.ra_all_gather(ranks)
+    B.ra_reduce_scatter_ex(ranks, algo="fused")
+    B.ra_all_gather_ex(ranks, algo="fused")
+    B.ra_stream_status()
+    # the second round re-reduces the already-reduced buffers: compare with the oracle's
+    # two rounds
+    want2 = oracle.ring_fold([want] * p, "float32")
+    got = from_dev(t, "float32")
+    for r in range(p):
+        assert same_bits(got[r], want2, "float32"), r
+
+
+def test_rank_buffers_rejects_bad_inputs_and_resized_tensors():
+    require_gpu()
+    a = torch.zeros(16, device="cuda")
+    with pytest.raises(ValueError):
+        B.RankBuffers([a, torch.zeros(17, device="cuda")])
+    with pytest.raises(ValueError):
+        B.RankBuffers([a, torch.zeros(32, device="cuda")[::2]])
+    b = torch.zeros(16, device="cuda")
+    ranks = B.RankBuffers([b, torch.zeros(16, device="cuda")])
+    b.resize_(1 << 20)   # the first rank now lives elsewhere
+    with pytest.raises(ValueError):
+        B.ra_allreduce(ranks)
+    with pytest.raises(B.RaError) as e:
+        B.ra_allreduce(B.RankBuffers([a, a]))
+    assert e.value.code == B.RA_ERR_ALIAS
+
+
 def test_stream_copy():
     require_gpu()
     src = torch.randn(1 << 20, device="cuda")
