@@ -389,6 +389,24 @@ __device__ __forceinline__ void st16(void* base, int64_t vec, u32x4 v) {
   if (NT) __builtin_nontemporal_store(v, p);
   else *p = v;
 }
+// The same accesses addressed as (tile start, lane): vector vt + lane of a
+// buffer, with vt wave-uniform.  Cached accesses take the tile's start address
+// as a scalar and the lane's offset as a 32-bit vector register, which the
+// global instructions accept as scalar base plus vector offset: one offset
+// register serves every rank, instead of a 64-bit address pair per access in
+// flight.  Streaming accesses keep the per-lane 64-bit address, the form the
+// 16 GB-per-rank measurements favour (see the issue patterns below).
+template <bool NT = false>
+__device__ __forceinline__ u32x4 ld16t(const void* base, int64_t vt, unsigned lane) {
+  if (NT) return ld16<true>(base, vt + (int64_t)lane);
+  return (reinterpret_cast<const u32x4*>(base) + vt)[lane];
+}
+template <bool NT = false>
+__device__ __forceinline__ void st16t(void* base, int64_t vt, unsigned lane, u32x4 v) {
+  if (NT) st16<true>(base, vt + (int64_t)lane, v);
+  else (reinterpret_cast<u32x4*>(base) + vt)[lane] = v;
+}
+
 template <int DT>
 __device__ __forceinline__ typename Elem<DT>::S ld1(const void* base, int64_t i) {
   return reinterpret_cast<const typename Elem<DT>::S*>(base)[i];
@@ -396,6 +414,118 @@ __device__ __forceinline__ typename Elem<DT>::S ld1(const void* base, int64_t i)
 template <int DT>
 __device__ __forceinline__ void st1(void* base, int64_t i, typename Elem<DT>::S v) {
   reinterpret_cast<typename Elem<DT>::S*>(base)[i] = v;
+}
+
+// Vector vt + lane of every rank (vt wave-uniform), folded or stored.
+//
+// The rank index is wave-uniform, so each rank's pointer is a scalar load from
+// the kernel arguments.  Two ways of issuing the accesses, chosen by the
+// streaming flag because each measured best in its own regime:
+//  * Cache-resident calls (NT = false) issue in batches of eight ring positions
+//    of straight-line code: the batch's pointer fetches go back to back behind
+//    one wait, then its vector accesses, all in flight together, addressed as a
+//    scalar tile base plus one 32-bit lane offset.  Guarding each rank on its
+//    own lets the compiler sink every fetch into its guard, which costs one
+//    scalar round trip per rank before its access can issue; at p = 64 and
+//    4 KiB per rank that was 16.6 us per call against 12.7 batched.  A run of
+//    any length is whole batches and one shorter batch, picked by a wave-uniform
+//    switch.
+//  * Streaming calls (NT = true) take one rank at a time, each access behind its
+//    own pointer fetch.  At 8 x 16 GB the batched issue measured 0.2% (loads)
+//    and 0.6% (stores) slower: there the round trips hide behind HBM time and
+//    the spaced issue streams slightly better.
+constexpr int kRankBatch = 8;
+
+// acc <- acc (op) x[first] (op) ... (op) x[first + N - 1], positions taken mod m
+// and offset by base: rank base + (first + i) mod m.  first + N - 1 < 2m.
+template <int N, bool NT, class F>
+__device__ __forceinline__ void fold_batch(typename F::A& acc, const RankPtrs& P, int base, int m,
+                                           int first, int64_t vt, unsigned lane, int p) {
+  void* q[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int r = first + i;
+    q[i] = P.b[base + (r >= m ? r - m : r)];
+  }
+  u32x4 x[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = ld16t<NT>(q[i], vt, lane);
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc = F::step(acc, x[i], p);
+}
+
+// Fold `count` ring positions starting at `first` (count >= 0, first + count - 1
+// < 2m) in ring order, at vector vt + lane.
+template <bool NT, class F>
+__device__ __forceinline__ void fold_run(typename F::A& acc, const RankPtrs& P, int base, int m,
+                                         int first, int count, int64_t vt, unsigned lane, int p) {
+  if constexpr (NT) {
+    const int64_t v = vt + lane;
+    for (int k0 = 0; k0 < count; k0 += kRankBatch) {
+      u32x4 x[kRankBatch];
+#pragma unroll
+      for (int i = 0; i < kRankBatch; ++i) {
+        if (k0 + i < count) {
+          const int r = first + k0 + i;
+          x[i] = ld16<NT>(P.b[base + (r >= m ? r - m : r)], v);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kRankBatch; ++i)
+        if (k0 + i < count) acc = F::step(acc, x[i], p);
+    }
+  } else {
+    for (; count >= kRankBatch; count -= kRankBatch, first += kRankBatch)
+      fold_batch<kRankBatch, NT, F>(acc, P, base, m, first, vt, lane, p);
+    switch (count) {
+      case 7: fold_batch<7, NT, F>(acc, P, base, m, first, vt, lane, p); break;
+      case 6: fold_batch<6, NT, F>(acc, P, base, m, first, vt, lane, p); break;
+      case 5: fold_batch<5, NT, F>(acc, P, base, m, first, vt, lane, p); break;
+      case 4: fold_batch<4, NT, F>(acc, P, base, m, first, vt, lane, p); break;
+      case 3: fold_batch<3, NT, F>(acc, P, base, m, first, vt, lane, p); break;
+      case 2: fold_batch<2, NT, F>(acc, P, base, m, first, vt, lane, p); break;
+      case 1: fold_batch<1, NT, F>(acc, P, base, m, first, vt, lane, p); break;
+      default: break;
+    }
+  }
+}
+
+// Store val as vector vt + lane of ranks r0 .. r0 + N - 1, except rank `skip`
+// (-1: none).
+template <int N, bool NT>
+__device__ __forceinline__ void store_batch(const RankPtrs& P, int r0, int64_t vt, unsigned lane,
+                                            u32x4 val, int skip) {
+  void* q[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) q[i] = P.b[r0 + i];
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (r0 + i != skip) st16t<NT>(q[i], vt, lane, val);
+}
+
+// Store val as vector vt + lane of every rank except `skip` (-1: none).
+template <bool NT>
+__device__ __forceinline__ void store_all(const RankPtrs& P, int p, int64_t vt, unsigned lane,
+                                          u32x4 val, int skip) {
+  if constexpr (NT) {
+    const int64_t v = vt + lane;
+    for (int r = 0; r < p; ++r)
+      if (r != skip) st16<NT>(P.b[r], v, val);
+  } else {
+    int r0 = 0;
+    for (; p - r0 >= kRankBatch; r0 += kRankBatch)
+      store_batch<kRankBatch, NT>(P, r0, vt, lane, val, skip);
+    switch (p - r0) {
+      case 7: store_batch<7, NT>(P, r0, vt, lane, val, skip); break;
+      case 6: store_batch<6, NT>(P, r0, vt, lane, val, skip); break;
+      case 5: store_batch<5, NT>(P, r0, vt, lane, val, skip); break;
+      case 4: store_batch<4, NT>(P, r0, vt, lane, val, skip); break;
+      case 3: store_batch<3, NT>(P, r0, vt, lane, val, skip); break;
+      case 2: store_batch<2, NT>(P, r0, vt, lane, val, skip); break;
+      case 1: store_batch<1, NT>(P, r0, vt, lane, val, skip); break;
+      default: break;
+    }
+  }
 }
 
 // Split [lo, hi) into a scalar head, whole 16-byte vectors, and a scalar tail.

@@ -38,42 +38,27 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
   typedef Elem<DT> E;
   typedef Fold<DT, OP, WIDE> F;
   constexpr int V = E::V;
-  constexpr int KB = 8;                     // ranks loaded per batch
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int c = (int)(t / T);
     const int64_t j = t - (int64_t)c * T;
     const int owner = c == 0 ? p - 1 : c - 1;
     const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
     const Span sp = split_span<V>(lo, hi);
-    const int64_t v = sp.v0 + j * kBlock + threadIdx.x;
-    if (v < sp.v1) {
+    const int64_t vt = sp.v0 + j * kBlock;          // the tile's first vector
+    const unsigned lane = threadIdx.x;
+    if (vt + lane < sp.v1) {
       u32x4 out;
       if (MODE == kAllGather) {
-        out = ld16<NT>(P.b[owner], v);
+        out = ld16t<NT>(P.b[owner], vt, lane);
       } else {
-        typename F::A acc = F::start(ld16<NT>(P.b[c], v), p);
-        for (int k0 = 1; k0 < p; k0 += KB) {
-          u32x4 x[KB];
-#pragma unroll
-          for (int i = 0; i < KB; ++i) {
-            if (k0 + i < p) {
-              int r = c + k0 + i;
-              r = r >= p ? r - p : r;
-              x[i] = ld16<NT>(P.b[r], v);
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < KB; ++i)
-            if (k0 + i < p) acc = F::step(acc, x[i], p);
-        }
+        typename F::A acc = F::start(ld16t<NT>(P.b[c], vt, lane), p);
+        fold_run<NT, F>(acc, P, 0, p, c + 1, p - 1, vt, lane, p);
         out = F::finish(acc);
       }
-      if (MODE == kReduceScatter) {
-        st16<NT>(P.b[owner], v, out);
-      } else {
-        for (int r = 0; r < p; ++r)
-          if (!(MODE == kAllGather && r == owner)) st16<NT>(P.b[r], v, out);
-      }
+      if (MODE == kReduceScatter)
+        st16t<NT>(P.b[owner], vt, lane, out);
+      else
+        store_all<NT>(P, p, vt, lane, out, MODE == kAllGather ? owner : -1);
     }
     if (j == 0) {
       const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
@@ -181,7 +166,6 @@ __global__ __launch_bounds__(kBlock) void k_fused_hier(RankPtrs P, ChunkGeo gi, 
   typedef Elem<DT> E;
   typedef Fold<DT, OP, false> F;
   constexpr int V = E::V;
-  constexpr int KB = 8;                     // ranks loaded per batch
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int seg = (int)(t / T);
     const int64_t j = t - (int64_t)seg * T;
@@ -190,31 +174,19 @@ __global__ __launch_bounds__(kBlock) void k_fused_hier(RankPtrs P, ChunkGeo gi, 
     const ChunkGeo sg = {clo, (chi - clo) / M, (chi - clo) % M};
     const int64_t lo = chunk_lo(sg, d), hi = chunk_hi(sg, d);
     const Span sp = split_span<V>(lo, hi);
-    const int64_t v = sp.v0 + j * kBlock + threadIdx.x;
-    if (v < sp.v1) {
+    const int64_t vt = sp.v0 + j * kBlock;          // the tile's first vector
+    const unsigned lane = threadIdx.x;
+    if (vt + lane < sp.v1) {
       u32x4 total;
       for (int k2 = 0; k2 < M; ++k2) {
         const int q = d + k2 < M ? d + k2 : d + k2 - M;
         const int base = q * G;
-        typename F::A acc = F::start(ld16<NT>(P.b[base + c], v), p);
-        for (int k0 = 1; k0 < G; k0 += KB) {
-          u32x4 x[KB];
-#pragma unroll
-          for (int i = 0; i < KB; ++i) {
-            if (k0 + i < G) {
-              int l = c + k0 + i;
-              l = l >= G ? l - G : l;
-              x[i] = ld16<NT>(P.b[base + l], v);
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < KB; ++i)
-            if (k0 + i < G) acc = F::step(acc, x[i], p);
-        }
+        typename F::A acc = F::start(ld16t<NT>(P.b[base + c], vt, lane), p);
+        fold_run<NT, F>(acc, P, base, G, c + 1, G - 1, vt, lane, p);
         const u32x4 node = F::finish(acc);
         total = k2 == 0 ? node : vcomb<DT, OP>(total, node);
       }
-      for (int r = 0; r < p; ++r) st16<NT>(P.b[r], v, total);
+      store_all<NT>(P, p, vt, lane, total, -1);
     }
     if (j == 0) {
       const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
