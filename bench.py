@@ -260,8 +260,10 @@ def phase_measure(bufs, S, p, torch, B):
 def alpha_measure(torch, B, inputs):
     """Per-step latency of the step-by-step ring.
 
-    (1) in-kernel: device wall-clock stamps as each step's grid barrier
-        releases, tiny buffers (p=64, 1 KiB per rank): median step time.
+    (1) in-kernel: device wall-clock stamps as each step's barrier releases,
+        tiny buffers (p=64, 1 KiB per rank): median step time, for the default
+        launch (one workgroup at this size), for 8 channels, and for 64
+        workgroups on the device-wide barrier.
     (2) fit: T(S) = 2(p-1) a + 2(p-1)/p * S / B over S from 4 KiB to 16 MiB per
         rank, p = 2 .. 64 (bf16), least squares per p; the tree under the same
         model (2 ceil(log2 p) steps of a + S / B) and the fused pass (a + 2pS/BW);
@@ -289,6 +291,15 @@ def alpha_measure(torch, B, inputs):
         v = ts.cpu().numpy().astype(np.float64)
         steps.append(np.diff(v) / hz * 1e6)
     out["in_kernel_step_us_p64_1KiB_8channels"] = round(float(np.median(np.concatenate(steps))), 3)
+    # the same steps on 64 workgroups synchronised by the device-wide barrier
+    # (at this size the library runs them on one workgroup by default)
+    steps = []
+    for _ in range(5):
+        B.ra_allreduce_ex(bufs, algo="ring_step", grid=64, step_ts=ts)
+        B.ra_stream_status()
+        v = ts.cpu().numpy().astype(np.float64)
+        steps.append(np.diff(v) / hz * 1e6)
+    out["in_kernel_step_us_p64_1KiB_grid64"] = round(float(np.median(np.concatenate(steps))), 3)
     fits = {}
     algos = ("ring_step", "ring_channels", "tree", "fused")
     sizes = [4 << 10, 16 << 10, 64 << 10, 256 << 10, 1 << 20, 4 << 20, 16 << 20]

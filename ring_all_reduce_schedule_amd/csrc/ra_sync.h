@@ -37,7 +37,10 @@ struct WsHeader {
 // invalidate that reaches the CU's L1 for lines other CUs wrote.
 // The host chooses the last two only after checking, once per device, that the
 // dispatcher places workgroup b on XCD b mod 8.
-enum SyncScope { kSyncDevice = 0, kSyncXcdGroups = 1, kSyncOneXcd = 2 };
+// How the workgroups of a step kernel wait for each other between steps:
+// device-wide barrier, two-level (per XCD, then across XCDs) barrier, barrier of
+// workgroups that share one XCD, or a single workgroup's own barrier.
+enum SyncScope { kSyncDevice = 0, kSyncXcdGroups = 1, kSyncOneXcd = 2, kSyncBlock = 3 };
 
 __device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 

@@ -80,6 +80,20 @@ def test_small_sweep(p, n, dtype):
         check(xs, dtype, algo)
 
 
+# Small steps run on one workgroup (its own barrier between steps); a grid
+# forced above one keeps them on the device-wide barriers.  Both must agree
+# with the oracle, at and around the size where the choice flips (p = 8 bf16:
+# one workgroup up to 256 whole vectors per step, a chunk of 256 elements).
+@pytest.mark.parametrize("grid", [0, 5])
+@pytest.mark.parametrize("p,n", [(3, 1), (3, 4097), (8, 9), (8, 2048), (8, 2049), (8, 2112),
+                                 (8, 2300), (64, 1023), (64, 70_001)])
+def test_small_steps_one_workgroup_and_grid(p, n, grid):
+    require_gpu()
+    xs = inputs.make_inputs(p, n, "bfloat16", seed=7 * p + n + grid, sigma=2.0)
+    for algo in ("ring_step", "ring_bidir", "tree"):
+        check(xs, "bfloat16", algo, grid=grid)
+
+
 @pytest.mark.parametrize("slice_elems,grid", [(8, 0), (24, 16), (1000, 0), (4096, 64),
                                               (1 << 20, 0), (64, 8)])
 @pytest.mark.parametrize("dtype", ["float32", "bfloat16"])
