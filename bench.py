@@ -191,7 +191,8 @@ def cpu_baseline(bufs, w, sample, torch):
 
 def per_workload(torch, B, inputs):
     """Effective GB/s and % of HBM peak for every workload that fits comfortably,
-    per algorithm, all rated on 2pS.
+    per algorithm, all rated on 2pS, and as % of a plain copy of the same bytes
+    (the streaming ceiling at that size).
 
     Each algorithm is timed twice: with a 1 GiB scratch buffer read before every
     call (cold: the read replaces the Infinity Cache's contents with clean lines,
@@ -213,6 +214,19 @@ def per_workload(torch, B, inputs):
         S = n * inputs.ITEMSIZE[dtype]
         two_ps = 2 * p * S
         rec = {"p": p, "n_per_rank": n, "dtype": dtype, "bytes_per_rank": S, "bytes_2pS": two_ps}
+        # the streaming ceiling at this size: a plain copy of the same p*S bytes
+        # (rounded down to 16) from one buffer to another, timed the same ways
+        cb = p * S // 16 * 16
+        src = torch.ones(cb, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        fn = lambda: B.ra_stream_copy(dst, src)
+        fn()
+        cold, _ = time_calls(fn, 9, torch, flush=flush)
+        warm, _ = time_calls(fn, 9, torch)
+        tc, tw = float(np.median(cold[1:])), float(np.median(warm[1:]))
+        rec["copy"] = {"ms_cold": round(tc, 4), "GBps_cold": round(2 * cb / (tc * 1e-3) / 1e9, 1),
+                       "ms_warm": round(tw, 4), "GBps_warm": round(2 * cb / (tw * 1e-3) / 1e9, 1)}
+        del src, dst
         ranks = B.RankBuffers(bufs)
         for algo in ("fused", "ring_step", "ring_channels", "tree", "hier", "hier_fused"):
             fn = lambda a=algo: B.ra_allreduce_ex(ranks, algo=a)
@@ -225,7 +239,9 @@ def per_workload(torch, B, inputs):
             tw = float(np.median(warm[1:]))
             rec[algo] = {"ms_cold": round(tc, 4), "GBps_cold": round(two_ps / (tc * 1e-3) / 1e9, 1),
                          "pct_peak_cold": round(100 * two_ps / (tc * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
-                         "ms_warm": round(tw, 4), "GBps_warm": round(two_ps / (tw * 1e-3) / 1e9, 1)}
+                         "pct_of_copy_cold": round(100 * rec["copy"]["ms_cold"] / tc, 1),
+                         "ms_warm": round(tw, 4), "GBps_warm": round(two_ps / (tw * 1e-3) / 1e9, 1),
+                         "pct_of_copy_warm": round(100 * rec["copy"]["ms_warm"] / tw, 1)}
         out[name] = rec
         del bufs, ranks
         torch.cuda.empty_cache()
