@@ -88,7 +88,8 @@ typedef enum ra_op { RA_SUM = 0, RA_MAX = 1, RA_AVG = 2 } ra_op;
 typedef enum ra_algo {
   RA_ALGO_DEFAULT = -1,       /* RA_ALGO_FUSED (all-reduce: overridable with the RA_ALGO
                                  environment variable, by name or number) */
-  RA_ALGO_RING_STEP = 0,      /* one persistent kernel, 2(p-1) steps, grid barrier between steps */
+  RA_ALGO_RING_STEP = 0,      /* one persistent kernel, 2(p-1) steps, grid barrier between steps
+                                 (a workgroup barrier when the grid is one workgroup) */
   RA_ALGO_RING_PIPELINED = 1, /* chunks cut into slices; per-slice ready flags instead of barriers */
   RA_ALGO_RING_BIDIR = 2,     /* two counter-rotating rings, each on half of the buffer */
   RA_ALGO_FUSED = 3,          /* one pass: each element folded in its ring order, written to all ranks */
@@ -124,7 +125,11 @@ typedef struct ra_options {
                            (about four slices per worker per hop, at least 64 KiB).
                            Rounded up to a multiple of 16 bytes. */
   int64_t timeout_us;   /* budget of any single device-side wait; 0 = 10 s */
-  int32_t grid;         /* workgroups of persistent kernels; 0 = as many as fit the GPU */
+  int32_t grid;         /* workgroups of persistent kernels; 0 = the library chooses: as many
+                           as fit the GPU, no more than the largest step has tiles, and a
+                           single workgroup (its own barrier between steps, no device-wide
+                           barrier) when every step moves at most 256 16-byte vectors.
+                           A value above 1 always uses the device-wide barriers. */
   uint32_t flags;       /* RA_FLAG_* */
   uint64_t* step_ts;    /* optional DEVICE array of (steps + 1) uint64: device wall-clock
                            ticks at kernel start and as each step's barrier releases
