@@ -280,7 +280,7 @@ def alpha_measure(torch, B, inputs):
         tiny buffers (p=64, 1 KiB per rank): median step time, for the default
         launch (one workgroup at this size), for 8 channels, and for 64
         workgroups on the device-wide barrier.
-    (2) fit: T(S) = 2(p-1) a + 2(p-1)/p * S / B over S from 4 KiB to 16 MiB per
+    (2) fit: T(S) = 2(p-1) a + 2(p-1)/p * S / B over S from 1 KiB to 64 MiB per
         rank, p = 2 .. 64 (bf16), least squares per p; the tree under the same
         model (2 ceil(log2 p) steps of a + S / B) and the fused pass (a + 2pS/BW);
         the ring/tree crossover measured and from the fitted model.
@@ -316,9 +316,16 @@ def alpha_measure(torch, B, inputs):
         v = ts.cpu().numpy().astype(np.float64)
         steps.append(np.diff(v) / hz * 1e6)
     out["in_kernel_step_us_p64_1KiB_grid64"] = round(float(np.median(np.concatenate(steps))), 3)
+    # what a launch per step would pay instead: GPU time of a minimal launch (a
+    # 16-byte copy) back to back, per launch
+    s16, d16 = torch.ones(16, dtype=torch.uint8, device="cuda"), torch.empty(16, dtype=torch.uint8,
+                                                                              device="cuda")
+    per, _ = time_calls(lambda: B.ra_stream_copy(d16, s16), 21, torch)
+    out["launch_per_step_us"] = round(float(np.median(per[1:])) * 1e3, 3)
     fits = {}
     algos = ("ring_step", "ring_channels", "tree", "fused")
-    sizes = [4 << 10, 16 << 10, 64 << 10, 256 << 10, 1 << 20, 4 << 20, 16 << 20]
+    sizes = [1 << 10, 4 << 10, 16 << 10, 64 << 10, 256 << 10, 1 << 20, 4 << 20, 16 << 20,
+             64 << 20]
     for p in (2, 4, 8, 9, 16, 32, 64):
         levels = max(1, (p - 1).bit_length())
         rows = []
@@ -440,7 +447,8 @@ def main():
     launch_ms = sum(per) / len(per)
     achieved = min_bytes / (launch_ms * 1e-3) / 1e9
     sha = kernel_source_sha()
-    traffic = read_traffic(sha, min_bytes)
+    # the committed counter summary covers the fused kernel only
+    traffic = read_traffic(sha, min_bytes) if args.algo == "fused" else None
 
     result = {
         "metric": METRIC,
@@ -460,6 +468,9 @@ def main():
                    "bytes_counted": "2*p*S (each rank buffer read once and written once)",
                    "bytes_per_step": min_bytes},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        # nccl-tests' bus bandwidth, 2(p-1)/p * S / t: the rate each rank's links
+        # would carry; here emulated, no link is involved
+        "busbw_emulated_GBps": round(2 * (p - 1) / p * S / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": f"ra::k_fused<{dtype}>" if args.algo == "fused" else args.algo,
