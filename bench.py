@@ -189,6 +189,27 @@ def cpu_baseline(bufs, w, sample, torch):
                        f"(p={p}, N={m:,} {w['dtype']}); rate on 2*p*S of that sample")}
 
 
+def cpu_baseline_workloads(inputs):
+    """The oracle (lock-step ring simulator, numpy, one thread) timed in full on
+    every workload the host holds comfortably: the worked trace, the 1e6-element
+    int32, the 1 MiB-per-rank and the 256 MiB-per-rank configurations.  The
+    16 GB-per-rank one is sampled by cpu_baseline.  Input generation is not
+    timed."""
+    import oracle
+    out = {}
+    for name in ("trace_p4_fp32_n4", "p9_int32_n1000003", "p64_bf16_1MiB", "p8_fp32_256MiB"):
+        w = inputs.WORKLOADS[name]
+        xs = inputs.workload_inputs(name)
+        t0 = time.perf_counter()
+        oracle.ring_allreduce(xs, w["dtype"])
+        dt = time.perf_counter() - t0
+        S = w["n"] * inputs.ITEMSIZE[w["dtype"]]
+        out[name] = {"seconds": round(dt, 4), "GBps_on_2pS": round(2 * w["p"] * S / dt / 1e9, 4),
+                     "cores": 1}
+        del xs
+    return out
+
+
 def per_workload(torch, B, inputs):
     """Effective GB/s and % of HBM peak for every workload that fits comfortably,
     per algorithm, all rated on 2pS, and as % of a plain copy of the same bytes
@@ -523,6 +544,9 @@ def main():
         torch.cuda.empty_cache()
         log("per-workload rates")
         result["per_workload"] = per_workload(torch, B, inputs)
+        if not args.no_cpu_baseline:
+            log("cpu baseline per workload (oracle, in full)")
+            result["cpu_baseline_per_workload"] = cpu_baseline_workloads(inputs)
         log("alpha")
         result["alpha"] = alpha_measure(torch, B, inputs)
         result["alpha_us"] = result["alpha"]["in_kernel_step_us_p64_1KiB"]
