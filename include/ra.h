@@ -42,13 +42,16 @@
  *  Concurrency: calls on different streams may overlap; calls on one stream
  *  are ordered by the stream.  The library keeps a small device workspace per
  *  (device, stream), allocated on first use and kept until process exit.  The
- *  step-by-step and pipelined algorithms run persistent grids whose workgroups
- *  must all be resident at once; by default one grid fills the GPU, so
+ *  pipelined and channel algorithms, and the step algorithms when
+ *  ra_options.grid or step_ts is set, run persistent grids whose workgroups
+ *  must all be resident at once; by default such a grid fills the GPU, so
  *  overlapping such calls should each set ra_options.grid to their share (a
  *  call that cannot get all its workgroups resident times out instead of
- *  hanging).  The one-pass algorithms (FUSED, HIER_FUSED) launch ordinary
- *  grids, use no workspace, and can be captured in a HIP graph; the pipelined
- *  algorithm cannot (its ready counters are numbered per call on the host).
+ *  hanging).  The one-pass algorithms (FUSED, HIER_FUSED) and the step
+ *  algorithms' default launches (one per step, or one workgroup) are ordinary
+ *  grids with no device-side waits, and can be captured in a HIP graph; the
+ *  pipelined algorithm cannot (its ready counters are numbered per call on the
+ *  host).
  *
  * Return codes are ra_status values; ra_status_string() names them and
  * ra_last_error() gives the calling thread's last error message.
@@ -88,8 +91,13 @@ typedef enum ra_op { RA_SUM = 0, RA_MAX = 1, RA_AVG = 2 } ra_op;
 typedef enum ra_algo {
   RA_ALGO_DEFAULT = -1,       /* RA_ALGO_FUSED (all-reduce: overridable with the RA_ALGO
                                  environment variable, by name or number) */
-  RA_ALGO_RING_STEP = 0,      /* one persistent kernel, 2(p-1) steps, grid barrier between steps
-                                 (a workgroup barrier when the grid is one workgroup) */
+  RA_ALGO_RING_STEP = 0,      /* the 2(p-1) steps one after another.  Steps that move at most
+                                 256 16-byte vectors: one workgroup, its own barrier between
+                                 steps.  Larger steps: one ordinary launch per step (the
+                                 stream orders them), or, when ra_options.grid or step_ts is
+                                 set, one persistent grid with a device-wide barrier between
+                                 steps.  RING_BIDIR, TREE and HIER run their steps the same
+                                 way. */
   RA_ALGO_RING_PIPELINED = 1, /* chunks cut into slices; per-slice ready flags instead of barriers */
   RA_ALGO_RING_BIDIR = 2,     /* two counter-rotating rings, each on half of the buffer */
   RA_ALGO_FUSED = 3,          /* one pass: each element folded in its ring order, written to all ranks */
@@ -99,7 +107,7 @@ typedef enum ra_algo {
   RA_ALGO_AUTO = 6,           /* chosen per call by ra_select_algo (all-reduce only) */
   RA_ALGO_HIER = 7,           /* two-level ring on g ranks per node (ra_options.group): in-node
                                  reduce-scatter, cross-node ring all-reduce of each 1/g shard,
-                                 in-node all-gather; one launch, 2(g-1) + 2(p/g-1) steps */
+                                 in-node all-gather; 2(g-1) + 2(p/g-1) steps */
   RA_ALGO_HIER_FUSED = 8      /* one pass in the same two-level order (the same bits as HIER) */
 } ra_algo;
 
@@ -125,16 +133,19 @@ typedef struct ra_options {
                            (about four slices per worker per hop, at least 64 KiB).
                            Rounded up to a multiple of 16 bytes. */
   int64_t timeout_us;   /* budget of any single device-side wait; 0 = 10 s */
-  int32_t grid;         /* workgroups of persistent kernels; 0 = the library chooses: as many
-                           as fit the GPU, no more than the largest step has tiles, and a
-                           single workgroup (its own barrier between steps, no device-wide
-                           barrier) when every step moves at most 256 16-byte vectors.
-                           A value above 1 always uses the device-wide barriers. */
+  int32_t grid;         /* step algorithms (RING_STEP, RING_BIDIR, TREE, HIER): 0 = the
+                           library chooses (see RA_ALGO_RING_STEP).  1 with steps of at
+                           most 256 vectors: the single workgroup.  Otherwise a value
+                           above 0 runs one persistent grid of that many workgroups (at
+                           most as many as fit the GPU) with a device-wide barrier
+                           between steps.  RING_PIPELINED, RING_CHANNELS: workgroups of
+                           their persistent grid; 0 = as many as fit the GPU. */
   uint32_t flags;       /* RA_FLAG_* */
   uint64_t* step_ts;    /* optional DEVICE array of (steps + 1) uint64: device wall-clock
                            ticks at kernel start and as each step's barrier releases
-                           (RING_STEP, RING_BIDIR, TREE, RING_CHANNELS: channel 0).
-                           NULL = not recorded. */
+                           (RING_STEP, RING_BIDIR, TREE, HIER, RING_CHANNELS: channel 0).
+                           Setting it keeps the steps in one launch (one workgroup or a
+                           persistent grid).  NULL = not recorded. */
   int32_t channels;     /* RING_CHANNELS: number of channels, 1..64; 0 = automatic (8, one
                            per XCD, when every segment of a channel still gets a
                            workgroup, else 1).  Capped at the number of workgroups.

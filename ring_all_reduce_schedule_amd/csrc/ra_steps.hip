@@ -516,6 +516,27 @@ __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
 }
 
 
+// One step as a launch of its own: tile t = (segment, tile j of the segment),
+// one 16-byte vector per thread, as many workgroups as tiles.  The stream orders
+// consecutive launches, so the kernel boundary is the step's barrier.  On
+// MI355X a grid that covers the data once streams about a fifth faster than a
+// resident grid looping over it (16 GiB copy: 6.47 TB/s against 5.0-5.3 TB/s;
+// in-place add: 6.44 against 4.8-5.4 TB/s), and back-to-back launches on one
+// stream cost about 3 us each, less than the resident grid's device-wide barrier
+// (4-5 us).
+template <int DT, int OP, bool NT>
+__global__ __launch_bounds__(kBlock) void k_step(StepArgs a, int step, int64_t T, int64_t ntiles) {
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int seg = (int)(t / T);
+    const int64_t j = t - (int64_t)seg * T;
+    const Seg g = step_segment(a, step, seg);
+    if (g.add)
+      hop_tile<DT, OP, 1, true, NT>(a.P.b[g.src], a.P.b[g.dst], g.lo, g.hi, j, a.p, g.f);
+    else
+      hop_tile<DT, OP, 1, false, NT>(a.P.b[g.src], a.P.b[g.dst], g.lo, g.hi, j, a.p, g.f);
+  }
+}
+
 // ================================================================ pipelined
 
 struct PipeArgs {
@@ -693,9 +714,11 @@ static constexpr int kAutoChannels = 8;
 // Smallest grid that synchronises through the two-level barrier.
 static constexpr int kTwoLevelMinGrid = 128;
 // Steps with at most this many whole vectors (4 KiB) across all their segments
-// run on a single workgroup.  Measured on MI355X (bf16 ring): p = 64 at 4 KiB
-// per rank (256 vectors a step) 398 us against 595 with the device-wide
-// barriers, but at 16 KiB (1024 a step) 714 against 525.
+// run on a single workgroup; larger ones one launch per step.  Measured on
+// MI355X, bf16 ring, GPU time per all-reduce: p = 8 at 1 KiB per rank 24.5 us
+// on one workgroup against 40.1 with a launch per step, p = 64 331 against 375;
+// with the bound at 1024 vectors, p = 8 at 16 KiB took 54 us against 41 and
+// p = 64 600 against 335.
 static constexpr int64_t kBlockModeVecs = 256;
 static constexpr int kPipeU = 4;
 
@@ -724,13 +747,18 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   // every element range a step may work on (chunks of the ring's halves, whole
   // buffers for the tree, intra chunks and their inter pieces for the hierarchy)
   std::vector<std::pair<int64_t, int64_t>> ranges;
+  int64_t hier_intra = 0, hier_inter = 0;   // hier: widest in-node chunk, widest cross-node piece
   if (mode == kModeHier) {
     a.half[0] = a.half[1] = make_geo(0, n, a.g);
     for (int c = 0; c < a.g; ++c) {
       const int64_t lo = host_chunk_lo(0, n, a.g, c), hi = host_chunk_lo(0, n, a.g, c + 1);
       ranges.emplace_back(lo, hi);
-      for (int d = 0; d < a.m; ++d)
-        ranges.emplace_back(host_chunk_lo(lo, hi - lo, a.m, d), host_chunk_lo(lo, hi - lo, a.m, d + 1));
+      hier_intra = std::max(hier_intra, vecs_in(lo, hi, V));
+      for (int d = 0; d < a.m; ++d) {
+        const int64_t plo = host_chunk_lo(lo, hi - lo, a.m, d), phi = host_chunk_lo(lo, hi - lo, a.m, d + 1);
+        ranges.emplace_back(plo, phi);
+        hier_inter = std::max(hier_inter, vecs_in(plo, phi, V));
+      }
     }
   } else if (mode == kModeTree) {
     a.half[0] = a.half[1] = make_geo(0, n, p);
@@ -760,6 +788,61 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
     return w;
   };
   const int64_t maxvec = widest(1);
+  // segments (independent chunk transfers) of step st, as step_segments counts them
+  auto nseg_of = [&](int st) {
+    if (mode == kModeHier) return p;
+    if (mode == kModeTree) {
+      const int k = st < a.levels ? st : 2 * a.levels - 1 - st;
+      return (p - 1 - (1 << k)) / (2 << k) + 1;
+    }
+    return mode == kModeBidir ? 2 * p : p;
+  };
+  int most_seg = 0;
+  for (int st = step_begin; st < step_end; ++st) most_seg = std::max(most_seg, nseg_of(st));
+  // How the steps are separated.  Test hooks that need device waits (forced
+  // timeout, stress delays) always get the persistent grid and its barriers.
+  //  * block: steps that move at most kBlockModeVecs vectors run on a single
+  //    workgroup of the persistent kernel, its own barrier between steps;
+  //  * launch: otherwise one launch per step (k_step), unless the caller asks
+  //    for a grid, for channels (RING_CHANNELS) or for step timestamps.
+  //    Measured against the persistent grid on MI355X (bf16, GPU time per
+  //    all-reduce): ring p = 8 at 16 MiB per rank 0.149 ms against 0.227, at
+  //    2 GiB 13.0 against 13.4; p = 64 at 1 MiB 0.40 against 0.62; tree p = 8
+  //    at 2 GiB 11.7 against 13.9 ms;
+  //  * the persistent grid with device-wide barriers in every other case.
+  const bool hooks_free = sc.expect_extra == 0 && sc.stress == 0;
+  const int64_t step_vecs = (int64_t)most_seg * maxvec;
+  const bool block_ok = step_vecs <= kBlockModeVecs && (sc.grid == 0 || sc.grid == 1) &&
+                        sc.channels <= 1 && hooks_free;
+  const bool launch_ok = !block_ok && sc.grid == 0 && sc.channels == 1 && hooks_free &&
+                         sc.step_ts == nullptr;
+  if (launch_ok) {
+    a.channels = 1;
+    a.T = 0;
+    a.sync = kSyncDevice;
+    a.W = 0;
+    int widest_grid = 0;
+    const bool nt = streaming(p, n, DT);
+    for (int st = step_begin; st < step_end; ++st) {
+      // tiles per segment for this step's widest segment (the hierarchy's
+      // cross-node steps move pieces m times smaller than its in-node steps)
+      int64_t w = maxvec;
+      if (mode == kModeHier)
+        w = st < a.g - 1 || st >= a.g - 1 + 2 * (a.m - 1) ? hier_intra : hier_inter;
+      const int64_t T = std::max<int64_t>(1, (w + kBlock - 1) / kBlock);
+      const int64_t ntiles = (int64_t)nseg_of(st) * T;
+      const int g = (int)std::min<int64_t>(ntiles, kMaxGrid);
+      widest_grid = std::max(widest_grid, g);
+      if (nt)
+        hipLaunchKernelGGL((k_step<DT, OP, true>), dim3(g), dim3(kBlock), 0, s, a, st, T, ntiles);
+      else
+        hipLaunchKernelGGL((k_step<DT, OP, false>), dim3(g), dim3(kBlock), 0, s, a, st, T, ntiles);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    *grid_used = widest_grid;
+    return hipSuccess;
+  }
   const void* func = streaming(p, n, DT)
                          ? reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, true>)
                          : reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, false>);
@@ -768,20 +851,6 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   if (e != hipSuccess) return e;
   int grid = sc.grid > 0 ? std::min(sc.grid, resident) : resident;
   const int64_t tv = (int64_t)kBlock * kStepU;
-  // most segments any step has
-  int most_seg = 0;
-  for (int st = step_begin; st < step_end; ++st) {
-    int nseg;
-    if (mode == kModeHier) {
-      nseg = p;
-    } else if (mode == kModeTree) {
-      const int k = st < a.levels ? st : 2 * a.levels - 1 - st;
-      nseg = (p - 1 - (1 << k)) / (2 << k) + 1;
-    } else {
-      nseg = mode == kModeBidir ? 2 * p : p;
-    }
-    most_seg = std::max(most_seg, nseg);
-  }
   // no more workgroups than whole-segment tiles: on small buffers every extra
   // workgroup only adds to each barrier's cost
   const int64_t most = (int64_t)most_seg * std::max<int64_t>(1, (maxvec + tv - 1) / tv);
@@ -807,18 +876,17 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   a.W = std::max<int64_t>(1, maxvec);
   // Small steps run on one workgroup with its own barrier between steps: a
   // device-wide barrier costs microseconds (L2 write-back, atomics across XCDs,
-  // L2 invalidate), a workgroup barrier well under one.  Not when the caller
-  // asks for a grid, for channels, or for a test hook that needs the
-  // device-wide waits (forced timeout, stress delays).
-  const bool small = (int64_t)most_seg * a.W <= kBlockModeVecs;
-  if (small && (sc.grid == 0 || sc.grid == 1) && sc.channels <= 1 && sc.expect_extra == 0 &&
-      sc.stress == 0) {
+  // L2 invalidate), a workgroup barrier well under one.
+  if (block_ok) {
     a.sync = kSyncBlock;
     a.channels = 1;
     grid = 1;
   }
   *grid_used = grid;
   void* args[] = {&a};
+  // one workgroup is resident by itself: an ordinary launch, which costs far
+  // less than a cooperative one (measured: a two-step call 8.9 us against 22)
+  if (a.sync == kSyncBlock) return hipLaunchKernel(func, dim3(1), dim3(kBlock), args, 0, s);
   return hipLaunchCooperativeKernel(func, dim3(grid), dim3(kBlock), args, 0, s);
 }
 
