@@ -239,6 +239,18 @@ int reserve_flags(Workspace* w, int64_t entries, hipStream_t s, uint32_t* base) 
   return RA_OK;
 }
 
+// Whether a step call may run the persistent grid, and so needs the stream's
+// workspace (status word, barrier words, ready counters): the pipelined and
+// channel algorithms always; the other step algorithms only for a caller's
+// grid, step timestamps or a test hook.  Otherwise their steps run as ordinary
+// launches with no device-side waits, and the call allocates nothing -- it can
+// be captured in a HIP graph, even as the stream's first call.
+bool needs_workspace(int algo, const ra_options* opt) {
+  if (algo == RA_ALGO_RING_PIPELINED || algo == RA_ALGO_RING_CHANNELS) return true;
+  return opt && (opt->grid > 0 || opt->step_ts != nullptr ||
+                 (opt->flags & (RA_FLAG_FORCE_TIMEOUT | RA_FLAG_STRESS)) != 0);
+}
+
 int sync_cfg(const ra_options* opt, Workspace* w, ra::SyncCfg* sc) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -247,7 +259,7 @@ int sync_cfg(const ra_options* opt, Workspace* w, ra::SyncCfg* sc) {
   e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
   if (e != hipSuccess || khz <= 0) khz = 100000;   // 100 MHz, the gfx9 constant clock
   const int64_t us = opt && opt->timeout_us > 0 ? opt->timeout_us : 10 * 1000 * 1000;
-  sc->ws = w->hdr;
+  sc->ws = w ? w->hdr : nullptr;
   sc->limit_ticks = (uint64_t)us * (uint64_t)khz / 1000u;
   sc->expect_extra = opt && (opt->flags & RA_FLAG_FORCE_TIMEOUT) ? 1u : 0u;
   // a different delay pattern on every call
@@ -288,8 +300,11 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
     return RA_OK;
   }
   Workspace* w = nullptr;
-  int rc = get_workspace(s, &w);
-  if (rc != RA_OK) return rc;
+  int rc = RA_OK;
+  if (needs_workspace(algo, opt)) {
+    rc = get_workspace(s, &w);
+    if (rc != RA_OK) return rc;
+  }
   ra::SyncCfg sc;
   rc = sync_cfg(opt, w, &sc);
   if (rc != RA_OK) return rc;
@@ -397,10 +412,12 @@ int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int 
     debug_line("allreduce", algo, p, n, dtype, grid);
     return RA_OK;
   }
-  // bidirectional rings or tree: one cooperative launch of the step kernel
+  // bidirectional rings, tree or hierarchy: the step kernels
   Workspace* w = nullptr;
-  rc = get_workspace(stream, &w);
-  if (rc != RA_OK) return rc;
+  if (needs_workspace(algo, opt)) {
+    rc = get_workspace(stream, &w);
+    if (rc != RA_OK) return rc;
+  }
   ra::SyncCfg sc;
   rc = sync_cfg(opt, w, &sc);
   if (rc != RA_OK) return rc;

@@ -461,12 +461,6 @@ __device__ __forceinline__ void block_step(const StepArgs& a, const RankPtrs& P,
 template <int DT, int OP, int U, bool NT>
 __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
   if (ws_failed(a.ws)) return;
-  const int C = a.channels;
-  const int h = (int)(blockIdx.x % (uint32_t)C);
-  const uint32_t nbh = (gridDim.x - (uint32_t)h + (uint32_t)C - 1u) / (uint32_t)C;
-  const int64_t b = blockIdx.x / (uint32_t)C;       // index within the channel
-  uint32_t* bar = a.ws->bar[h];
-  const bool leader = b == 0;
   if (a.step_ts && blockIdx.x == 0 && threadIdx.x == 0) a.step_ts[0] = now_ticks();
   if (a.sync == kSyncBlock) {
     // one workgroup: its own barrier (with workgroup-scope release and acquire,
@@ -482,6 +476,12 @@ __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
     }
     return;
   }
+  const int C = a.channels;
+  const int h = (int)(blockIdx.x % (uint32_t)C);
+  const uint32_t nbh = (gridDim.x - (uint32_t)h + (uint32_t)C - 1u) / (uint32_t)C;
+  const int64_t b = blockIdx.x / (uint32_t)C;       // index within the channel
+  uint32_t* bar = a.ws->bar[h];
+  const bool leader = b == 0;
   uint32_t extra = a.expect_extra;
   for (int step = a.step_begin; step < a.step_end; ++step) {
     const int64_t ntiles = (int64_t)step_segments(a, step) * a.T;
@@ -846,6 +846,22 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   const void* func = streaming(p, n, DT)
                          ? reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, true>)
                          : reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, false>);
+  void* args[] = {&a};
+  // Small steps run on one workgroup with its own barrier between steps: a
+  // device-wide barrier costs microseconds (L2 write-back, atomics across XCDs,
+  // L2 invalidate), a workgroup barrier well under one.  One workgroup is
+  // resident by itself, so this is an ordinary launch, which costs far less
+  // than a cooperative one (measured: a two-step call 8.9 us against 22).
+  if (block_ok) {
+    a.sync = kSyncBlock;
+    a.channels = 1;
+    a.T = 1;
+    a.W = std::max<int64_t>(1, maxvec);
+    *grid_used = 1;
+    return hipLaunchKernel(func, dim3(1), dim3(kBlock), args, 0, s);
+  }
+  // the persistent grid's barriers live in the stream's workspace
+  if (sc.ws == nullptr) return hipErrorInvalidValue;
   int resident = 0;
   hipError_t e = resident_blocks(func, &resident);
   if (e != hipSuccess) return e;
@@ -874,19 +890,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
            : a.channels % kXcds == 0 ? kSyncOneXcd : kSyncDevice;
   a.T = std::max<int64_t>(1, (widest(a.channels) + tv - 1) / tv);
   a.W = std::max<int64_t>(1, maxvec);
-  // Small steps run on one workgroup with its own barrier between steps: a
-  // device-wide barrier costs microseconds (L2 write-back, atomics across XCDs,
-  // L2 invalidate), a workgroup barrier well under one.
-  if (block_ok) {
-    a.sync = kSyncBlock;
-    a.channels = 1;
-    grid = 1;
-  }
   *grid_used = grid;
-  void* args[] = {&a};
-  // one workgroup is resident by itself: an ordinary launch, which costs far
-  // less than a cooperative one (measured: a two-step call 8.9 us against 22)
-  if (a.sync == kSyncBlock) return hipLaunchKernel(func, dim3(1), dim3(kBlock), args, 0, s);
   return hipLaunchCooperativeKernel(func, dim3(grid), dim3(kBlock), args, 0, s);
 }
 

@@ -256,6 +256,7 @@ __device__ __forceinline__ void stress_delay(uint32_t seed, uint32_t point) {
 }
 
 __device__ __forceinline__ bool ws_failed(WsHeader* ws) {
+  if (ws == nullptr) return false;          // a launch without workspace has no waits
   __shared__ int bad;
   if (threadIdx.x == 0) bad = ld_relaxed(&ws->status) != 0;
   __syncthreads();

@@ -4,8 +4,12 @@
   library keeps one workspace (barrier words, status) per (device, stream), so
   the grid barriers of concurrent step-by-step calls never mix.  Each call is
   given 64 workgroups so that both persistent grids are resident together.
-* The one-pass algorithms launch ordinary kernels and use no workspace, so they
-  can be captured into a HIP graph; every replay (with eager work and
+* The same with the library's default launches (one launch per step), which
+  use no workspace and need no co-residency.
+* The one-pass algorithms, and the step algorithms' default launches (one
+  workgroup for tiny steps, one launch per step otherwise), are ordinary
+  kernels with no workspace, so they can be captured into a HIP graph -- on a
+  stream that has never run a call; every replay (with eager work and
   synchronisation in between) must equal the eager result.
 """
 
@@ -21,24 +25,28 @@ from tests.gpu_util import require_gpu, to_dev, from_dev, same_bits, first_diff
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("algo", ["ring_step", "tree", "hier", "ring_channels", "ring_pipelined"])
-def test_two_streams_at_once(algo):
+@pytest.mark.parametrize("algo,grid", [("ring_step", 64), ("tree", 64), ("hier", 64),
+                                       ("ring_channels", 64), ("ring_pipelined", 64),
+                                       ("ring_step", 0), ("tree", 0), ("hier", 0), ("ring_bidir", 0)])
+def test_two_streams_at_once(algo, grid):
     require_gpu()
     p, n, dtype = 8, 300_007, "float32"
     xa = inputs.make_inputs(p, n, dtype, seed=1)
     xb = inputs.make_inputs(p, n, dtype, seed=2)
     want = {"tree": lambda x: oracle.tree_allreduce(x, dtype)[0][0],
-            "hier": lambda x: oracle.hier_fold(x, dtype, 8)}.get(algo, lambda x: oracle.ring_fold(x, dtype))
+            "hier": lambda x: oracle.hier_fold(x, dtype, 8),
+            "ring_bidir": lambda x: oracle.bidir_allreduce(x, dtype)[0][0]}.get(
+                algo, lambda x: oracle.ring_fold(x, dtype))
     ta, tb = to_dev(xa, dtype), to_dev(xb, dtype)
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
     torch.cuda.synchronize()
-    print(f"[case] two streams algo={algo}", flush=True)
+    print(f"[case] two streams algo={algo} grid={grid}", flush=True)
     for _ in range(3):
         # 64 workgroups each: both persistent grids fit on the GPU together
         with torch.cuda.stream(sa):
-            B.ra_allreduce_ex(ta, algo=algo, grid=64)
+            B.ra_allreduce_ex(ta, algo=algo, grid=grid)
         with torch.cuda.stream(sb):
-            B.ra_allreduce_ex(tb, algo=algo, grid=64)
+            B.ra_allreduce_ex(tb, algo=algo, grid=grid)
         B.ra_stream_status(stream=sa)
         B.ra_stream_status(stream=sb)
         # the next round starts from this round's result on both streams
@@ -50,10 +58,27 @@ def test_two_streams_at_once(algo):
             assert same_bits(g, xb[0], dtype), f"stream b rank {r} at {first_diff(g, xb[0], dtype)}"
 
 
-@pytest.mark.parametrize("call", ["allreduce_fused", "allreduce_hier_fused", "rs_then_ag_fused"])
+STEP_CALLS = {"allreduce_ring_step": "ring_step", "allreduce_tree": "tree",
+              "allreduce_hier": "hier", "allreduce_ring_bidir": "ring_bidir",
+              "allreduce_ring_step_tiny": "ring_step", "allreduce_tree_tiny": "tree"}
+
+
+def _graph_want(call, xs, dtype):
+    algo = STEP_CALLS.get(call)
+    if call == "allreduce_hier_fused" or algo == "hier":
+        return oracle.hier_fold(xs, dtype, 3)
+    if algo == "tree":
+        return oracle.tree_allreduce(xs, dtype)[0][0]
+    if algo == "ring_bidir":
+        return oracle.bidir_allreduce(xs, dtype)[0][0]
+    return oracle.ring_fold(xs, dtype)
+
+
+@pytest.mark.parametrize("call", ["allreduce_fused", "allreduce_hier_fused", "rs_then_ag_fused",
+                                  "rs_then_ag_ring_step"] + list(STEP_CALLS))
 def test_graph_capture_and_replay(call):
     require_gpu()
-    p, n, dtype = 9, 100_003, "bfloat16"
+    p, n, dtype = 9, (200 if call.endswith("_tiny") else 100_003), "bfloat16"
     xs = inputs.make_inputs(p, n, dtype, seed=3)
     src = to_dev(xs, dtype)
     bufs = [torch.empty_like(s) for s in src]
@@ -63,6 +88,11 @@ def test_graph_capture_and_replay(call):
             B.ra_allreduce_ex(bufs, algo="fused")
         elif call == "allreduce_hier_fused":
             B.ra_allreduce_ex(bufs, algo="hier_fused", group=3)
+        elif call in STEP_CALLS:
+            B.ra_allreduce_ex(bufs, algo=STEP_CALLS[call], group=3)
+        elif call == "rs_then_ag_ring_step":
+            B.ra_reduce_scatter_ex(bufs, algo="ring_step")
+            B.ra_all_gather_ex(bufs, algo="ring_step")
         else:
             B.ra_reduce_scatter_ex(bufs, algo="fused")
             B.ra_all_gather_ex(bufs, algo="fused")
@@ -73,7 +103,7 @@ def test_graph_capture_and_replay(call):
     run()
     B.ra_stream_status()
     eager = from_dev(bufs, dtype)
-    want = oracle.hier_fold(xs, dtype, 3) if call == "allreduce_hier_fused" else oracle.ring_fold(xs, dtype)
+    want = _graph_want(call, xs, dtype)
     assert all(same_bits(e, want, dtype) for e in eager)
 
     g = torch.cuda.CUDAGraph()
