@@ -337,12 +337,17 @@ def alpha_measure(torch, B, inputs):
         v = ts.cpu().numpy().astype(np.float64)
         steps.append(np.diff(v) / hz * 1e6)
     out["in_kernel_step_us_p64_1KiB_grid64"] = round(float(np.median(np.concatenate(steps))), 3)
-    # what a launch per step would pay instead: GPU time of a minimal launch (a
-    # 16-byte copy) back to back, per launch
+    # what a launch per step pays: 64 minimal launches (16-byte copies) queued back
+    # to back on the stream, timed as one span (events between launches would add
+    # their own cost)
     s16, d16 = torch.ones(16, dtype=torch.uint8, device="cuda"), torch.empty(16, dtype=torch.uint8,
                                                                               device="cuda")
-    per, _ = time_calls(lambda: B.ra_stream_copy(d16, s16), 21, torch)
-    out["launch_per_step_us"] = round(float(np.median(per[1:])) * 1e3, 3)
+    B.ra_stream_copy(d16, s16)
+    spans = []
+    for _ in range(5):
+        _, span = time_calls(lambda: [B.ra_stream_copy(d16, s16) for _ in range(64)], 1, torch)
+        spans.append(span / 64)
+    out["launch_per_step_us"] = round(float(np.median(spans)) * 1e3, 3)
     fits = {}
     algos = ("ring_step", "ring_channels", "tree", "fused")
     sizes = [1 << 10, 4 << 10, 16 << 10, 64 << 10, 256 << 10, 1 << 20, 4 << 20, 16 << 20,
