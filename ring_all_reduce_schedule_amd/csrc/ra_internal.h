@@ -17,9 +17,10 @@ struct WsHeader;
 // Kernel families of the step-by-step schedule run by launch_steps().
 enum StepMode { kModeRing = 0, kModeBidir = 1, kModeTree = 2, kModeHier = 3 };
 
-// What every persistent (grid-synchronised) launch needs besides the data.
+// What the step and pipelined launchers need besides the data.
 struct SyncCfg {
-  WsHeader* ws;           // device workspace of this (device, stream)
+  WsHeader* ws;           // device workspace of this (device, stream); null when the call
+                          // cannot run a persistent grid (its launches have no waits)
   uint64_t limit_ticks;   // bound of one device-side wait, device clock ticks
   uint32_t expect_extra;  // 1 = first wait expects an arrival that never comes (test hook)
   uint32_t stress;        // nonzero: pseudo-random delays before arrivals and hops (test hook)
@@ -38,11 +39,15 @@ struct SyncCfg {
 hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, int op, bool wide,
                         int mode, hipStream_t s, int* grid_used);
 
-// Steps [step_begin, step_end) of a step-by-step schedule, one cooperative launch,
-// a grid barrier between steps.  Ring/bidir: steps 0..p-2 reduce-scatter,
-// p-1..2p-3 all-gather.  Tree: L reduce levels then L broadcast levels.
-// Hier (g = sc.group, m = p / g): g-1 intra-node reduce-scatter steps, 2(m-1)
-// inter-node all-reduce steps on the shards, g-1 intra-node all-gather steps.
+// Steps [step_begin, step_end) of a step-by-step schedule, in order.  Steps
+// that move at most 256 vectors run on one workgroup (its own barrier between
+// steps); larger ones as one launch per step, or -- when sc asks for a grid,
+// channels, step timestamps or a test hook -- as one persistent cooperative
+// launch with a grid barrier between steps.  Ring/bidir: steps 0..p-2
+// reduce-scatter, p-1..2p-3 all-gather.  Tree: L reduce levels then L broadcast
+// levels.  Hier (g = sc.group, m = p / g): g-1 intra-node reduce-scatter steps,
+// 2(m-1) inter-node all-reduce steps on the shards, g-1 intra-node all-gather
+// steps.
 hipError_t launch_steps(const RankPtrs& P, int p, int64_t n, int dtype, int op, StepMode mode,
                         int step_begin, int step_end, const SyncCfg& sc, hipStream_t s,
                         int* grid_used);

@@ -7,10 +7,16 @@
 // schedule", "An implementation", "What real libraries add"; "Derive the cost of
 // a ring all-reduce" (aiinfrainterviews.com), section "Where it stops scaling".
 //
-//   k_steps      the schedule step by step in one persistent cooperative launch:
-//                reduce-scatter steps, all-gather steps (forward ring, or both
-//                rings of the bidirectional variant on the two halves), or the
-//                binomial tree's levels; a grid barrier separates steps.
+//   k_step       one step of the schedule as a launch of its own: reduce-scatter
+//                and all-gather steps (forward ring, or both rings of the
+//                bidirectional variant on the two halves), the binomial tree's
+//                levels, or the hierarchy's in-node and cross-node steps; the
+//                stream's ordering separates steps.  The default for steps that
+//                move more than 256 vectors.
+//   k_steps      the same schedules in one launch: on a single workgroup (its own
+//                barrier between steps; the default for smaller steps), or on a
+//                persistent cooperative grid with a grid barrier between steps
+//                (a caller's grid, channels, step timestamps, test hooks).
 //   k_pipelined  the forward ring with chunks cut into slices; workgroups are
 //                assigned to ranks, and a rank forwards slice k as soon as its
 //                left neighbour has finished slice k (per-slice ready counters
