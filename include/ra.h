@@ -245,9 +245,10 @@ int ra_stream_status(hipStream_t stream);
 
 /*
  * ra_select_algo -- the algorithm RA_ALGO_AUTO runs for an all-reduce of p buffers
- * of n elements of `dtype` ([InDepth] "Trade-offs": the library picks ring or
- * tree per call from message size and rank count; [Derive] "Where it stops
- * scaling": the choice reverses when S/p falls to a few hundred kilobytes).
+ * of n elements of `dtype` ([InDepth] "Trade-offs": libraries choose between
+ * ring and tree for each call, by the size of the message and the number of
+ * ranks; [Derive] "Where it stops scaling": the tree takes over when each
+ * rank's share shrinks to some hundreds of kilobytes).
  *   With opt->link_alpha_us > 0 and opt->link_GBps > 0: the pages' cost model for
  *   S = n * element size bytes -- T_ring = 2(p-1) alpha + 2(p-1)/p * S/B
  *   ([Derive] "Where it stops scaling") against T_tree = 2 ceil(log2 p) (alpha + S/B),

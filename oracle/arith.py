@@ -2,8 +2,8 @@
 
 Which precision each hop uses: [InDepth] "An implementation" accumulates every
 hop of the torch ring with an in-place add on the tensor itself, i.e. in the
-tensor's own dtype, and [Derive] "What interviewers probe next" states that the
-library reduces in the buffer's dtype unless told otherwise.  So every hop of the
+tensor's own dtype, and [Derive] "What interviewers probe next" notes that the
+library's default accumulation type is the buffers' own.  So every hop of the
 ring rounds its sum back to the element type of the buffers:
 
 * int32    -- two's-complement sum, wrapped modulo 2**32 (the pages are silent

@@ -79,8 +79,8 @@ def choose_ring_or_tree(p, size_bytes, bandwidth, alpha):
     """The algorithm the cost model favours: "tree" if T_tree < T_ring, else "ring".
 
     [InDepth] "Trade-offs" and [Derive] "Where it stops scaling": libraries price
-    both algorithms per call and take the ring for large buffers and the tree
-    for small ones.  Ties go to the ring.
+    both algorithms for every call; big messages go to the ring, small ones to
+    the tree.  Ties go to the ring.
     """
     return "tree" if t_tree(p, size_bytes, bandwidth, alpha) < t_ring(p, size_bytes, bandwidth, alpha) else "ring"
 

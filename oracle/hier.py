@@ -1,10 +1,11 @@
 """Hierarchical (two-level) ring all-reduce (oracle; test infrastructure only).
 
-[InDepth] "What real libraries add", hierarchy: a 2D scheme runs a reduce-scatter
-inside each node, then an all-reduce across nodes on each GPU's 1/g shard among
-the GPUs with the same local rank, then an all-gather inside the node; each GPU's
-cross-node traffic shrinks by the factor g.  [Deepinsea] "Ring vs Hierarchical"
-describes the same two-level ring.
+[InDepth] "What real libraries add", hierarchy: the two-level scheme first
+reduce-scatters within every node; each rank then all-reduces the 1/g of the
+buffer it now owns with its counterparts (same position within their nodes) in
+the other nodes; a final in-node all-gather spreads the result.  Only the middle
+phase crosses nodes, and it moves 1/g of what a flat ring would send across
+them.  [Deepinsea] "Ring vs Hierarchical" describes the same two-level ring.
 
 Reading of the layout (the pages give none): p = g * m ranks; node q holds ranks
 q*g .. q*g + g - 1 and rank r has local index l = r mod g.  Every ring below is
@@ -62,7 +63,7 @@ def hier_allreduce(bufs, dtype, g, op="sum"):
         for r, b, s in zip(ranks, out, tr.sent):
             bufs[r] = b
             inner[r] += s
-    # 2. all-reduce across nodes on each local index's shard
+    # 2. cross-node ring all-reduce of the shard each local index owns
     intra = chunk_bounds(n, g)
     for l, ranks in enumerate(locals_):
         lo, hi = intra[(l + 1) % g]

@@ -1,9 +1,10 @@
 """Chunk partition and the ring's index rules (oracle; test infrastructure only).
 
-[InDepth] "The schedule": p ranks sit on a logical ring; each sends only to its
-right neighbour and receives only from its left.  The N-element buffer of every
-rank is cut into p chunks.  Reduce-scatter step s: rank r sends chunk
-(r - s) mod p to rank r + 1, which adds it into its own copy.  All-gather step s:
+[InDepth] "The schedule": the p ranks form a logical ring in which every rank
+talks to two neighbours, sending to the next and receiving from the previous.
+Every rank's N-element buffer is cut into p chunks.  Reduce-scatter step s:
+rank r sends chunk (r - s) mod p to rank r + 1, whose copy of that chunk then
+becomes the sum of the two.  All-gather step s:
 rank r sends chunk (r + 1 - s) mod p and the receiver overwrites.  After the
 reduce-scatter rank r holds the finished sum of chunk (r + 1) mod p.
 

@@ -1,6 +1,6 @@
 """Streams and graphs (through the C ABI).
 
-* Two streams run all-reduces at the same time on different buffers: the
+* Two streams run all-reduces concurrently, each on its own buffers: the
   library keeps one workspace (barrier words, status) per (device, stream), so
   the grid barriers of concurrent step-by-step calls never mix.  Each call is
   given 64 workgroups so that both persistent grids are resident together.
