@@ -808,7 +808,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   // How the steps are separated.  Test hooks that need device waits (forced
   // timeout, stress delays) always get the persistent grid and its barriers.
   //  * block: steps that move at most kBlockModeVecs vectors run on a single
-  //    workgroup of the persistent kernel, its own barrier between steps;
+  //    workgroup of k_steps, its own barrier between steps;
   //  * launch: otherwise one launch per step (k_step), unless the caller asks
   //    for a grid, for channels (RING_CHANNELS) or for step timestamps.
   //    Measured against the persistent grid on MI355X (bf16, GPU time per
