@@ -64,7 +64,7 @@ def parse_args():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip variants, alpha, ceiling (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 27,
+    ap.add_argument("--cpu-sample", type=int, default=3 << 27,
                     help="elements per rank of the CPU-oracle sample")
     ap.add_argument("--mode", default="allreduce", choices=["allreduce", "copy"],
                     help="copy: only the plain copy kernel, for counter calibration")
