@@ -47,7 +47,10 @@
  *  must all be resident at once; by default such a grid fills the GPU, so
  *  overlapping such calls should each set ra_options.grid to their share (a
  *  call that cannot get all its workgroups resident times out instead of
- *  hanging).  The one-pass algorithms (FUSED, HIER_FUSED) and the step
+ *  hanging).  Persistent grids are cooperative launches, and a cooperative
+ *  launch fails (RA_ERR_HIP, "cannot be performed in the present state") while
+ *  another live process on the same GPU has made one; the default launches of
+ *  every algorithm but the pipelined and channel ones are not cooperative.  The one-pass algorithms (FUSED, HIER_FUSED) and the step
  *  algorithms' default launches (one per step, or one workgroup) are ordinary
  *  grids with no device-side waits, and can be captured in a HIP graph; the
  *  pipelined algorithm cannot (its ready counters are numbered per call on the

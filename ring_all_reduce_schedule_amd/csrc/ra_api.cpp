@@ -277,10 +277,13 @@ void fill_ptrs(void* const* bufs, int p, ra::RankPtrs* P) {
   for (int r = 0; r < p; ++r) P->b[r] = bufs[r];
 }
 
-void debug_line(const char* call, int algo, int p, int64_t n, int dtype, int grid) {
+// launches: kernels the call enqueued (the step algorithms run one per step on
+// larger buffers)
+void debug_line(const char* call, int algo, int p, int64_t n, int dtype, int grid,
+                int launches = 1) {
   if (!debug_on()) return;
-  std::fprintf(stderr, "[ra] %s algo=%s p=%d n=%lld dtype=%d grid=%d ring=", call,
-               algo_name(algo), p, (long long)n, dtype, grid);
+  std::fprintf(stderr, "[ra] %s algo=%s p=%d n=%lld dtype=%d grid=%d launches=%d ring=", call,
+               algo_name(algo), p, (long long)n, dtype, grid, launches);
   for (int r = 0; r < p; ++r) std::fprintf(stderr, "%d%s", r, r + 1 < p ? "->" : "->0\n");
 }
 
@@ -310,7 +313,7 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
   if (rc != RA_OK) return rc;
   ra::RankPtrs P;
   fill_ptrs(bufs, p, &P);
-  int grid = 0;
+  int grid = 0, launches = 1;
   hipError_t e;
   if (algo == RA_ALGO_RING_PIPELINED) {
     int64_t slice = opt && opt->slice_elems > 0
@@ -326,10 +329,11 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
                              sc, s, &grid);
   } else {
     if (algo == RA_ALGO_RING_CHANNELS) sc.channels = opt ? opt->channels : 0;   // 0: automatic
-    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeRing, hop_begin, hop_end, sc, s, &grid);
+    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeRing, hop_begin, hop_end, sc, s, &grid,
+                         &launches);
   }
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
-  debug_line(call, algo, p, n, dtype, grid);
+  debug_line(call, algo, p, n, dtype, grid, launches);
   return RA_OK;
 }
 
@@ -423,22 +427,24 @@ int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int 
   if (rc != RA_OK) return rc;
   ra::RankPtrs P;
   fill_ptrs(bufs, p, &P);
-  int grid = 0;
+  int grid = 0, launches = 1;
   hipError_t e;
   if (algo == RA_ALGO_RING_BIDIR) {
-    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeBidir, 0, 2 * (p - 1), sc, stream, &grid);
+    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeBidir, 0, 2 * (p - 1), sc, stream, &grid,
+                         &launches);
   } else if (algo == RA_ALGO_HIER) {
     sc.group = hier_group(opt, p);
     const int m = p / sc.group;
     e = ra::launch_steps(P, p, n, dtype, op, ra::kModeHier, 0, 2 * (sc.group - 1) + 2 * (m - 1), sc,
-                         stream, &grid);
+                         stream, &grid, &launches);
   } else {
     int levels = 0;
     while ((1 << levels) < p) ++levels;
-    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeTree, 0, 2 * levels, sc, stream, &grid);
+    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeTree, 0, 2 * levels, sc, stream, &grid,
+                         &launches);
   }
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
-  debug_line("allreduce", algo, p, n, dtype, grid);
+  debug_line("allreduce", algo, p, n, dtype, grid, launches);
   return RA_OK;
 }
 

@@ -50,7 +50,7 @@ hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, int op, 
 // steps.
 hipError_t launch_steps(const RankPtrs& P, int p, int64_t n, int dtype, int op, StepMode mode,
                         int step_begin, int step_end, const SyncCfg& sc, hipStream_t s,
-                        int* grid_used);
+                        int* grid_used, int* launches);
 
 // One pass in the two-level order: node partials folded over local ranks,
 // then folded over nodes (g ranks per node), stored to every rank.

@@ -730,7 +730,8 @@ static constexpr int kPipeU = 4;
 
 template <int DT, int OP>
 static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, int step_begin,
-                           int step_end, const SyncCfg& sc, hipStream_t s, int* grid_used) {
+                           int step_end, const SyncCfg& sc, hipStream_t s, int* grid_used,
+                           int* launches) {
   const int V = Elem<DT>::V;
   StepArgs a;
   a.P = P;
@@ -847,6 +848,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
       if (e != hipSuccess) return e;
     }
     *grid_used = widest_grid;
+    *launches = step_end - step_begin;
     return hipSuccess;
   }
   const void* func = streaming(p, n, DT)
@@ -864,6 +866,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
     a.T = 1;
     a.W = std::max<int64_t>(1, maxvec);
     *grid_used = 1;
+    *launches = 1;
     return hipLaunchKernel(func, dim3(1), dim3(kBlock), args, 0, s);
   }
   // the persistent grid's barriers live in the stream's workspace
@@ -897,6 +900,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   a.T = std::max<int64_t>(1, (widest(a.channels) + tv - 1) / tv);
   a.W = std::max<int64_t>(1, maxvec);
   *grid_used = grid;
+  *launches = 1;
   return hipLaunchCooperativeKernel(func, dim3(grid), dim3(kBlock), args, 0, s);
 }
 
@@ -904,26 +908,27 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
 template <int DT>
 static hipError_t steps_op(const RankPtrs& P, int p, int64_t n, int op, StepMode mode,
                            int step_begin, int step_end, const SyncCfg& sc, hipStream_t s,
-                           int* grid_used) {
+                           int* grid_used, int* launches) {
   constexpr bool kFloat = DT == 1 || DT == 2 || DT == 3 || DT == 4;
-  if (op == kMax) return steps_dt<DT, kMax>(P, p, n, mode, step_begin, step_end, sc, s, grid_used);
+  if (op == kMax)
+    return steps_dt<DT, kMax>(P, p, n, mode, step_begin, step_end, sc, s, grid_used, launches);
   if constexpr (kFloat) {
     if (op == kAvg)
-      return steps_dt<DT, kAvg>(P, p, n, mode, step_begin, step_end, sc, s, grid_used);
+      return steps_dt<DT, kAvg>(P, p, n, mode, step_begin, step_end, sc, s, grid_used, launches);
   }
-  return steps_dt<DT, kSum>(P, p, n, mode, step_begin, step_end, sc, s, grid_used);
+  return steps_dt<DT, kSum>(P, p, n, mode, step_begin, step_end, sc, s, grid_used, launches);
 }
 
 hipError_t launch_steps(const RankPtrs& P, int p, int64_t n, int dtype, int op, StepMode mode,
                         int step_begin, int step_end, const SyncCfg& sc, hipStream_t s,
-                        int* grid_used) {
+                        int* grid_used, int* launches) {
   switch (dtype) {
-    case 0: return steps_op<0>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used);
-    case 1: return steps_op<1>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used);
-    case 2: return steps_op<2>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used);
-    case 3: return steps_op<3>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used);
-    case 4: return steps_op<4>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used);
-    default: return steps_op<5>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used);
+    case 0: return steps_op<0>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used, launches);
+    case 1: return steps_op<1>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used, launches);
+    case 2: return steps_op<2>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used, launches);
+    case 3: return steps_op<3>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used, launches);
+    case 4: return steps_op<4>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used, launches);
+    default: return steps_op<5>(P, p, n, op, mode, step_begin, step_end, sc, s, grid_used, launches);
   }
 }
 
