@@ -189,6 +189,14 @@ def cpu_baseline(bufs, w, sample, torch):
                        f"(p={p}, N={m:,} {w['dtype']}); rate on 2*p*S of that sample")}
 
 
+def hier_group(p):
+    """Ranks per node for the hierarchical algorithms here: the largest divisor of
+    p that is at most 8 and leaves at least two nodes (p = 8: 2 nodes of 4;
+    p = 9: 3 of 3; p = 64: 8 of 8).  The library's own default for p = 8 is one
+    node of 8, where the hierarchy is the flat ring."""
+    return max([g for g in range(1, min(8, p - 1) + 1) if p % g == 0] or [1])
+
+
 def cpu_baseline_workloads(inputs):
     """The oracle (lock-step ring simulator, numpy, one thread) timed in full on
     every workload the host holds comfortably: the worked trace, the 1e6-element
@@ -249,8 +257,10 @@ def per_workload(torch, B, inputs):
                        "ms_warm": round(tw, 4), "GBps_warm": round(2 * cb / (tw * 1e-3) / 1e9, 1)}
         del src, dst
         ranks = B.RankBuffers(bufs)
+        rec["hier_group"] = hier_group(p)
         for algo in ("fused", "ring_step", "ring_channels", "tree", "hier", "hier_fused"):
-            fn = lambda a=algo: B.ra_allreduce_ex(ranks, algo=a)
+            kw = {"group": hier_group(p)} if algo.startswith("hier") else {}
+            fn = lambda a=algo, k=kw: B.ra_allreduce_ex(ranks, algo=a, **k)
             fn()
             B.ra_stream_status()
             cold, _ = time_calls(fn, 9, torch, flush=flush)
@@ -512,7 +522,8 @@ def main():
         fill_workload(args.workload, bufs, torch, inputs)
         variants = {}
         runs = [(a, a, {}) for a in ("ring_step", "ring_pipelined", "ring_bidir", "ring_channels",
-                                     "tree", "hier", "hier_fused")]
+                                     "tree")]
+        runs += [(a, a, {"group": hier_group(p)}) for a in ("hier", "hier_fused")]
         runs += [("fused_wide_fp32_accumulate", "fused", {"wide": True}),
                  ("fused_avg", "fused", {"op": "avg"}), ("fused_max", "fused", {"op": "max"})]
         for name, algo, kw in runs:
@@ -524,6 +535,8 @@ def main():
             B.ra_stream_status()
             t = sum(vper) / len(vper)
             variants[name] = {"ms": round(t, 3), "GBps_on_2pS": round(min_bytes / (t * 1e-3) / 1e9, 1)}
+            if "group" in kw:
+                variants[name]["group"] = kw["group"]
         result["variants"] = variants
         log("standalone phases")
         fill_workload(args.workload, bufs, torch, inputs)
