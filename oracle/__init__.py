@@ -22,8 +22,8 @@ Sources, cited by page title and section throughout:
 * [Fable]     "Ring All-Reduce" fable of the Jade Ring Pond (fables.day) --
               "What it is", "Metaphor mapping".
 
-Element storage: int32 -> numpy int32, float32 -> numpy float32, bfloat16 ->
-numpy uint16 holding the bf16 bit pattern.
+Element storage: int32 / int64 / float16 / float32 / float64 -> the numpy type
+of that name, bfloat16 -> numpy uint16 holding the bf16 bit pattern.
 
 Modules
   schedule  chunk partition and the send/receive index rules

@@ -1,0 +1,128 @@
+"""Property-based pins of the oracle (CPU, hypothesis).
+
+Random small cases (p up to 12, n up to 200, every element type and reduction)
+check each formulation of the oracle against an independent one:
+
+* the lock-step simulator's result on every rank equals the closed-form fold
+  in ring order, and its reduce-scatter leaves each owned chunk equal to the
+  fold of that chunk ([InDepth] "The schedule");
+* integer sums by every algorithm (ring, mirrored ring, bidirectional rings,
+  binomial tree, two-level ring with any group size dividing p) equal the
+  elementwise sum computed with Python integers modulo 2^32 or 2^64, since
+  wrapped integer addition is exact in any order;
+* maxima by every algorithm equal numpy's elementwise maximum over the ranks
+  for finite inputs, since a maximum is exact in any order;
+* the chunk partition covers [0, n) with sizes that differ by at most one, the
+  larger ones first ([InDepth] "An implementation").
+"""
+
+import numpy as np
+import pytest
+
+hypothesis = pytest.importorskip("hypothesis")
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+import oracle  # noqa: E402
+from ring_all_reduce_schedule_amd import inputs  # noqa: E402
+
+DTYPES = ["int32", "int64", "float16", "bfloat16", "float32", "float64"]
+INTS = {"int32": 32, "int64": 64}
+SETTINGS = settings(max_examples=60, deadline=None, derandomize=True)
+
+case = st.tuples(st.integers(1, 12), st.integers(0, 200), st.sampled_from(DTYPES),
+                 st.integers(0, 2**31 - 1))
+
+
+def _inputs(p, n, dtype, seed):
+    if dtype == "int64":
+        return inputs.make_inputs(p, n, dtype, seed, lo=-2**62, hi=2**62)
+    if dtype == "int32":
+        return inputs.make_inputs(p, n, dtype, seed, lo=-2**30, hi=2**30)
+    return inputs.make_inputs(p, n, dtype, seed, sigma=3.0)
+
+
+def _bits(a, dtype):
+    return np.asarray(a).view({"int32": np.uint32, "int64": np.uint64, "float16": np.uint16,
+                               "bfloat16": np.uint16, "float32": np.uint32,
+                               "float64": np.uint64}[dtype])
+
+
+def _int_sum(xs, bits):
+    """Elementwise sum with Python integers, wrapped to a signed `bits`-bit value."""
+    n = len(xs[0])
+    out = []
+    for i in range(n):
+        s = sum(int(x[i]) for x in xs) % (1 << bits)
+        out.append(s - (1 << bits) if s >= 1 << (bits - 1) else s)
+    return np.array(out, dtype=np.int32 if bits == 32 else np.int64)
+
+
+@SETTINGS
+@given(case, st.sampled_from(["sum", "max", "avg"]))
+def test_simulator_equals_closed_form(c, op):
+    p, n, dtype, seed = c
+    if op == "avg" and dtype in INTS:
+        op = "sum"
+    xs = _inputs(p, n, dtype, seed)
+    final, after_rs, _ = oracle.ring_allreduce(xs, dtype, op=op)
+    want = oracle.ring_fold(xs, dtype, op=op)
+    for r in range(p):
+        assert np.array_equal(_bits(final[r], dtype), _bits(want, dtype)), r
+    bounds = oracle.chunk_bounds(n, p)
+    for r in range(p):
+        lo, hi = bounds[oracle.owned_chunk(r, p)]
+        assert np.array_equal(_bits(after_rs[r][lo:hi], dtype), _bits(want[lo:hi], dtype)), r
+
+
+@SETTINGS
+@given(case, st.data())
+def test_integer_sums_by_every_algorithm_are_exact(c, data):
+    p, n, _, seed = c
+    dtype = data.draw(st.sampled_from(sorted(INTS)))
+    xs = _inputs(p, n, dtype, seed)
+    want = _int_sum(xs, INTS[dtype])
+    g = data.draw(st.sampled_from([d for d in range(1, p + 1) if p % d == 0]))
+    results = {
+        "ring": oracle.ring_fold(xs, dtype),
+        "mirrored": oracle.ring_fold(xs, dtype, direction=-1),
+        "bidir": oracle.bidir_allreduce(xs, dtype)[0][0],
+        "tree": oracle.tree_allreduce(xs, dtype)[0][0],
+        "hier": oracle.hier_fold(xs, dtype, g),
+        "hier_sim": oracle.hier_allreduce(xs, dtype, g)[0][0],
+    }
+    for name, got in results.items():
+        assert np.array_equal(np.asarray(got), want), name
+
+
+@SETTINGS
+@given(case, st.data())
+def test_maxima_by_every_algorithm_are_exact(c, data):
+    p, n, dtype, seed = c
+    xs = _inputs(p, n, dtype, seed)
+    if dtype == "bfloat16":
+        vals = [oracle.bf16_bits_to_f32(x) for x in xs]
+    else:
+        vals = [np.asarray(x) for x in xs]
+    want_vals = np.maximum.reduce(vals) if n else np.array([], dtype=vals[0].dtype)
+    g = data.draw(st.sampled_from([d for d in range(1, p + 1) if p % d == 0]))
+    results = {
+        "ring": oracle.ring_fold(xs, dtype, op="max"),
+        "bidir": oracle.bidir_allreduce(xs, dtype, op="max")[0][0],
+        "tree": oracle.tree_allreduce(xs, dtype, op="max")[0][0],
+        "hier": oracle.hier_fold(xs, dtype, g, op="max"),
+    }
+    for name, got in results.items():
+        got_vals = oracle.bf16_bits_to_f32(got) if dtype == "bfloat16" else np.asarray(got)
+        assert np.array_equal(got_vals, want_vals), name
+
+
+@SETTINGS
+@given(st.integers(0, 10**12), st.integers(1, 64))
+def test_chunk_partition(n, p):
+    bounds = oracle.chunk_bounds(n, p)
+    assert len(bounds) == p and bounds[0][0] == 0 and bounds[-1][1] == n
+    assert all(bounds[i][1] == bounds[i + 1][0] for i in range(p - 1))
+    sizes = [b - a for a, b in bounds]
+    assert max(sizes) - min(sizes) <= 1
+    assert sizes == sorted(sizes, reverse=True)
+    assert sum(1 for s in sizes if s == n // p + 1) == (n % p if n % p else 0)
