@@ -420,7 +420,7 @@ def alpha_measure(torch, B, inputs):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: --gpus {args.gpus} is not supported: this build runs the ring "
+        print(f"bench.py: --gpus {args.gpus} is not supported: the library runs the ring "
               "schedule's p virtual ranks inside ONE GPU's HBM; nothing crosses GPUs, so "
               "only --gpus 1 is measured.", file=sys.stderr)
         sys.exit(2)

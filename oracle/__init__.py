@@ -3,7 +3,8 @@
 This package is a plain, slow, obviously-correct restatement of what the ring
 all-reduce computes, written with numpy from the pages' descriptions.  It is the
 parity reference for the HIP path and nothing else: only the test-suite, the
-graft smoke check and the CPU-baseline leg of ``bench.py`` may import it.  The
+smoke check in ``__graft_entry__.py`` and the CPU-baseline leg of ``bench.py``
+may import it.  The
 product path (the C-ABI library and its Python binding) never imports, links or
 calls anything in here, and this package imports nothing from the product.
 
