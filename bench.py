@@ -197,6 +197,39 @@ def hier_group(p):
     return max([g for g in range(1, min(8, p - 1) + 1) if p % g == 0] or [1])
 
 
+def own_bytes(algo, p, S):
+    """HBM bytes an all-reduce algorithm moves on p buffers of S bytes each.
+
+    The fused passes read every buffer once and write it once: 2pS.  Every
+    step-by-step algorithm moves 5(p-1)S:
+    * ring (and its pipelined, channel and bidirectional forms): each
+      reduce-scatter step reads two copies of a chunk and writes one, 3S over
+      all ranks, and each all-gather step reads one and writes one, 2S;
+      (p-1) steps of each;
+    * binomial tree: p-1 pairwise adds of whole buffers (read 2S, write S) and
+      p-1 whole-buffer copies (read S, write S);
+    * two-level ring with g ranks per node and m = p/g nodes: 3(g-1)mS in the
+      in-node reduce-scatter, 5(m-1)S in the g cross-node rings over S/g-byte
+      shards, 2(g-1)mS in the in-node all-gather, which add up to 5(p-1)S."""
+    if algo in ("fused", "hier_fused"):
+        return 2 * p * S
+    return 5 * (p - 1) * S
+
+
+def phase_bytes(call, algo, p, S):
+    """(byte floor, bytes moved) of a standalone reduce-scatter or all-gather.
+
+    The floors: (p+1)S for a reduce-scatter (every rank read, one owned chunk
+    per rank written) and pS for an all-gather (every owned chunk read once,
+    written p-1 times); the fused passes move exactly that.  The step-by-step
+    phases move 3(p-1)S (p-1 steps that read two copies of each chunk and write
+    one) and 2(p-1)S (p-1 steps that read one and write one)."""
+    floor = (p + 1) * S if call == "reduce_scatter" else p * S
+    if algo == "fused":
+        return floor, floor
+    return floor, (3 if call == "reduce_scatter" else 2) * (p - 1) * S
+
+
 def cpu_baseline_workloads(inputs):
     """The oracle (lock-step ring simulator, numpy, one thread) timed in full on
     every workload the host holds comfortably: the worked trace, the 1e6-element
@@ -283,14 +316,11 @@ def per_workload(torch, B, inputs):
 
 def phase_measure(bufs, S, p, torch, B):
     """Standalone reduce-scatter and all-gather on the workload's buffers, each
-    rated on its own byte floor: (p+1)S for the fused reduce-scatter (every rank
-    read, one owned chunk per rank written) and pS for the fused all-gather
-    (every owned chunk read once, written p-1 times)."""
+    rated on its own byte floor and on the bytes it moves (phase_bytes)."""
     out = {}
-    for call, algo, floor in (("reduce_scatter", "fused", (p + 1) * S),
-                              ("all_gather", "fused", p * S),
-                              ("reduce_scatter", "ring_step", (p + 1) * S),
-                              ("all_gather", "ring_step", p * S)):
+    for call, algo in (("reduce_scatter", "fused"), ("all_gather", "fused"),
+                       ("reduce_scatter", "ring_step"), ("all_gather", "ring_step")):
+        floor, moved = phase_bytes(call, algo, p, S)
         f = B.ra_reduce_scatter_ex if call == "reduce_scatter" else B.ra_all_gather_ex
         fn = lambda f=f, a=algo: f(bufs, algo=a)
         fn()
@@ -300,7 +330,9 @@ def phase_measure(bufs, S, p, torch, B):
         t = sum(per) / len(per)
         out[f"{call}_{algo}"] = {"ms": round(t, 3), "bytes_floor": floor,
                                  "GBps_on_floor": round(floor / (t * 1e-3) / 1e9, 1),
-                                 "pct_peak": round(100 * floor / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}
+                                 "pct_peak": round(100 * floor / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                                 "hbm_bytes": moved,
+                                 "GBps_on_hbm_bytes": round(moved / (t * 1e-3) / 1e9, 1)}
     return out
 
 
@@ -534,7 +566,12 @@ def main():
             vper, _ = time_calls(fn, 3, torch)
             B.ra_stream_status()
             t = sum(vper) / len(vper)
-            variants[name] = {"ms": round(t, 3), "GBps_on_2pS": round(min_bytes / (t * 1e-3) / 1e9, 1)}
+            moved = own_bytes(algo, p, S)
+            variants[name] = {"ms": round(t, 3), "GBps_on_2pS": round(min_bytes / (t * 1e-3) / 1e9, 1),
+                              "hbm_bytes": moved,
+                              "GBps_on_hbm_bytes": round(moved / (t * 1e-3) / 1e9, 1),
+                              "pct_peak_on_hbm_bytes": round(100 * moved / (t * 1e-3) / 1e9
+                                                             / HBM_PEAK_GBPS, 2)}
             if "group" in kw:
                 variants[name]["group"] = kw["group"]
         result["variants"] = variants
