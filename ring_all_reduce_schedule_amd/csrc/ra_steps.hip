@@ -158,7 +158,15 @@ __device__ __forceinline__ void stage_step(void* src, void* dst, int64_t v0, int
   if (n0 < n1) {
     stage_fill<ADD, NT>(reinterpret_cast<const u32x4*>(src), reinterpret_cast<const u32x4*>(dst),
                         n0, n1, nxt_src, nxt_dst);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));       // the current stage has landed
+    // The current stage has landed once no more than the next stage's copies are
+    // outstanding -- but only if this wave issued all kLoads of them.  A short
+    // next stage (the slice's last) leaves some waves with fewer or none, and
+    // the counter also holds the previous stage's stores, which may complete
+    // before the current stage's copies; there, wait for everything.
+    if (n1 - n0 == kStageV)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   } else {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   }
