@@ -291,7 +291,8 @@ def per_workload(torch, B, inputs):
         del src, dst
         ranks = B.RankBuffers(bufs)
         rec["hier_group"] = hier_group(p)
-        for algo in ("fused", "ring_step", "ring_channels", "tree", "hier", "hier_fused"):
+        for algo in ("fused", "ring_step", "ring_pipelined", "ring_bidir", "ring_channels", "tree",
+                     "hier", "hier_fused"):
             kw = {"group": hier_group(p)} if algo.startswith("hier") else {}
             fn = lambda a=algo, k=kw: B.ra_allreduce_ex(ranks, algo=a, **k)
             fn()
@@ -305,7 +306,8 @@ def per_workload(torch, B, inputs):
                          "pct_peak_cold": round(100 * two_ps / (tc * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
                          "pct_of_copy_cold": round(100 * rec["copy"]["ms_cold"] / tc, 1),
                          "ms_warm": round(tw, 4), "GBps_warm": round(two_ps / (tw * 1e-3) / 1e9, 1),
-                         "pct_of_copy_warm": round(100 * rec["copy"]["ms_warm"] / tw, 1)}
+                         "pct_of_copy_warm": round(100 * rec["copy"]["ms_warm"] / tw, 1),
+                         "hbm_bytes": own_bytes(algo, p, S)}
         out[name] = rec
         del bufs, ranks
         torch.cuda.empty_cache()
