@@ -49,7 +49,7 @@ from .arith import (DTYPES, STORAGE, add_rounded, bf16_bits_to_f32,
 from .ring import (RingTimeout, reduce_scatter, all_gather, ring_allreduce)
 from .fold import ring_fold, ring_fold_window, rs_partial, rs_owned
 from .tree import tree_allreduce
-from .bidir import bidir_allreduce, bidir_halves
+from .bidir import bidir_allreduce, bidir_halves, bidir_fold_window
 from .hier import hier_allreduce, hier_fold, hier_fold_window, hier_layout
 from .exact import exact_sum, normwise_error
 from . import cost
@@ -60,5 +60,5 @@ __all__ = [
     "bf16_bits_to_f32", "f32_to_bf16_bits", "as_values", "RingTimeout",
     "reduce_scatter", "all_gather", "ring_allreduce", "ring_fold",
     "ring_fold_window", "rs_partial", "rs_owned", "tree_allreduce", "bidir_allreduce",
-    "bidir_halves", "hier_allreduce", "hier_fold", "hier_fold_window", "hier_layout", "exact_sum", "normwise_error", "cost",
+    "bidir_halves", "bidir_fold_window", "hier_allreduce", "hier_fold", "hier_fold_window", "hier_layout", "exact_sum", "normwise_error", "cost",
 ]

@@ -11,6 +11,7 @@ an ordinary ring all-reduce with its own p chunks.
 
 import numpy as np
 
+from .fold import ring_fold_window
 from .ring import ring_allreduce
 from .schedule import chunk_bounds
 
@@ -30,3 +31,28 @@ def bidir_allreduce(bufs, dtype, op="sum"):
     final = [np.concatenate([fwd[r], rev[r]]) for r in range(p)]
     after_rs = [np.concatenate([fwd_rs[r], rev_rs[r]]) for r in range(p)]
     return final, after_rs
+
+
+def bidir_fold_window(windows, lo, n, dtype, op="sum"):
+    """The bidirectional result for elements [lo, lo + len(window)) of n-element
+    buffers: the part of the window in the forward half folds in the forward
+    ring's order over that half's chunks, the part in the mirrored half in the
+    mirrored ring's order over its chunks.  ``windows[r]`` holds rank r's
+    elements of the window, which may straddle the two halves."""
+    w = len(windows[0])
+    hi = lo + w
+    if not 0 <= lo <= hi <= n:
+        raise ValueError("window outside the buffer")
+    (a0, a1), (b0, b1) = bidir_halves(n)
+    parts = []
+    if lo < a1:
+        s, e = lo, min(hi, a1)
+        parts.append(ring_fold_window([np.asarray(x)[s - lo:e - lo] for x in windows], s - a0,
+                                      a1 - a0, dtype, 1, op=op))
+    if hi > b0:
+        s, e = max(lo, b0), hi
+        parts.append(ring_fold_window([np.asarray(x)[s - lo:e - lo] for x in windows], s - b0,
+                                      b1 - b0, dtype, -1, op=op))
+    if not parts:
+        return np.empty_like(np.asarray(windows[0]))
+    return np.concatenate(parts)

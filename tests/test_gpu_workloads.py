@@ -93,7 +93,8 @@ def _windows(n, p, seed):
     return sorted(set((max(0, a), min(n, b)) for a, b in wins))
 
 
-@pytest.mark.parametrize("algo", ["fused", "hier_fused", "ring_step", "tree"])
+@pytest.mark.parametrize("algo", ["fused", "hier_fused", "ring_step", "tree", "ring_bidir",
+                                  "ring_channels", "ring_pipelined", "hier"])
 def test_p8_bf16_16GB_windowed(algo):
     dev = require_gpu()
     w = inputs.WORKLOADS["p8_bf16_16GB"]
@@ -107,14 +108,18 @@ def test_p8_bf16_16GB_windowed(algo):
     wins = _windows(n, p, w["seed"])
     before = [[x[a:b].view(torch.int16).cpu().numpy().view(np.uint16) for x in t] for a, b in wins]
     torch.cuda.synchronize()
-    print(f"[case] workload=p8_bf16_16GB algo={algo}: running", flush=True)
-    B.ra_allreduce_ex(t, algo=algo)
+    # the hierarchical algorithms as two nodes of four ranks
+    opts = {"group": 4} if algo.startswith("hier") else {}
+    print(f"[case] workload=p8_bf16_16GB algo={algo} {opts}: running", flush=True)
+    B.ra_allreduce_ex(t, algo=algo, **opts)
     B.ra_stream_status()
     for r in range(1, p):
         assert torch.equal(t[0].view(torch.int16), t[r].view(torch.int16)), f"rank {r} != rank 0"
     for (a, b), xw in zip(wins, before):
-        if algo == "hier_fused":
-            want = oracle.hier_fold_window(xw, a, n, "bfloat16", _group(p))
+        if algo in ("hier_fused", "hier"):
+            want = oracle.hier_fold_window(xw, a, n, "bfloat16", 4)
+        elif algo == "ring_bidir":
+            want = oracle.bidir_fold_window(xw, a, n, "bfloat16")
         elif algo == "tree":
             # the tree's order is the same for every element: fold whole windows
             want = oracle.tree_allreduce(xw, "bfloat16")[0][0]

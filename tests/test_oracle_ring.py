@@ -216,12 +216,13 @@ def test_rs_owned_int32_brute_force():
         assert np.array_equal(oracle.rs_owned(xs, "int32", r)[lo:hi], total[lo:hi])
 
 
-def test_fold_window_matches_whole():
+@pytest.mark.parametrize("direction", [1, -1])
+def test_fold_window_matches_whole(direction):
     p, n = 9, 1003
     xs = inputs.make_inputs(p, n, "bfloat16", seed=9)
-    whole = oracle.ring_fold(xs, "bfloat16")
+    whole = oracle.ring_fold(xs, "bfloat16", direction=direction)
     for lo, hi in [(0, 5), (100, 300), (110, 115), (998, 1003), (0, 1003)]:
-        got = oracle.ring_fold_window([x[lo:hi] for x in xs], lo, n, "bfloat16")
+        got = oracle.ring_fold_window([x[lo:hi] for x in xs], lo, n, "bfloat16", direction)
         assert np.array_equal(got, whole[lo:hi])
 
 

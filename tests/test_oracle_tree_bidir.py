@@ -94,3 +94,19 @@ def test_bidir_mirrored_half_order_by_hand():
     final, _ = oracle.bidir_allreduce(xs, "float32")
     want = np.array([1 - e, 1 + 2 * e, 1, 1, 1, 1 + 2 * e], np.float32)
     assert all(np.array_equal(f, want) for f in final)
+
+
+@pytest.mark.parametrize("dtype", ["bfloat16", "float32", "int32"])
+@pytest.mark.parametrize("p,n", [(3, 101), (8, 1003), (9, 64), (5, 7)])
+def test_bidir_fold_window_matches_whole(dtype, p, n):
+    # windows of the bidirectional result, including ones that straddle the
+    # boundary between the two halves and the chunk edges of either half, equal
+    # the same elements of the lock-step simulation of both rings
+    xs = inputs.make_inputs(p, n, dtype, seed=p + n, sigma=2.0)
+    whole = oracle.bidir_allreduce(xs, dtype)[0][0]
+    mid = oracle.bidir_halves(n)[1][0]
+    wins = [(0, n), (0, 1), (n - 1, n), (max(0, mid - 3), min(n, mid + 4)), (mid, n), (0, mid),
+            (n // 3, 2 * n // 3)]
+    for lo, hi in wins:
+        got = oracle.bidir_fold_window([x[lo:hi] for x in xs], lo, n, dtype)
+        assert np.array_equal(np.asarray(got), np.asarray(whole[lo:hi])), (lo, hi)
