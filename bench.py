@@ -346,9 +346,11 @@ def alpha_measure(torch, B, inputs):
         launch (one workgroup at this size), for 8 channels, and for 64
         workgroups on the device-wide barrier.
     (2) fit: T(S) = 2(p-1) a + 2(p-1)/p * S / B over S from 1 KiB to 64 MiB per
-        rank, p = 2 .. 64 (bf16), least squares per p; the tree under the same
-        model (2 ceil(log2 p) steps of a + S / B) and the fused pass (a + 2pS/BW);
-        the ring/tree crossover measured and from the fitted model.
+        rank, p = 2 .. 64 (bf16), least squares per p, for the step-by-step,
+        pipelined and channel rings; the tree under the same model (2 ceil(log2 p)
+        steps of a + S / B) and the fused pass (a + 2pS/BW); the ring/tree
+        crossover measured and from the fitted model; the sizes at which the
+        pipelined ring beats the step-by-step one.
     """
     import numpy as np
     hz = B.ra_wallclock_hz()
@@ -393,7 +395,7 @@ def alpha_measure(torch, B, inputs):
         spans.append(span / 64)
     out["launch_per_step_us"] = round(float(np.median(spans)) * 1e3, 3)
     fits = {}
-    algos = ("ring_step", "ring_channels", "tree", "fused")
+    algos = ("ring_step", "ring_pipelined", "ring_channels", "tree", "fused")
     sizes = [1 << 10, 4 << 10, 16 << 10, 64 << 10, 256 << 10, 1 << 20, 4 << 20, 16 << 20,
              64 << 20]
     for p in (2, 4, 8, 9, 16, 32, 64):
@@ -413,7 +415,7 @@ def alpha_measure(torch, B, inputs):
         S = np.array([r["S_per_rank"] for r in rows], dtype=np.float64)
         # ring: T = 2(p-1) a + 2(p-1)/p * S / B ([Derive] Where it stops scaling)
         A = np.stack([np.full(len(S), 2.0 * (p - 1)), 2 * (p - 1) / p * S], axis=1)
-        for algo in ("ring_step", "ring_channels"):
+        for algo in ("ring_step", "ring_pipelined", "ring_channels"):
             y = np.array([r[f"{algo}_ms"] * 1e-3 for r in rows])
             (a, inv_b), *_ = np.linalg.lstsq(A, y, rcond=None)
             rec[algo] = {"alpha_us": round(a * 1e6, 3),
@@ -437,6 +439,10 @@ def alpha_measure(torch, B, inputs):
             if r["tree_ms"] < r["ring_step_ms"]:
                 cross = r["S_per_rank"]
         rec["largest_S_per_rank_where_tree_beats_ring"] = cross
+        # where slicing the chunks pays ([InDepth] What real libraries add,
+        # pipelining): sizes at which the pipelined ring beats one launch per step
+        rec["S_per_rank_where_pipelined_beats_ring_step"] = [
+            r["S_per_rank"] for r in rows if r["ring_pipelined_ms"] < r["ring_step_ms"]]
         a_r = rec["ring_step"]["alpha_us"] * 1e-6
         b_r = (rec["ring_step"]["B_GBps_per_rank"] or 0) * 1e9
         lat, bw = 2.0 * (p - 1) - 2.0 * levels, 2.0 * levels - 2.0 * (p - 1) / p
