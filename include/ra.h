@@ -133,8 +133,9 @@ typedef enum ra_algo {
 
 typedef struct ra_options {
   int64_t slice_elems;  /* RING_PIPELINED slice length in elements; 0 = library default
-                           (about four slices per worker per hop, at least 64 KiB).
-                           Rounded up to a multiple of 16 bytes. */
+                           (about four slices per worker per hop, at least 64 KiB, but
+                           at least eight slices per chunk when they can be 16 KiB or
+                           more).  Rounded up to a multiple of 16 bytes. */
   int64_t timeout_us;   /* budget of any single device-side wait; 0 = 10 s */
   int32_t grid;         /* step algorithms (RING_STEP, RING_BIDIR, TREE, HIER): 0 = the
                            library chooses (see RA_ALGO_RING_STEP).  1 with steps of at
