@@ -11,9 +11,14 @@ makes per call, so that every code path meets odd combinations:
   and slice lengths drawn at random where they apply;
 * reduce-scatter followed by all-gather with independently drawn algorithms.
 
+A second list of 40 cases draws n from 100 000 to 3 000 000 elements, where
+the launch shapes that only large buffers get (two vectors per thread for copy
+steps, eight or more pipelined slices per chunk, whole-buffer tree launches)
+come into play.
+
 Each result must equal the oracle's result for that algorithm's order bit for
-bit.  The list is generated from one seed, so a failure names a reproducible
-case.
+bit.  The lists are generated from fixed seeds, so a failure names a
+reproducible case.
 """
 
 import random
@@ -99,3 +104,31 @@ def test_random_case(case):
     B.ra_stream_status()
     for r, g in enumerate(from_dev(t, dtype)):
         assert same_bits(g, want, dtype), f"rank {r} first diff {first_diff(g, want, dtype)}"
+
+
+# Larger buffers (up to a few million elements), where copy steps take two
+# vectors per thread, pipelined chunks are cut into eight or more slices with
+# workers in multiples of 8, and whole-buffer tree steps run as large launches.
+def _large_cases(count=40, seed=20261203):
+    rng = random.Random(seed)
+    out = []
+    for i in range(count):
+        p = rng.choice([2, 3, 4, 8, 9, 16])
+        n = rng.randrange(100_000, 3_000_000)
+        dtype = rng.choice(DTYPES)
+        op = rng.choice(["sum", "max", "avg"] if dtype in FLOATS else ["sum", "max"])
+        algo = rng.choice(["ring_step", "ring_pipelined", "ring_bidir", "tree", "hier", "auto"])
+        opts = {}
+        if algo == "ring_pipelined" and rng.random() < 0.5:
+            opts["slice_elems"] = rng.choice([1024, 4096, 65536])
+        if algo == "ring_pipelined" and rng.random() < 0.3:
+            opts["grid"] = rng.choice([64, 200, 512])
+        if algo == "hier":
+            opts["group"] = rng.choice(_divisors(p))
+        out.append(("allreduce", 1000 + i, p, n, dtype, op, algo, None, opts))
+    return out
+
+
+@pytest.mark.parametrize("case", _large_cases(), ids=lambda c: f"large{c[1]}")
+def test_random_large_case(case):
+    test_random_case(case)
