@@ -1,6 +1,6 @@
 """GPU parity on seeded random cases (through the C ABI).
 
-A fixed list of 300 pseudo-random configurations spans the choices the library
+A fixed list of 1000 pseudo-random configurations spans the choices the library
 makes per call, so that every code path meets odd combinations:
 
 * p from 2 to 64, n from 0 to about 60 000 (below, at and above the size where
@@ -11,7 +11,7 @@ makes per call, so that every code path meets odd combinations:
   and slice lengths drawn at random where they apply;
 * reduce-scatter followed by all-gather with independently drawn algorithms.
 
-A second list of 40 cases draws n from 100 000 to 3 000 000 elements, where
+A second list of 60 cases draws n from 100 000 to 3 000 000 elements, where
 the launch shapes that only large buffers get (two vectors per thread for copy
 steps, eight or more pipelined slices per chunk, whole-buffer tree launches)
 come into play.
@@ -44,7 +44,7 @@ def _divisors(p):
     return [g for g in range(1, p + 1) if p % g == 0]
 
 
-def _cases(count=300, seed=20261202):
+def _cases(count=1000, seed=20261202):
     rng = random.Random(seed)
     out = []
     for i in range(count):
@@ -109,7 +109,7 @@ def test_random_case(case):
 # Larger buffers (up to a few million elements), where copy steps take two
 # vectors per thread, pipelined chunks are cut into eight or more slices with
 # workers in multiples of 8, and whole-buffer tree steps run as large launches.
-def _large_cases(count=40, seed=20261203):
+def _large_cases(count=60, seed=20261203):
     rng = random.Random(seed)
     out = []
     for i in range(count):
