@@ -448,9 +448,11 @@ def alpha_measure(torch, B, inputs):
         lat, bw = 2.0 * (p - 1) - 2.0 * levels, 2.0 * levels - 2.0 * (p - 1) / p
         rec["model_crossover_S_per_rank"] = (round(b_r * a_r * lat / bw)
                                              if lat > 0 and bw > 0 and b_r > 0 and a_r > 0 else None)
-        # within 3%: at the launch floor (one ~6 us launch each) ties go either way
+        # within 3% and 2 us: at the launch floor (one ~6 us launch each) ties go
+        # either way from run to run
         rec["fused_fastest_at_every_size"] = all(
-            r["fused_ms"] <= 1.03 * min(r[f"{a}_ms"] for a in algos if a != "fused") for r in rows)
+            r["fused_ms"] <= 1.03 * min(r[f"{a}_ms"] for a in algos if a != "fused") + 0.002
+            for r in rows)
         fits[f"p{p}"] = rec
     out["fit"] = fits
     torch.cuda.empty_cache()
