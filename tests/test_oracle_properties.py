@@ -27,7 +27,7 @@ from ring_all_reduce_schedule_amd import inputs  # noqa: E402
 
 DTYPES = ["int32", "int64", "float16", "bfloat16", "float32", "float64"]
 INTS = {"int32": 32, "int64": 64}
-SETTINGS = settings(max_examples=60, deadline=None, derandomize=True)
+SETTINGS = settings(max_examples=300, deadline=None, derandomize=True)
 
 case = st.tuples(st.integers(1, 12), st.integers(0, 200), st.sampled_from(DTYPES),
                  st.integers(0, 2**31 - 1))
