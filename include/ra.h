@@ -142,8 +142,10 @@ typedef struct ra_options {
                            most 256 vectors: the single workgroup.  Otherwise a value
                            above 0 runs one persistent grid of that many workgroups (at
                            most as many as fit the GPU) with a device-wide barrier
-                           between steps.  RING_PIPELINED, RING_CHANNELS: workgroups of
-                           their persistent grid; 0 = as many as fit the GPU. */
+                           between steps.  RING_PIPELINED, RING_CHANNELS: an upper bound
+                           on the workgroups of their persistent grid (the pipelined ring
+                           uses the same number per rank, rounded down to a multiple of 8
+                           when 8 or more fit); 0 = as many as fit the GPU. */
   uint32_t flags;       /* RA_FLAG_* */
   uint64_t* step_ts;    /* optional DEVICE array of (steps + 1) uint64: device wall-clock
                            ticks at kernel start and as each step's barrier releases
