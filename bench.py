@@ -10,16 +10,21 @@ workload is p8_bf16_16GB: 8 virtual ranks x 8e9 bf16 elements (16 GB per rank,
 bandwidth on the least traffic any one-GPU all-reduce needs, 2*p*S bytes (every
 rank buffer read once and written once), against the 8 TB/s HBM3E peak.
 
-Prints ONE JSON line.  Besides the driver's fields it carries
+Prints ONE short JSON line on stdout, last (at most 4 KB: a reader that keeps
+only the tail of stdout still gets it whole).  Besides the driver's fields it
+carries
   roofline      the all-reduce kernel's achieved bytes/s vs the HBM peak, its
                 launch duration from HIP events on the launch stream, and the
                 HBM traffic read from the committed rocprofv3 counter summary
                 (null when that summary was taken on different kernel source)
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
-  variants      the other algorithms on the same buffers
-  alpha         per-step latency of the step-by-step ring, from in-kernel
-                timestamps and from a fit of T = 2(p-1)a + 2(p-1)/p*S/B
-  ceiling       a plain copy of the same byte count (read + write)
+  algos_ms      every other algorithm's time on the same buffers
+  alpha_us      per-step latency of the step-by-step ring (in-kernel timestamps)
+  crossover_S_per_rank  per rank count: the largest per-rank size at which the
+                tree beat the ring, and the pages' model crossover
+  copy_ceiling_GBps  a plain copy of the same byte count (read + write)
+The full record (per-workload rates, the alpha fits, the standalone phases)
+goes to the --detail file (default gpurun_out/bench_detail.json).
 
 Buffers are all-reduced in place, so values grow by about p per call; the
 default step counts stay far from bf16 overflow and inputs are redrawn before
@@ -68,6 +73,8 @@ def parse_args():
                     help="elements per rank of the CPU-oracle sample")
     ap.add_argument("--mode", default="allreduce", choices=["allreduce", "copy"],
                     help="copy: only the plain copy kernel, for counter calibration")
+    ap.add_argument("--detail", default=os.path.join(ROOT, "gpurun_out", "bench_detail.json"),
+                    help="file for the full measurement record ('' = none)")
     return ap.parse_args()
 
 
@@ -448,15 +455,62 @@ def alpha_measure(torch, B, inputs):
         lat, bw = 2.0 * (p - 1) - 2.0 * levels, 2.0 * levels - 2.0 * (p - 1) / p
         rec["model_crossover_S_per_rank"] = (round(b_r * a_r * lat / bw)
                                              if lat > 0 and bw > 0 and b_r > 0 and a_r > 0 else None)
-        # within 3% and 2 us: at the launch floor (one ~6 us launch each) ties go
-        # either way from run to run
-        rec["fused_fastest_at_every_size"] = all(
-            r["fused_ms"] <= 1.03 * min(r[f"{a}_ms"] for a in algos if a != "fused") + 0.002
-            for r in rows)
+        # every size at which another algorithm's median beat the fused pass
+        rec["not_fused_fastest"] = []
+        for r in rows:
+            best = min((r[f"{a}_ms"], a) for a in algos)
+            if best[1] != "fused":
+                rec["not_fused_fastest"].append(
+                    [p, r["S_per_rank"], best[1], best[0], r["fused_ms"]])
         fits[f"p{p}"] = rec
     out["fit"] = fits
     torch.cuda.empty_cache()
     return out
+
+
+# Keys of the final stdout line, which must stay short (a reader that keeps only
+# the tail of stdout must still get it whole); everything else goes to the
+# detail file.
+SUMMARY_KEYS = ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "pct_of_hbm_peak", "busbw_emulated_GBps", "roofline", "cpu_baseline",
+                "pct_of_copy_ceiling", "alpha_us", "detail_file")
+SUMMARY_MAX_CHARS = 4096
+
+
+def summary_line(result):
+    """The one-line record printed last: the headline, its roofline and CPU
+    baseline, the copy ceiling, the step latency, every algorithm's time on the
+    headline workload and, per rank count, the ring/tree crossover (measured
+    and from the pages' model)."""
+    out = {k: result[k] for k in SUMMARY_KEYS if k in result}
+    if "ceiling" in result:
+        out["copy_ceiling_GBps"] = result["ceiling"].get("GBps")
+    if "variants" in result:
+        out["algos_ms"] = {k: v["ms"] for k, v in result["variants"].items()}
+    fit = result.get("alpha", {}).get("fit")
+    if fit:
+        out["crossover_S_per_rank"] = {
+            p: [rec.get("largest_S_per_rank_where_tree_beats_ring"),
+                rec.get("model_crossover_S_per_rank")] for p, rec in fit.items()}
+        out["fused_not_fastest"] = [x for rec in fit.values() for x in rec.get("not_fused_fastest", [])]
+    line = json.dumps(out)
+    if len(line) > SUMMARY_MAX_CHARS:
+        # never let the headline grow past what a tail reader keeps
+        for k in ("fused_not_fastest", "crossover_S_per_rank", "algos_ms"):
+            out.pop(k, None)
+            if len(json.dumps(out)) <= SUMMARY_MAX_CHARS:
+                break
+    return out
+
+
+def write_detail(path, result):
+    if not path:
+        return
+    os.makedirs(os.path.dirname(path) or ".", exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(result, f, indent=1)
+    log(f"full record in {path}")
 
 
 def main():
@@ -617,7 +671,10 @@ def main():
         result["alpha"] = alpha_measure(torch, B, inputs)
         result["alpha_us"] = result["alpha"]["in_kernel_step_us_p64_1KiB"]
 
-    print(json.dumps(result), flush=True)
+    # everything measured goes to the detail file; stdout ends with the short line
+    write_detail(args.detail, result)
+    result["detail_file"] = os.path.relpath(args.detail, ROOT) if args.detail else None
+    print(json.dumps(summary_line(result)), flush=True)
 
 
 if __name__ == "__main__":
