@@ -207,9 +207,12 @@ def hier_group(p):
 def own_bytes(algo, p, S):
     """HBM bytes an all-reduce algorithm moves on p buffers of S bytes each.
 
-    The fused passes read every buffer once and write it once: 2pS.  Every
-    step-by-step algorithm moves 5(p-1)S:
-    * ring (and its pipelined, channel and bidirectional forms): each
+    The fused passes read every buffer once and write it once: 2pS.  The
+    slice-carrying pipelined ring reads every buffer once and writes each
+    element position 2(p-1) times (the p-1 receivers' partials, then the
+    all-gather's p-1 copies): (3p-2)S.  Every step-by-step algorithm moves
+    5(p-1)S:
+    * ring (and its flag-driven pipelined, channel and bidirectional forms): each
       reduce-scatter step reads two copies of a chunk and writes one, 3S over
       all ranks, and each all-gather step reads one and writes one, 2S;
       (p-1) steps of each;
@@ -220,6 +223,8 @@ def own_bytes(algo, p, S):
       shards, 2(g-1)mS in the in-node all-gather, which add up to 5(p-1)S."""
     if algo in ("fused", "hier_fused"):
         return 2 * p * S
+    if algo == "ring_pipelined":
+        return (3 * p - 2) * S
     return 5 * (p - 1) * S
 
 
@@ -228,12 +233,17 @@ def phase_bytes(call, algo, p, S):
 
     The floors: (p+1)S for a reduce-scatter (every rank read, one owned chunk
     per rank written) and pS for an all-gather (every owned chunk read once,
-    written p-1 times); the fused passes move exactly that.  The step-by-step
-    phases move 3(p-1)S (p-1 steps that read two copies of each chunk and write
-    one) and 2(p-1)S (p-1 steps that read one and write one)."""
+    written p-1 times); the fused passes move exactly that.  The slice-carrying
+    pipelined ring's reduce-scatter reads every rank once and writes the p-1
+    receivers' partials of every chunk, (2p-1)S; its all-gather is the floor.
+    The step-by-step phases move 3(p-1)S (p-1 steps that read two copies of
+    each chunk and write one) and 2(p-1)S (p-1 steps that read one and write
+    one)."""
     floor = (p + 1) * S if call == "reduce_scatter" else p * S
     if algo == "fused":
         return floor, floor
+    if algo == "ring_pipelined":
+        return floor, (2 * p - 1) * S if call == "reduce_scatter" else floor
     return floor, (3 if call == "reduce_scatter" else 2) * (p - 1) * S
 
 
@@ -298,7 +308,8 @@ def per_workload(torch, B, inputs):
         del src, dst
         ranks = B.RankBuffers(bufs)
         rec["hier_group"] = hier_group(p)
-        for algo in ("fused", "ring_step", "ring_pipelined", "ring_bidir", "ring_channels", "tree",
+        for algo in ("fused", "ring_step", "ring_pipelined", "ring_pipelined_flags", "ring_bidir",
+                     "ring_channels", "tree",
                      "hier", "hier_fused"):
             kw = {"group": hier_group(p)} if algo.startswith("hier") else {}
             fn = lambda a=algo, k=kw: B.ra_allreduce_ex(ranks, algo=a, **k)
@@ -328,6 +339,7 @@ def phase_measure(bufs, S, p, torch, B):
     rated on its own byte floor and on the bytes it moves (phase_bytes)."""
     out = {}
     for call, algo in (("reduce_scatter", "fused"), ("all_gather", "fused"),
+                       ("reduce_scatter", "ring_pipelined"), ("all_gather", "ring_pipelined"),
                        ("reduce_scatter", "ring_step"), ("all_gather", "ring_step")):
         floor, moved = phase_bytes(call, algo, p, S)
         f = B.ra_reduce_scatter_ex if call == "reduce_scatter" else B.ra_all_gather_ex
@@ -402,7 +414,7 @@ def alpha_measure(torch, B, inputs):
         spans.append(span / 64)
     out["launch_per_step_us"] = round(float(np.median(spans)) * 1e3, 3)
     fits = {}
-    algos = ("ring_step", "ring_pipelined", "ring_channels", "tree", "fused")
+    algos = ("ring_step", "ring_pipelined", "ring_pipelined_flags", "ring_channels", "tree", "fused")
     sizes = [1 << 10, 4 << 10, 16 << 10, 64 << 10, 256 << 10, 1 << 20, 4 << 20, 16 << 20,
              64 << 20]
     for p in (2, 4, 8, 9, 16, 32, 64):
@@ -422,7 +434,7 @@ def alpha_measure(torch, B, inputs):
         S = np.array([r["S_per_rank"] for r in rows], dtype=np.float64)
         # ring: T = 2(p-1) a + 2(p-1)/p * S / B ([Derive] Where it stops scaling)
         A = np.stack([np.full(len(S), 2.0 * (p - 1)), 2 * (p - 1) / p * S], axis=1)
-        for algo in ("ring_step", "ring_pipelined", "ring_channels"):
+        for algo in ("ring_step", "ring_pipelined_flags", "ring_channels"):
             y = np.array([r[f"{algo}_ms"] * 1e-3 for r in rows])
             (a, inv_b), *_ = np.linalg.lstsq(A, y, rcond=None)
             rec[algo] = {"alpha_us": round(a * 1e6, 3),
@@ -447,9 +459,10 @@ def alpha_measure(torch, B, inputs):
                 cross = r["S_per_rank"]
         rec["largest_S_per_rank_where_tree_beats_ring"] = cross
         # where slicing the chunks pays ([InDepth] What real libraries add,
-        # pipelining): sizes at which the pipelined ring beats one launch per step
-        rec["S_per_rank_where_pipelined_beats_ring_step"] = [
-            r["S_per_rank"] for r in rows if r["ring_pipelined_ms"] < r["ring_step_ms"]]
+        # pipelining): sizes at which each pipelined ring beats one launch per step
+        for algo in ("ring_pipelined", "ring_pipelined_flags"):
+            rec[f"S_per_rank_where_{algo}_beats_ring_step"] = [
+                r["S_per_rank"] for r in rows if r[f"{algo}_ms"] < r["ring_step_ms"]]
         a_r = rec["ring_step"]["alpha_us"] * 1e-6
         b_r = (rec["ring_step"]["B_GBps_per_rank"] or 0) * 1e9
         lat, bw = 2.0 * (p - 1) - 2.0 * levels, 2.0 * levels - 2.0 * (p - 1) / p
@@ -617,7 +630,8 @@ def main():
         log("variants")
         fill_workload(args.workload, bufs, torch, inputs)
         variants = {}
-        runs = [(a, a, {}) for a in ("ring_step", "ring_pipelined", "ring_bidir", "ring_channels",
+        runs = [(a, a, {}) for a in ("ring_step", "ring_pipelined", "ring_pipelined_flags",
+                                     "ring_bidir", "ring_channels",
                                      "tree")]
         runs += [(a, a, {"group": hier_group(p)}) for a in ("hier", "hier_fused")]
         runs += [("fused_wide_fp32_accumulate", "fused", {"wide": True}),

@@ -42,19 +42,18 @@
  *  Concurrency: calls on different streams may overlap; calls on one stream
  *  are ordered by the stream.  The library keeps a small device workspace per
  *  (device, stream), allocated on first use and kept until process exit.  The
- *  pipelined and channel algorithms, and the step algorithms when
- *  ra_options.grid or step_ts is set, run persistent grids whose workgroups
- *  must all be resident at once; by default such a grid fills the GPU, so
- *  overlapping such calls should each set ra_options.grid to their share (a
- *  call that cannot get all its workgroups resident times out instead of
- *  hanging).  Persistent grids are cooperative launches, and a cooperative
- *  launch fails (RA_ERR_HIP, "cannot be performed in the present state") while
- *  another live process on the same GPU has made one; the default launches of
- *  every algorithm but the pipelined and channel ones are not cooperative.  The one-pass algorithms (FUSED, HIER_FUSED) and the step
- *  algorithms' default launches (one per step, or one workgroup) are ordinary
- *  grids with no device-side waits, and can be captured in a HIP graph; the
- *  pipelined algorithm cannot (its ready counters are numbered per call on the
- *  host).
+ *  flag-driven pipelined and channel algorithms, and the step algorithms when
+ *  ra_options.grid or step_ts is set, run persistent grids: ordinary launches
+ *  whose workgroups wait for each other, so all of them must be resident at
+ *  once.  Such a grid is sized to what the GPU can hold of it (by default 4
+ *  workgroups per compute unit), so overlapping such calls should each set
+ *  ra_options.grid to their share; a call that cannot get all its workgroups
+ *  resident times out (RA_ERR_TIMEOUT from ra_stream_status) instead of
+ *  hanging.  The one-pass algorithms (FUSED, HIER_FUSED), the pipelined ring
+ *  (RING_PIPELINED) and the step algorithms' default launches (one per step,
+ *  or one workgroup) are grids with no device-side waits, and can be captured
+ *  in a HIP graph; RING_PIPELINED_FLAGS cannot (its ready counters are
+ *  numbered per call on the host).
  *
  * Return codes are ra_status values; ra_status_string() names them and
  * ra_last_error() gives the calling thread's last error message.
@@ -101,7 +100,12 @@ typedef enum ra_algo {
                                  set, one persistent grid with a device-wide barrier between
                                  steps.  RING_BIDIR, TREE and HIER run their steps the same
                                  way. */
-  RA_ALGO_RING_PIPELINED = 1, /* chunks cut into slices; per-slice ready flags instead of barriers */
+  RA_ALGO_RING_PIPELINED = 1, /* chunks cut into slices, each carried through all its hops by one
+                                 workgroup: no barriers, no flags; the running partial stays in
+                                 registers and every hop writes the receiver's partial, so the
+                                 all-reduce moves (3p-2)S bytes (p reads, 2(p-1) writes per
+                                 element position) and a reduce-scatter leaves the step-by-step
+                                 partials */
   RA_ALGO_RING_BIDIR = 2,     /* two counter-rotating rings, each on half of the buffer */
   RA_ALGO_FUSED = 3,          /* one pass: each element folded in its ring order, written to all ranks */
   RA_ALGO_TREE = 4,           /* binomial tree: reduce to rank 0, broadcast back */
@@ -111,7 +115,11 @@ typedef enum ra_algo {
   RA_ALGO_HIER = 7,           /* two-level ring on g ranks per node (ra_options.group): in-node
                                  reduce-scatter, cross-node ring all-reduce of each 1/g shard,
                                  in-node all-gather; 2(g-1) + 2(p/g-1) steps */
-  RA_ALGO_HIER_FUSED = 8      /* one pass in the same two-level order (the same bits as HIER) */
+  RA_ALGO_HIER_FUSED = 8,     /* one pass in the same two-level order (the same bits as HIER) */
+  RA_ALGO_RING_PIPELINED_FLAGS = 9 /* chunks cut into slices; workgroups play ranks, and a rank
+                                 forwards slice k as soon as its left neighbour's per-slice
+                                 ready counter says it has finished slice k (the layout a
+                                 ring of GPUs would run); 5(p-1)S bytes */
 } ra_algo;
 
 /* ra_options.flags bits */
@@ -123,6 +131,10 @@ typedef enum ra_algo {
                                      before each barrier arrival and each slice hop,
                                      shuffling arrival orders so that a missing fence
                                      or wait shows up as a wrong result */
+#define RA_FLAG_RENEW_COUNTERS 8u /* test hook, RING_PIPELINED_FLAGS: before the call the
+                                     stream's ready counters are reallocated (fresh zeros)
+                                     and the call's counter numbering starts at 2^31, as
+                                     after about 16.7 million calls and a larger one */
 #define RA_FLAG_WIDE_ACCUM 2u     /* RA_ALGO_FUSED, bfloat16 / float16 / float32 only:
                                      every term is widened exactly to float32
                                      (float64 for float32 buffers), the ring order
@@ -132,20 +144,25 @@ typedef enum ra_algo {
                                      Other algorithms or dtypes: RA_ERR_UNSUPPORTED. */
 
 typedef struct ra_options {
-  int64_t slice_elems;  /* RING_PIPELINED slice length in elements; 0 = library default
-                           (about four slices per worker per hop, at least 64 KiB, but
-                           at least eight slices per chunk when they can be 16 KiB or
-                           more).  Rounded up to a multiple of 16 bytes. */
+  int64_t slice_elems;  /* RING_PIPELINED: elements of a chunk one workgroup carries, in
+                           whole 256-vector tiles (rounded up); 0 = one tile (4 KiB).
+                           RING_PIPELINED_FLAGS: slice length in elements; 0 = library
+                           default (about four slices per worker per hop, at least
+                           64 KiB, but at least eight slices per chunk when they can be
+                           16 KiB or more), rounded up to a multiple of 16 bytes.  The
+                           result does not depend on it. */
   int64_t timeout_us;   /* budget of any single device-side wait; 0 = 10 s */
   int32_t grid;         /* step algorithms (RING_STEP, RING_BIDIR, TREE, HIER): 0 = the
                            library chooses (see RA_ALGO_RING_STEP).  1 with steps of at
                            most 256 vectors: the single workgroup.  Otherwise a value
                            above 0 runs one persistent grid of that many workgroups (at
                            most as many as fit the GPU) with a device-wide barrier
-                           between steps.  RING_PIPELINED, RING_CHANNELS: an upper bound
-                           on the workgroups of their persistent grid (the pipelined ring
-                           uses the same number per rank, rounded down to a multiple of 8
-                           when 8 or more fit); 0 = as many as fit the GPU. */
+                           between steps.  RING_PIPELINED_FLAGS, RING_CHANNELS: an upper
+                           bound on the workgroups of their persistent grid (the flag
+                           ring uses the same number per rank, rounded down to a
+                           multiple of 8 when 8 or more fit); 0 = 4 per compute unit.
+                           Values above what fits the GPU are cut to that.  Other
+                           algorithms ignore it. */
   uint32_t flags;       /* RA_FLAG_* */
   uint64_t* step_ts;    /* optional DEVICE array of (steps + 1) uint64: device wall-clock
                            ticks at kernel start and as each step's barrier releases
@@ -179,10 +196,11 @@ int ra_chunk_bounds(int64_t n, int p, int64_t* starts);
  * [Deepinsea] "Phase 1: Reduce-Scatter").  Step s: rank r's chunk (r - s) mod p is
  * added into rank r+1's copy of that chunk.  Afterwards rank r's chunk
  * (r + 1) mod p holds the full sum, accumulated in ring order.  What the other
- * chunks hold depends on the algorithm: RING_STEP, RING_PIPELINED and
- * RING_CHANNELS leave the ring's partial sum of chunk c over ranks c, c+1, ..., r
- * (the step-by-step states); FUSED (the default) leaves them as they were, and
- * moves (p+1)*S bytes instead of 3(p-1)*S ([InDepth] "Trade-offs": reduce-scatter
+ * chunks hold depends on the algorithm: RING_STEP, RING_PIPELINED,
+ * RING_PIPELINED_FLAGS and RING_CHANNELS leave the ring's partial sum of chunk c
+ * over ranks c, c+1, ..., r (the step-by-step states; RING_PIPELINED writes them
+ * in (2p-1)*S bytes); FUSED (the default) leaves them as they were, and moves
+ * (p+1)*S bytes instead of 3(p-1)*S ([InDepth] "Trade-offs": reduce-scatter
  * and all-gather are used on their own by sharded optimisers and FSDP).
  */
 int ra_reduce_scatter(void* const* bufs, int p, int64_t n, int dtype, int op,
@@ -213,8 +231,10 @@ int ra_allreduce(void* const* bufs, int p, int64_t n, int dtype, int op,
  *   algo  an ra_algo value.  RING_BIDIR: [InDepth] "What real libraries add",
  *         bidirectional rings -- the first ceil(n/2) elements go round the
  *         forward ring, the rest round the mirrored ring (rank r sends to r - 1,
- *         reduce-scatter step s sends chunk (r + s) mod p).  RING_PIPELINED:
- *         [InDepth] "What real libraries add", pipelining.  TREE: [Derive]
+ *         reduce-scatter step s sends chunk (r + s) mod p).  RING_PIPELINED,
+ *         RING_PIPELINED_FLAGS: [InDepth] "What real libraries add", pipelining
+ *         (a chunk cut into pieces, so that a piece moves on while the next one
+ *         is reduced).  TREE: [Derive]
  *         "Where it stops scaling", a binomial tree rooted at rank 0 (reduce
  *         level k adds rank r + 2^k into rank r for r a multiple of 2^(k+1)).
  *         RING_CHANNELS: [InDepth] "What real libraries add", multiple rings or
@@ -231,8 +251,8 @@ int ra_allreduce(void* const* bufs, int p, int64_t n, int dtype, int op,
 int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
                     const ra_options* opt, hipStream_t stream);
 
-/* ra_reduce_scatter / ra_all_gather with algo RING_STEP, RING_PIPELINED, RING_CHANNELS
- * or FUSED and options; other algorithms return RA_ERR_UNSUPPORTED, a channel count
+/* ra_reduce_scatter / ra_all_gather with algo RING_STEP, RING_PIPELINED,
+ * RING_PIPELINED_FLAGS, RING_CHANNELS or FUSED and options; other algorithms return RA_ERR_UNSUPPORTED, a channel count
  * outside 0..64 RA_ERR_INVALID_ARG. */
 int ra_reduce_scatter_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
                          const ra_options* opt, hipStream_t stream);

@@ -24,11 +24,12 @@ RA_MAX_RANKS = 64
 RA_FLAG_FORCE_TIMEOUT = 1
 RA_FLAG_WIDE_ACCUM = 2
 RA_FLAG_STRESS = 4
+RA_FLAG_RENEW_COUNTERS = 8
 OPS = {"sum": RA_SUM, "max": RA_MAX, "avg": RA_AVG}
 
 ALGOS = {"default": -1, "ring_step": 0, "ring_pipelined": 1, "ring_bidir": 2,
          "fused": 3, "tree": 4, "ring_channels": 5, "auto": 6, "hier": 7,
-         "hier_fused": 8}
+         "hier_fused": 8, "ring_pipelined_flags": 9}
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 DTYPE_NAMES = {"int32": RA_INT32, "float32": RA_FLOAT32, "bfloat16": RA_BFLOAT16,
                "float16": RA_FLOAT16, "float64": RA_FLOAT64, "int64": RA_INT64}

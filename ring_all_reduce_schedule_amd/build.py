@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libra.so")
 
-SOURCES = ["ra_fused.hip", "ra_steps.hip", "ra_copy.hip", "ra_api.cpp"]
+SOURCES = ["ra_fused.hip", "ra_rider.hip", "ra_steps.hip", "ra_copy.hip", "ra_api.cpp"]
 HEADERS = ["ra_elem.h", "ra_sync.h", "ra_internal.h"]
 
 

@@ -46,7 +46,7 @@ bool debug_on() {
   return on != 0;
 }
 
-constexpr int kLastAlgo = RA_ALGO_HIER_FUSED;
+constexpr int kLastAlgo = RA_ALGO_RING_PIPELINED_FLAGS;
 
 const char* algo_name(int a) {
   switch (a) {
@@ -59,6 +59,7 @@ const char* algo_name(int a) {
     case RA_ALGO_AUTO: return "auto";
     case RA_ALGO_HIER: return "hier";
     case RA_ALGO_HIER_FUSED: return "hier_fused";
+    case RA_ALGO_RING_PIPELINED_FLAGS: return "ring_pipelined_flags";
     default: return "?";
   }
 }
@@ -147,7 +148,8 @@ int model_choice(int p, double size_bytes, double alpha_s, double bytes_per_s) {
 
 bool phase_algo(int algo) {
   return algo == RA_ALGO_RING_STEP || algo == RA_ALGO_RING_PIPELINED ||
-         algo == RA_ALGO_RING_CHANNELS || algo == RA_ALGO_FUSED;
+         algo == RA_ALGO_RING_PIPELINED_FLAGS || algo == RA_ALGO_RING_CHANNELS ||
+         algo == RA_ALGO_FUSED;
 }
 
 bool is_float(int dtype) {
@@ -207,9 +209,12 @@ int get_workspace(hipStream_t s, Workspace** out) {
 }
 
 // Make room for `entries` ready counters and return the flag base of this call.
-int reserve_flags(Workspace* w, int64_t entries, hipStream_t s, uint32_t* base) {
+// renew (test hook): reallocate the counters (fresh zeros) and number this call
+// from 2^31, as a stream would after about 16.7 million calls and a larger one.
+int reserve_flags(Workspace* w, int64_t entries, hipStream_t s, bool renew, uint32_t* base) {
   std::lock_guard<std::mutex> lock(g_ws_mu);
-  if (entries > w->flag_cap) {
+  if (renew) w->epoch = (1u << 31) / kFlagStride - 1;
+  if (entries > w->flag_cap || (renew && w->flags)) {
     if (w->flags) {
       // the old counters may still be read by queued work on this stream
       hipError_t e = hipStreamSynchronize(s);
@@ -246,7 +251,8 @@ int reserve_flags(Workspace* w, int64_t entries, hipStream_t s, uint32_t* base) 
 // launches with no device-side waits, and the call allocates nothing -- it can
 // be captured in a HIP graph, even as the stream's first call.
 bool needs_workspace(int algo, const ra_options* opt) {
-  if (algo == RA_ALGO_RING_PIPELINED || algo == RA_ALGO_RING_CHANNELS) return true;
+  if (algo == RA_ALGO_RING_PIPELINED_FLAGS || algo == RA_ALGO_RING_CHANNELS) return true;
+  if (algo == RA_ALGO_RING_PIPELINED) return false;   // no device-side waits at all
   return opt && (opt->grid > 0 || opt->step_ts != nullptr ||
                  (opt->flags & (RA_FLAG_FORCE_TIMEOUT | RA_FLAG_STRESS)) != 0);
 }
@@ -302,6 +308,21 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
     debug_line(call, algo, p, n, dtype, grid);
     return RA_OK;
   }
+  if (algo == RA_ALGO_RING_PIPELINED) {
+    // slices carried through every hop by one workgroup: one ordinary launch
+    const int mode = hop_begin == 0 && hop_end == 2 * (p - 1) ? 0 : hop_begin == 0 ? 1 : 2;
+    ra::RankPtrs P;
+    fill_ptrs(bufs, p, &P);
+    ra::SyncCfg sc;
+    int rc = sync_cfg(opt, nullptr, &sc);
+    if (rc != RA_OK) return rc;
+    int grid = 0;
+    hipError_t e = ra::launch_rider(P, p, n, dtype, op, mode, opt ? opt->slice_elems : 0, sc.stress,
+                                    s, &grid);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    debug_line(call, algo, p, n, dtype, grid);
+    return RA_OK;
+  }
   Workspace* w = nullptr;
   int rc = RA_OK;
   if (needs_workspace(algo, opt)) {
@@ -315,7 +336,7 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
   fill_ptrs(bufs, p, &P);
   int grid = 0, launches = 1;
   hipError_t e;
-  if (algo == RA_ALGO_RING_PIPELINED) {
+  if (algo == RA_ALGO_RING_PIPELINED_FLAGS) {
     int64_t slice = opt && opt->slice_elems > 0
                         ? opt->slice_elems
                         : ra::pipelined_default_slice(p, n, dtype, sc.grid);
@@ -323,7 +344,7 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
     slice = (slice + V - 1) / V * V;
     const int64_t kmax = ra::pipelined_slices_per_chunk(p, n, dtype, slice);
     uint32_t base = 0;
-    rc = reserve_flags(w, kmax * p, s, &base);
+    rc = reserve_flags(w, kmax * p, s, opt && (opt->flags & RA_FLAG_RENEW_COUNTERS), &base);
     if (rc != RA_OK) return rc;
     e = ra::launch_pipelined(P, p, n, dtype, op, hop_begin, hop_end, slice, kmax, w->flags, base,
                              sc, s, &grid);
@@ -360,7 +381,8 @@ int ra_reduce_scatter_ex(void* const* bufs, int p, int64_t n, int dtype, int op,
   if (algo == RA_ALGO_DEFAULT) algo = RA_ALGO_FUSED;
   if (!phase_algo(algo))
     return fail(RA_ERR_UNSUPPORTED,
-                "reduce-scatter runs RING_STEP, RING_PIPELINED, RING_CHANNELS or FUSED, not %d", algo);
+                "reduce-scatter runs RING_STEP, RING_PIPELINED(_FLAGS), RING_CHANNELS or FUSED, not %d",
+                algo);
   rc = check_wide(opt, dtype, algo);
   if (rc != RA_OK) return rc;
   if (p == 1 || n == 0) return RA_OK;
@@ -375,7 +397,8 @@ int ra_all_gather_ex(void* const* bufs, int p, int64_t n, int dtype, int algo,
   if (algo == RA_ALGO_DEFAULT) algo = RA_ALGO_FUSED;
   if (!phase_algo(algo))
     return fail(RA_ERR_UNSUPPORTED,
-                "all-gather runs RING_STEP, RING_PIPELINED, RING_CHANNELS or FUSED, not %d", algo);
+                "all-gather runs RING_STEP, RING_PIPELINED(_FLAGS), RING_CHANNELS or FUSED, not %d",
+                algo);
   if (p == 1 || n == 0) return RA_OK;
   return run_ring("all_gather", bufs, p, n, dtype, RA_SUM, algo, p - 1, 2 * (p - 1), opt, stream);
 }

@@ -64,6 +64,13 @@ hipError_t launch_pipelined(const RankPtrs& P, int p, int64_t n, int dtype, int 
                             int hop_end, int64_t slice, int64_t kmax, uint32_t* flags,
                             uint32_t base, const SyncCfg& sc, hipStream_t s, int* grid_used);
 
+// The pipelined ring with every slice carried through all its hops by one
+// workgroup (no flags, no barriers).  mode 0: all-reduce, 1: reduce-scatter
+// (leaves the step-by-step partials), 2: all-gather.  slice_elems 0 = one tile
+// (kBlock vectors) per slice; stress != 0 adds the test hook's delays.
+hipError_t launch_rider(const RankPtrs& P, int p, int64_t n, int dtype, int op, int mode,
+                        int64_t slice_elems, uint32_t stress, hipStream_t s, int* grid_used);
+
 // Slices per chunk for the pipelined kernel (the host sizes `flags` with it).
 int64_t pipelined_slices_per_chunk(int p, int64_t n, int dtype, int64_t slice);
 

@@ -16,7 +16,8 @@
 //                per thread, everything else one.
 //   k_steps      the same schedules in one launch: on a single workgroup (its own
 //                barrier between steps; the default for smaller steps), or on a
-//                persistent cooperative grid with a grid barrier between steps
+//                persistent grid (every workgroup resident at once) with a grid
+//                barrier between steps
 //                (a caller's grid, channels, step timestamps, test hooks).
 //   k_pipelined  the forward ring with chunks cut into slices; workgroups are
 //                assigned to ranks, and a rank forwards slice k as soon as its
@@ -720,14 +721,27 @@ static hipError_t xcd_placement(bool* ok) {
   return hipSuccess;
 }
 
-// Workgroups per CU that persistent kernels rely on being co-resident.  The
-// occupancy query (and the cooperative-launch check built on it) counts vector
-// registers but not the scalar-register budget: kernels using ~100 SGPRs per
-// wave fit only 7 waves per SIMD on gfx950 while the query reports 8, so a
-// grid sized from the query can leave workgroups waiting for a slot that never
-// frees (measured: 2043 workgroups of the pipelined kernel stall, 576 do not).
-// Four workgroups of 256 threads put 4 waves on each SIMD, which fits any wave
-// using <= 128 VGPRs whatever its SGPR count; every kernel here uses < 64.
+// Persistent grids (the step kernels' device-wide barriers, the flag-driven
+// pipelined ring) are ordinary launches: nothing in them uses the runtime's
+// grid-wide synchronisation, so all they need is that every workgroup be
+// resident at once, and every wait in them is bounded (a grid that cannot
+// become resident -- another persistent grid holds the rest of the GPU -- ends
+// with RA_ERR_TIMEOUT instead of hanging).  The grid is therefore sized here
+// from what one CU can hold of the kernel:
+//  * the occupancy query, which accounts for vector registers and LDS, but not
+//    for the scalar-register file (measured: 2043 workgroups of a kernel the
+//    query rated at 8 per CU stalled, 576 did not);
+//  * the scalar-register bound: a gfx9 SIMD holds 800 SGPRs and a wave's
+//    allocation is at most 112 (the 102 addressable, VCC and the trap and
+//    flat-scratch registers, in granules of 16), so at least 7 waves per SIMD
+//    always fit -- 7 workgroups of 256 threads (one wave per SIMD each) per CU.
+// The kernels' actual use is below that (compiler resource report: at most
+// 106 SGPRs and 117 VGPRs per wave among the persistent kernels).
+static constexpr int kSgprWavesPerSimd = 7;
+// Of the resident maximum, the grid a persistent kernel takes by default:
+// 4 workgroups per CU (measured faster than fuller grids for the pipelined
+// flags kernel, whose 32 KiB of LDS per workgroup allows 4 anyway; a caller's
+// ra_options.grid may ask for up to the resident maximum).
 static constexpr int kPersistentPerCU = 4;
 
 // Workgroups of `func` that can be resident at once on the current device.
@@ -738,8 +752,15 @@ static hipError_t resident_blocks(const void* func, int* out) {
   int per_cu = 0;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, func, kBlock, 0);
   if (e != hipSuccess) return e;
-  *out = std::max(1, std::min(per_cu, kPersistentPerCU)) * cus;
+  *out = std::max(1, std::min(per_cu, kSgprWavesPerSimd)) * cus;
   return hipSuccess;
+}
+
+// The grid a persistent kernel runs by default, at most `resident`.
+static int default_persistent_grid(int resident) {
+  int cus = 0;
+  if (device_cus(&cus) != hipSuccess || cus <= 0) return resident;
+  return std::min(resident, kPersistentPerCU * cus);
 }
 
 
@@ -919,8 +940,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   // Small steps run on one workgroup with its own barrier between steps: a
   // device-wide barrier costs microseconds (L2 write-back, atomics across XCDs,
   // L2 invalidate), a workgroup barrier well under one.  One workgroup is
-  // resident by itself, so this is an ordinary launch, which costs far less
-  // than a cooperative one (measured: a two-step call 8.9 us against 22).
+  // resident by itself.
   if (block_ok) {
     a.sync = kSyncBlock;
     a.channels = 1;
@@ -935,7 +955,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   int resident = 0;
   hipError_t e = resident_blocks(func, &resident);
   if (e != hipSuccess) return e;
-  int grid = sc.grid > 0 ? std::min(sc.grid, resident) : resident;
+  int grid = sc.grid > 0 ? std::min(sc.grid, resident) : default_persistent_grid(resident);
   const int64_t tv = (int64_t)kBlock * kStepU;
   // no more workgroups than whole-segment tiles: on small buffers every extra
   // workgroup only adds to each barrier's cost
@@ -962,7 +982,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   a.W = std::max<int64_t>(1, maxvec);
   *grid_used = grid;
   *launches = 1;
-  return hipLaunchCooperativeKernel(func, dim3(grid), dim3(kBlock), args, 0, s);
+  return hipLaunchKernel(func, dim3(grid), dim3(kBlock), args, 0, s);
 }
 
 // (dtype, op) pairs that exist: avg needs a float type.
@@ -1004,8 +1024,7 @@ int64_t pipelined_default_slice(int p, int64_t n, int dtype, int grid_override) 
   int cus = 0;
   int64_t workers = 64;
   if (device_cus(&cus) == hipSuccess && cus > 0) {
-    int64_t budget = (int64_t)cus * kPersistentPerCU;
-    if (grid_override > 0) budget = std::min<int64_t>(budget, grid_override);
+    const int64_t budget = grid_override > 0 ? grid_override : (int64_t)cus * kPersistentPerCU;
     workers = std::max<int64_t>(1, budget / p);
   }
   const int64_t chunk = n / p + 1;
@@ -1059,9 +1078,9 @@ static hipError_t pipelined_dt(const RankPtrs& P, int p, int64_t n, int hop_begi
   int resident = 0;
   hipError_t e = resident_blocks(func, &resident);
   if (e != hipSuccess) return e;
-  int budget = sc.grid > 0 ? std::min(sc.grid, resident) : resident;
+  int budget = sc.grid > 0 ? std::min(sc.grid, resident) : default_persistent_grid(resident);
   int workers = (int)std::max<int64_t>(1, std::min<int64_t>(budget / p, kmax));
-  if (workers * p > resident) return hipErrorCooperativeLaunchTooLarge;
+  if (workers * p > resident) return hipErrorInvalidConfiguration;   // p > resident
   bool placed = false;
   e = xcd_placement(&placed);
   if (e != hipSuccess) return e;
@@ -1075,8 +1094,8 @@ static hipError_t pipelined_dt(const RankPtrs& P, int p, int64_t n, int hop_begi
   a.workers = workers;
   *grid_used = workers * p;
   void* args[] = {&a};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(func), dim3(workers * p),
-                                    dim3(kBlock), args, 0, s);
+  return hipLaunchKernel(reinterpret_cast<const void*>(func), dim3(workers * p), dim3(kBlock), args,
+                         0, s);
 }
 
 template <int DT>

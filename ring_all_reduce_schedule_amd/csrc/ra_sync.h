@@ -199,14 +199,19 @@ __device__ __forceinline__ bool xcd_local_barrier(WsHeader* ws, uint32_t* bar, b
 
 // Wait until *flag >= target (thread 0 spins, the workgroup follows).  Same
 // timeout and abort rules as grid_barrier.  Returns false when the caller must exit.
+// The comparison is unsigned: ready counters only grow between the host's
+// resets (every call numbers its hops above anything an earlier call left, and
+// the host zeroes the counters before the numbering would pass 2^32), so a
+// counter is below its target exactly when its unsigned value is -- also for a
+// counter left at zero by a fresh buffer while the numbering is past 2^31.
 __device__ __forceinline__ bool wait_flag(WsHeader* ws, const uint32_t* flag, uint32_t target,
                                           uint64_t limit) {
   __shared__ int go;
   if (threadIdx.x == 0) {
     int ok = 1;
-    if ((int32_t)(ld_relaxed(flag) - target) < 0) {
+    if (ld_relaxed(flag) < target) {
       uint64_t t0 = now_ticks();
-      while ((int32_t)(ld_relaxed(flag) - target) < 0) {
+      while (ld_relaxed(flag) < target) {
         if (ld_relaxed(&ws->status) != 0) { ok = 0; break; }
         if (now_ticks() - t0 > limit) {
           __hip_atomic_store(&ws->status, 6u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -58,7 +58,7 @@ int main(void) {
 
   const int algos[] = {RA_ALGO_DEFAULT, RA_ALGO_RING_STEP, RA_ALGO_RING_PIPELINED, RA_ALGO_RING_BIDIR,
                        RA_ALGO_FUSED, RA_ALGO_TREE, RA_ALGO_RING_CHANNELS, RA_ALGO_AUTO,
-                       RA_ALGO_HIER, RA_ALGO_HIER_FUSED};
+                       RA_ALGO_HIER, RA_ALGO_HIER_FUSED, RA_ALGO_RING_PIPELINED_FLAGS};
   for (unsigned a = 0; a < sizeof algos / sizeof algos[0]; ++a) {
     char what[96];
     snprintf(what, sizeof what, "ra_allreduce_ex algo %d, p=9 n=1000003 int32", algos[a]);

@@ -7,13 +7,13 @@ the documented choices:
 * steps that move at most 256 vectors: one launch of one workgroup;
 * larger steps: one launch per step (2(p-1) for the ring, 2*ceil(log2 p) for
   the tree);
-* a caller's grid, or channels: one persistent launch of that many workgroups.
+* a caller's grid, or channels: one persistent launch of that many workgroups;
+* the slice-carrying pipelined ring: one launch, one workgroup per 4 KiB slice
+  of every chunk.
 
-The persistent launches are cooperative, and a cooperative launch fails in a
-process while another live process on the same GPU has made one (the device's
-global wave-sync resource is held by one process at a time).  This file's name
-sorts first among the GPU tests, so the child runs before the test process
-itself makes any cooperative launch.
+Every launch is an ordinary one (persistent grids are sized to stay resident,
+not launched cooperatively), so the child can run while the test process holds
+the GPU too.
 """
 
 import os
@@ -40,6 +40,7 @@ B.ra_allreduce_ex(bufs(8, 1 << 20), algo="ring_step")            # large: a laun
 B.ra_allreduce_ex(bufs(8, 1 << 20), algo="tree")
 B.ra_allreduce_ex(bufs(8, 1 << 20), algo="ring_step", grid=16)   # caller's grid: persistent
 B.ra_allreduce_ex(bufs(8, 1 << 20), algo="ring_channels", channels=8)
+B.ra_allreduce_ex(bufs(8, 1 << 20), algo="ring_pipelined")       # one launch, a slice per workgroup
 B.ra_stream_status()
 torch.cuda.synchronize()
 """
@@ -58,10 +59,12 @@ def test_step_launch_choices():
         m = re.search(r"algo=(\w+) p=(\d+) n=(\d+) dtype=\d+ grid=(\d+) launches=(\d+)", ln)
         assert m, ln
         got.append((m.group(1), int(m.group(3)), int(m.group(4)), int(m.group(5))))
-    assert len(got) == 5, lines
-    (a0, n0, g0, l0), (a1, n1, g1, l1), (a2, n2, g2, l2), (a3, n3, g3, l3), (a4, n4, g4, l4) = got
+    assert len(got) == 6, lines
+    (a0, n0, g0, l0), (a1, n1, g1, l1), (a2, n2, g2, l2), (a3, n3, g3, l3), (a4, n4, g4, l4) = got[:5]
     assert (a0, g0, l0) == ("ring_step", 1, 1)
     assert (a1, l1) == ("ring_step", 14) and g1 > 1
     assert (a2, l2) == ("tree", 6) and g2 > 1
     assert (a3, g3, l3) == ("ring_step", 16, 1)
     assert a4 == "ring_channels" and l4 == 1 and g4 % 8 == 0
+    # 2^20 bf16 per rank: 8 chunks of 16384 vectors, 64 tiles of 256 each
+    assert got[5] == ("ring_pipelined", 1 << 20, 8 * 64, 1)

@@ -4,7 +4,7 @@ Four host threads, each with its own stream and its own rank buffers, issue
 interleaved sequences of all-reduces with every algorithm.  The library keeps
 its workspace per (device, stream) behind a lock and its error text per
 thread; the default step launches use no workspace at all.  Persistent grids
-(channels, pipelined) are given 32 workgroups each so that all four can be
+(channels, flag-driven pipelined) are given 32 workgroups each so that all four can be
 resident together.  Every result must equal the oracle's, bit for bit.
 """
 
@@ -22,7 +22,7 @@ from tests.gpu_util import require_gpu, to_dev, from_dev, same_bits, first_diff
 pytestmark = pytest.mark.gpu
 
 ALGOS = ["fused", "ring_step", "tree", "ring_bidir", "hier", "hier_fused", "ring_channels",
-         "ring_pipelined"]
+         "ring_pipelined", "ring_pipelined_flags"]
 
 
 def _want(xs, dtype, algo):
@@ -48,7 +48,7 @@ def _worker(tid, errors):
                 xs = inputs.make_inputs(p, n, dtype, seed=tid * 100 + k)
                 t = to_dev(xs, dtype)
                 opts = {"group": 2} if algo.startswith("hier") else {}
-                if algo in ("ring_channels", "ring_pipelined"):
+                if algo in ("ring_channels", "ring_pipelined_flags"):
                     opts["grid"] = 32
                 B.ra_allreduce_ex(t, algo=algo, **opts)
                 B.ra_stream_status(stream=stream)
@@ -62,9 +62,6 @@ def _worker(tid, errors):
         errors.append(f"thread {tid}: {e!r}")
 
 
-@pytest.mark.skip(reason="the GPU test process once ended with a segmentation fault at "
-                         "interpreter exit after this test and all others had passed; the "
-                         "cause is not established, so the test stays off until it is")
 def test_four_threads_four_streams():
     require_gpu()
     print("[case] four threads, four streams, mixed algorithms", flush=True)

@@ -3,7 +3,7 @@
 Element types int32, int64, float16, bfloat16, float32, float64; reductions sum,
 max and avg (pre-divided, floats only); the fused pass also with wide
 accumulation.  Every algorithm must match the oracle's result for its own order
-bit for bit: ring order for fused, ring_step, ring_pipelined and ring_channels,
+bit for bit: ring order for fused, ring_step, both pipelined rings and ring_channels,
 the bidirectional rings' halves for ring_bidir, the binomial tree for tree.
 """
 
@@ -20,8 +20,9 @@ pytestmark = pytest.mark.gpu
 
 DTYPES = ["int32", "int64", "float16", "bfloat16", "float32", "float64"]
 FLOATS = ["float16", "bfloat16", "float32", "float64"]
-ALGOS = ["fused", "ring_step", "ring_pipelined", "ring_channels", "ring_bidir", "tree"]
-RING = ["fused", "ring_step", "ring_pipelined", "ring_channels"]
+ALGOS = ["fused", "ring_step", "ring_pipelined", "ring_pipelined_flags", "ring_channels",
+         "ring_bidir", "tree"]
+RING = ["fused", "ring_step", "ring_pipelined", "ring_pipelined_flags", "ring_channels"]
 
 
 def expected(xs, dtype, algo, op, wide=False):
@@ -86,7 +87,8 @@ def test_wide_reduce_scatter(dtype, op):
         assert same_bits(got[r], want, dtype), f"rank {r} at {first_diff(got[r], want, dtype)}"
 
 
-@pytest.mark.parametrize("algo", ["ring_step", "ring_pipelined", "ring_channels", "fused"])
+@pytest.mark.parametrize("algo", ["ring_step", "ring_pipelined", "ring_pipelined_flags",
+                                  "ring_channels", "fused"])
 @pytest.mark.parametrize("op", ["max", "avg"])
 @pytest.mark.parametrize("dtype", ["float16", "float64"])
 def test_reduce_scatter_states_with_ops(algo, op, dtype):

@@ -1,6 +1,6 @@
 """GPU parity: every algorithm of libra.so against the CPU oracle (through the C ABI).
 
-Ring-ordered algorithms (ring_step, ring_pipelined, fused) and the bidirectional
+Ring-ordered algorithms (ring_step, both pipelined rings, fused) and the bidirectional
 rings must match the oracle bit for bit; the tree must match the oracle's tree
 bit for bit and be within the normwise tolerance of the float64 sum (1e-5 for
 float32, 1e-2 for bfloat16).  Integer results are exact for every algorithm.
@@ -17,7 +17,7 @@ from tests.gpu_util import require_gpu, to_dev, from_dev, same_bits, first_diff
 
 pytestmark = pytest.mark.gpu
 
-RING = ["fused", "ring_step", "ring_pipelined"]
+RING = ["fused", "ring_step", "ring_pipelined", "ring_pipelined_flags"]
 ALL = RING + ["ring_bidir", "tree"]
 TOL = {"float32": 1e-5, "bfloat16": 1e-2, "int32": 0.0}
 
@@ -136,7 +136,49 @@ def test_pipelined_slices_and_grids(slice_elems, grid, dtype):
     require_gpu()
     p, n = 9, 100_003
     xs = inputs.make_inputs(p, n, dtype, seed=slice_elems + grid, sigma=1.0)
-    check(xs, dtype, "ring_pipelined", slice_elems=slice_elems, grid=grid)
+    check(xs, dtype, "ring_pipelined_flags", slice_elems=slice_elems, grid=grid)
+
+
+# The slice-carrying pipelined ring: a workgroup carries one or more 256-vector
+# tiles of a chunk through all hops; chunk edges ride with slice 0.  Slices of
+# 1, 2 and many tiles, chunks shorter than a tile, ragged edges.
+@pytest.mark.parametrize("slice_elems", [0, 1, 2048, 2049, 5000, 1 << 20])
+@pytest.mark.parametrize("p,n,dtype", [(9, 100_003, "bfloat16"), (3, 70_001, "float32"),
+                                       (64, 8_195, "bfloat16"), (5, 40_960, "int32"),
+                                       (2, 4_111, "float64")])
+def test_pipelined_rider_slices(slice_elems, p, n, dtype):
+    require_gpu()
+    xs = inputs.make_inputs(p, n, dtype, seed=slice_elems % 1000 + p + n, sigma=1.0)
+    check(xs, dtype, "ring_pipelined", slice_elems=slice_elems)
+    # the reduce-scatter alone leaves the step-by-step partials on every chunk
+    t = to_dev(xs, dtype)
+    print(f"[case] RS ring_pipelined slice={slice_elems} p={p} n={n} {dtype}", flush=True)
+    B.ra_reduce_scatter_ex(t, algo="ring_pipelined", slice_elems=slice_elems)
+    B.ra_stream_status()
+    got = from_dev(t, dtype)
+    for r in range(p):
+        want = oracle.rs_partial(xs, dtype, r)
+        assert same_bits(got[r], want, dtype), f"rank {r} at {first_diff(got[r], want, dtype)}"
+
+
+def test_pipelined_flags_counters_numbered_past_two_to_the_31():
+    """Ready counters compared against targets above 2^31: a fresh (zeroed)
+    counter buffer must still read as 'not ready'.  The test hook reallocates
+    the counters and numbers the call from 2^31; later calls continue from
+    there, one of them on a larger buffer (the counters grow again)."""
+    require_gpu()
+    stream = torch.cuda.current_stream()
+    for k, (p, n, flags) in enumerate([(8, 300_007, B.RA_FLAG_RENEW_COUNTERS), (8, 300_007, 0),
+                                       (9, 2_000_003, 0), (4, 50_001, B.RA_FLAG_RENEW_COUNTERS)]):
+        xs = inputs.make_inputs(p, n, "bfloat16", seed=40 + k, sigma=1.0)
+        t = to_dev(xs, "bfloat16")
+        print(f"[case] flag counters call {k} p={p} n={n} flags={flags}", flush=True)
+        B.ra_allreduce_ex(t, algo="ring_pipelined_flags", flags=flags, slice_elems=2048,
+                          stream=stream)
+        B.ra_stream_status(stream=stream)
+        want = oracle.ring_fold(xs, "bfloat16")
+        for r, g in enumerate(from_dev(t, "bfloat16")):
+            assert same_bits(g, want, "bfloat16"), f"call {k} rank {r} at {first_diff(g, want, 'bfloat16')}"
 
 
 @pytest.mark.parametrize("algo", ["ring_step", "ring_bidir", "tree"])
@@ -161,7 +203,7 @@ def test_noop_cases():
 
 # ------------------------------------------------------------ reduce-scatter / all-gather
 
-@pytest.mark.parametrize("algo", ["ring_step", "ring_pipelined"])
+@pytest.mark.parametrize("algo", ["ring_step", "ring_pipelined", "ring_pipelined_flags"])
 @pytest.mark.parametrize("p,n,dtype", [(4, 4, "float32"), (9, 1_003, "int32"),
                                        (9, 100_003, "bfloat16"), (16, 70_001, "float32")])
 def test_reduce_scatter_states_then_all_gather(algo, p, n, dtype):
@@ -201,7 +243,7 @@ def test_default_entry_points():
 
 # ------------------------------------------------------------ failure handling
 
-@pytest.mark.parametrize("algo", ["ring_step", "ring_pipelined", "tree"])
+@pytest.mark.parametrize("algo", ["ring_step", "ring_pipelined_flags", "tree"])
 def test_forced_timeout_is_reported_and_cleared(algo):
     # the host asks the first device wait to expect an arrival that never comes;
     # with a 2 ms budget every workgroup gives up and exits, and the error shows

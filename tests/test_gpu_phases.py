@@ -20,7 +20,7 @@ from tests.gpu_util import require_gpu, to_dev, from_dev, same_bits, first_diff
 
 pytestmark = pytest.mark.gpu
 
-PHASE_ALGOS = ["ring_step", "ring_pipelined", "ring_channels", "fused"]
+PHASE_ALGOS = ["ring_step", "ring_pipelined", "ring_pipelined_flags", "ring_channels", "fused"]
 CASES = [(2, 1, "float32"), (3, 7, "int32"), (4, 4, "float32"), (5, 3, "bfloat16"),
          (8, 1023, "bfloat16"), (9, 100_003, "bfloat16"), (9, 1_000_003, "int32"),
          (16, 70_001, "float32"), (64, 4097, "bfloat16"), (64, 524_288, "float32")]

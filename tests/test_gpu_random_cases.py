@@ -37,7 +37,8 @@ FLOATS = {"float16", "bfloat16", "float32", "float64"}
 ALL_REDUCE = ["fused", "ring_step", "ring_pipelined", "ring_channels", "ring_bidir", "tree",
               "hier", "hier_fused", "auto"]
 PHASE = ["fused", "ring_step", "ring_pipelined", "ring_channels"]
-RING_ORDER = {"fused", "ring_step", "ring_pipelined", "ring_channels", "auto"}
+RING_ORDER = {"fused", "ring_step", "ring_pipelined", "ring_pipelined_flags", "ring_channels",
+              "auto"}
 
 
 def _divisors(p):
@@ -65,11 +66,15 @@ def _cases(count=1000, seed=20261202):
                     opts["grid"] = rng.choice([8, 24, 64])
             if algo == "ring_pipelined" and rng.random() < 0.5:
                 opts["slice_elems"] = rng.choice([8, 64, 1000, 4096])
+            if algo == "ring_pipelined" and i % 2 == 0:
+                algo = "ring_pipelined_flags"   # both pipelined forms, same draws
             if algo in ("hier", "hier_fused"):
                 opts["group"] = rng.choice(_divisors(p))
             out.append(("allreduce", i, p, n, dtype, op, algo, None, opts))
         else:
             rs, ag = rng.choice(PHASE), rng.choice(PHASE)
+            if i % 2 == 0:
+                rs, ag = (a + "_flags" if a == "ring_pipelined" else a for a in (rs, ag))
             out.append(("rs_ag", i, p, n, dtype, op, rs, ag, {}))
     return out
 
@@ -123,6 +128,8 @@ def _large_cases(count=60, seed=20261203):
             opts["slice_elems"] = rng.choice([1024, 4096, 65536])
         if algo == "ring_pipelined" and rng.random() < 0.3:
             opts["grid"] = rng.choice([64, 200, 512])
+        if algo == "ring_pipelined" and ("grid" in opts or i % 2 == 0):
+            algo = "ring_pipelined_flags"       # grids are the flag ring's option
         if algo == "hier":
             opts["group"] = rng.choice(_divisors(p))
         out.append(("allreduce", 1000 + i, p, n, dtype, op, algo, None, opts))

@@ -26,7 +26,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("algo,grid", [("ring_step", 64), ("tree", 64), ("hier", 64),
-                                       ("ring_channels", 64), ("ring_pipelined", 64),
+                                       ("ring_channels", 64), ("ring_pipelined_flags", 64),
+                                       ("ring_pipelined", 0),
                                        ("ring_step", 0), ("tree", 0), ("hier", 0), ("ring_bidir", 0)])
 def test_two_streams_at_once(algo, grid):
     require_gpu()

@@ -15,8 +15,9 @@ pytestmark = pytest.mark.gpu
 
 CASES = [  # (algo, options, oracle order)
     ("ring_step", {}, "ring"), ("ring_step", {"grid": 1024}, "ring"),
-    ("ring_step", {"grid": 64}, "ring"), ("ring_pipelined", {}, "ring"),
-    ("ring_pipelined", {"slice_elems": 4096}, "ring"), ("ring_bidir", {}, "bidir"),
+    ("ring_step", {"grid": 64}, "ring"), ("ring_pipelined_flags", {}, "ring"),
+    ("ring_pipelined_flags", {"slice_elems": 4096}, "ring"), ("ring_pipelined", {}, "ring"),
+    ("ring_bidir", {}, "bidir"),
     ("ring_channels", {"channels": 8}, "ring"), ("ring_channels", {"channels": 3}, "ring"),
     ("tree", {}, "tree"), ("hier", {"group": 4}, "hier"), ("hier", {"group": 2}, "hier"),
 ]
@@ -48,6 +49,7 @@ def test_stressed_allreduce(algo, opts, order, p, n, dtype):
 
 
 @pytest.mark.parametrize("algo,opts", [("ring_step", {}), ("ring_pipelined", {}),
+                                       ("ring_pipelined_flags", {}),
                                        ("ring_channels", {"channels": 8})])
 def test_stressed_reduce_scatter_states(algo, opts):
     require_gpu()

@@ -94,7 +94,8 @@ def _windows(n, p, seed):
 
 
 @pytest.mark.parametrize("algo", ["fused", "hier_fused", "ring_step", "tree", "ring_bidir",
-                                  "ring_channels", "ring_pipelined", "hier"])
+                                  "ring_channels", "ring_pipelined", "ring_pipelined_flags",
+                                  "hier"])
 def test_p8_bf16_16GB_windowed(algo):
     dev = require_gpu()
     w = inputs.WORKLOADS["p8_bf16_16GB"]
