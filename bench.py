@@ -66,6 +66,10 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="p8_bf16_16GB")
     ap.add_argument("--algo", default="fused")
+    ap.add_argument("--grid", type=int, default=0,
+                    help="ra_options.grid for the timed algorithm (0 = the library's choice)")
+    ap.add_argument("--channels", type=int, default=0,
+                    help="ra_options.channels for ring_channels (0 = automatic)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip variants, alpha, ceiling (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -566,8 +570,10 @@ def main():
     min_bytes = 2 * p * S
     ranks = B.RankBuffers(bufs)   # checked and marshalled once; refills are in place
 
+    step_opts = {k: v for k, v in (("grid", args.grid), ("channels", args.channels)) if v}
+
     def step():
-        B.ra_allreduce_ex(ranks, algo=args.algo)
+        B.ra_allreduce_ex(ranks, algo=args.algo, **step_opts)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -591,7 +597,10 @@ def main():
     ms_per_step = span / args.steps
     value = min_bytes / (ms_per_step * 1e-3) / 1e9
     launch_ms = sum(per) / len(per)
-    achieved = min_bytes / (launch_ms * 1e-3) / 1e9
+    # the roofline rates the timed kernel on the bytes it must move itself
+    # (2pS for the fused pass; the other algorithms move more, see own_bytes)
+    kernel_bytes = own_bytes(args.algo, p, S)
+    achieved = kernel_bytes / (launch_ms * 1e-3) / 1e9
     sha = kernel_source_sha()
     # the committed counter summary covers the fused kernel only
     traffic = read_traffic(sha, min_bytes) if args.algo == "fused" else None
@@ -610,7 +619,7 @@ def main():
         "dtype": {"bfloat16": "bf16", "float32": "f32", "int32": "int32"}[dtype],
         "data": "synthetic (seeded normal/uniform draws, generated in HBM or on the host)",
         "config": {"workload": args.workload, "p": p, "n_per_rank": n,
-                   "bytes_per_rank": S, "algo": args.algo,
+                   "bytes_per_rank": S, "algo": args.algo, **step_opts,
                    "bytes_counted": "2*p*S (each rank buffer read once and written once)",
                    "bytes_per_step": min_bytes},
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
@@ -620,6 +629,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": f"ra::k_fused<{dtype}>" if args.algo == "fused" else args.algo,
+                     "algorithmic_bytes": kernel_bytes,
                      "launch_ms_mean": round(launch_ms, 4),
                      "launch_ms_min": round(min(per), 4),
                      "kernel_source_sha": sha},

@@ -49,6 +49,41 @@ struct HopFlags {
   bool div_src, div_dst, keep_src;
 };
 
+// The vectors [t0, t1) of one tile, U per thread.  GUARD = false: the tile is
+// whole (t1 - t0 = kBlock * U), so no access needs a bounds test and all 2U
+// loads issue back to back before the first wait; with per-access guards the
+// compiler splits them into separately waited branches.
+template <int DT, int OP, int U, bool ADD, bool NT, bool GUARD>
+__device__ __forceinline__ void hop_vectors(void* __restrict__ src, void* __restrict__ dst,
+                                            int64_t t0, int64_t t1, int p, HopFlags f) {
+  constexpr bool kDiv = OP == kAvg && ADD;
+  int64_t v[U];
+  u32x4 a[U], b[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    v[u] = t0 + u * kBlock + threadIdx.x;
+    if (!GUARD || v[u] < t1) {
+      a[u] = ld16<NT>(src, v[u]);
+      if (ADD) b[u] = ld16<NT>(dst, v[u]);
+    }
+  }
+  if (kDiv) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (f.div_src) a[u] = vdiv<DT>(a[u], p);
+      if (f.div_dst) b[u] = vdiv<DT>(b[u], p);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (!GUARD || v[u] < t1) st16<NT>(dst, v[u], ADD ? vcomb<DT, OP>(b[u], a[u]) : a[u]);
+  if (kDiv && f.keep_src) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (!GUARD || v[u] < t1) st16<NT>(src, v[u], a[u]);
+  }
+}
+
 template <int DT, int OP, int U, bool ADD, bool NT>
 __device__ __forceinline__ void hop_tile(void* __restrict__ src, void* __restrict__ dst,
                                          int64_t lo, int64_t hi, int64_t j, int p, HopFlags f) {
@@ -59,33 +94,10 @@ __device__ __forceinline__ void hop_tile(void* __restrict__ src, void* __restric
   const int64_t tv = (int64_t)kBlock * U;
   const int64_t t0 = sp.v0 + j * tv;
   const int64_t t1 = t0 + tv < sp.v1 ? t0 + tv : sp.v1;
-  if (t0 < t1) {
-    int64_t v[U];
-    u32x4 a[U], b[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      v[u] = t0 + u * kBlock + threadIdx.x;
-      if (v[u] < t1) {
-        a[u] = ld16<NT>(src, v[u]);
-        if (ADD) b[u] = ld16<NT>(dst, v[u]);
-      }
-    }
-    if (kDiv) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (f.div_src) a[u] = vdiv<DT>(a[u], p);
-        if (f.div_dst) b[u] = vdiv<DT>(b[u], p);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (v[u] < t1) st16<NT>(dst, v[u], ADD ? vcomb<DT, OP>(b[u], a[u]) : a[u]);
-    if (kDiv && f.keep_src) {
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (v[u] < t1) st16<NT>(src, v[u], a[u]);
-    }
-  }
+  if (t1 - t0 == tv)        // the same for the whole workgroup
+    hop_vectors<DT, OP, U, ADD, NT, false>(src, dst, t0, t1, p, f);
+  else if (t0 < t1)
+    hop_vectors<DT, OP, U, ADD, NT, true>(src, dst, t0, t1, p, f);
   if (j == 0) {
     const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
     const int t = threadIdx.x;
