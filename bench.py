@@ -70,13 +70,18 @@ def parse_args():
                     help="ra_options.grid for the timed algorithm (0 = the library's choice)")
     ap.add_argument("--channels", type=int, default=0,
                     help="ra_options.channels for ring_channels (0 = automatic)")
+    ap.add_argument("--group", type=int, default=0,
+                    help="ra_options.group for hier / hier_fused (0 = the library's default)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip variants, alpha, ceiling (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=3 << 27,
                     help="elements per rank of the CPU-oracle sample")
-    ap.add_argument("--mode", default="allreduce", choices=["allreduce", "copy"],
-                    help="copy: only the plain copy kernel, for counter calibration")
+    ap.add_argument("--mode", default="allreduce",
+                    choices=["allreduce", "copy", "reduce_scatter", "all_gather"],
+                    help="copy: only the plain copy kernel, for counter calibration; "
+                         "reduce_scatter / all_gather: only that phase with --algo on the "
+                         "workload's buffers (counter runs)")
     ap.add_argument("--detail", default=os.path.join(ROOT, "gpurun_out", "bench_detail.json"),
                     help="file for the full measurement record ('' = none)")
     return ap.parse_args()
@@ -503,6 +508,7 @@ def summary_line(result):
     out = {k: result[k] for k in SUMMARY_KEYS if k in result}
     if "ceiling" in result:
         out["copy_ceiling_GBps"] = result["ceiling"].get("GBps")
+        out["resident_copy_ceiling_GBps"] = result["ceiling"].get("resident_GBps")
     if "variants" in result:
         out["algos_ms"] = {k: v["ms"] for k, v in result["variants"].items()}
     fit = result.get("alpha", {}).get("fit")
@@ -570,7 +576,23 @@ def main():
     min_bytes = 2 * p * S
     ranks = B.RankBuffers(bufs)   # checked and marshalled once; refills are in place
 
-    step_opts = {k: v for k, v in (("grid", args.grid), ("channels", args.channels)) if v}
+    step_opts = {k: v for k, v in (("grid", args.grid), ("channels", args.channels),
+                                   ("group", args.group)) if v}
+
+    if args.mode in ("reduce_scatter", "all_gather"):
+        # one phase alone, for counter runs: its time and byte counts only
+        f = B.ra_reduce_scatter_ex if args.mode == "reduce_scatter" else B.ra_all_gather_ex
+        fn = lambda: f(ranks, algo=args.algo, **step_opts)
+        for _ in range(args.warmup):
+            fn()
+        B.ra_stream_status()
+        per, _ = time_calls(fn, args.steps, torch)
+        B.ra_stream_status()
+        floor, moved = phase_bytes(args.mode, args.algo, p, S)
+        print(json.dumps({"mode": args.mode, "algo": args.algo, "workload": args.workload,
+                          "ms": [round(x, 3) for x in per], "bytes_floor": floor,
+                          "bytes_moved": moved}), flush=True)
+        return
 
     def step():
         B.ra_allreduce_ex(ranks, algo=args.algo, **step_opts)
@@ -644,6 +666,10 @@ def main():
                                      "ring_bidir", "ring_channels",
                                      "tree")]
         runs += [(a, a, {"group": hier_group(p)}) for a in ("hier", "hier_fused")]
+        # the step ring on one persistent grid with device-wide barriers between
+        # steps (the library's default persistent grid: 5 workgroups per CU)
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        runs += [("ring_step_persistent", "ring_step", {"grid": 5 * cus})]
         runs += [("fused_wide_fp32_accumulate", "fused", {"wide": True}),
                  ("fused_avg", "fused", {"op": "avg"}), ("fused_max", "fused", {"op": "max"})]
         for name, algo, kw in runs:
@@ -673,8 +699,16 @@ def main():
         src = bufs[0].view(torch.int16)[: chunk // 2]
         dst = bufs[1].view(torch.int16)[: chunk // 2]
         cper, _ = time_calls(lambda: B.ra_stream_copy(dst, src), 5, torch)
+        # the same copy on the persistent kernels' default resident grid, their
+        # own streaming ceiling
+        rper, _ = time_calls(lambda: B.ra_stream_copy_resident(dst, src), 5, torch)
         result["ceiling"] = {"kernel": "ra::k_copy", "bytes_moved": 2 * chunk,
-                             "GBps": round(2 * chunk / (min(cper) * 1e-3) / 1e9, 1)}
+                             "GBps": round(2 * chunk / (min(cper) * 1e-3) / 1e9, 1),
+                             "resident_kernel": "ra::k_copy_resident",
+                             "resident_GBps": round(2 * chunk / (min(rper) * 1e-3) / 1e9, 1)}
+        for v in result["variants"].values():
+            v["pct_of_copy_on_hbm_bytes"] = round(
+                100 * v["GBps_on_hbm_bytes"] / result["ceiling"]["GBps"], 1)
         if "GBps" in result["ceiling"] and result["ceiling"]["GBps"]:
             result["pct_of_copy_ceiling"] = round(100.0 * value / result["ceiling"]["GBps"], 2)
 

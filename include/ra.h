@@ -311,6 +311,18 @@ int ra_wallclock_hz(int64_t* hz);
  */
 int ra_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream);
 
+/*
+ * ra_stream_copy_resident -- the same copy on a resident grid of `grid`
+ * workgroups (0 = the library's default persistent grid, 5 per compute unit)
+ * that loop over 16 KiB tiles, workgroup b taking tiles b, b + grid, ...: the
+ * shape of the persistent step kernels, and the streaming ceiling they are
+ * compared with (on MI355X a resident grid streams slower than a grid that
+ * covers the data once).  Same argument rules as ra_stream_copy; grid < 0 is
+ * RA_ERR_INVALID_ARG.  Not part of the all-reduce.
+ */
+int ra_stream_copy_resident(void* dst, const void* src, int64_t bytes, int grid,
+                            hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

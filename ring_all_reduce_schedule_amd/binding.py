@@ -78,6 +78,7 @@ _SIGNATURES = {
     "ra_last_error": (ctypes.c_char_p, []),
     "ra_wallclock_hz": (_int, [ctypes.POINTER(ctypes.c_int64)]),
     "ra_stream_copy": (_int, [_vp, _vp, _i64, _vp]),
+    "ra_stream_copy_resident": (_int, [_vp, _vp, _i64, _int, _vp]),
 }
 
 
@@ -296,3 +297,12 @@ def ra_stream_copy(dst, src, stream=None):
     return _check(lib().ra_stream_copy(ctypes.c_void_p(dst.data_ptr()),
                                        ctypes.c_void_p(src.data_ptr()), nbytes,
                                        _stream_handle(stream, src.device)))
+
+
+def ra_stream_copy_resident(dst, src, grid=0, stream=None):
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    return _check(lib().ra_stream_copy_resident(ctypes.c_void_p(dst.data_ptr()),
+                                                ctypes.c_void_p(src.data_ptr()), nbytes,
+                                                int(grid), _stream_handle(stream, src.device)))

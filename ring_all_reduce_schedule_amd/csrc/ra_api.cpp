@@ -542,6 +542,20 @@ int ra_wallclock_hz(int64_t* hz) {
   return RA_OK;
 }
 
+int ra_stream_copy_resident(void* dst, const void* src, int64_t bytes, int grid,
+                            hipStream_t stream) {
+  if (!dst || !src) return fail(RA_ERR_INVALID_ARG, "NULL pointer");
+  if (bytes < 0 || bytes % 16 != 0) return fail(RA_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+  if (grid < 0) return fail(RA_ERR_INVALID_ARG, "grid = %d, need grid >= 0", grid);
+  if (reinterpret_cast<uintptr_t>(dst) % 16 || reinterpret_cast<uintptr_t>(src) % 16)
+    return fail(RA_ERR_MISALIGNED, "pointers must be 16-byte aligned");
+  if (grid == 0) grid = ra::default_persistent_workgroups();
+  if (grid <= 0) return fail(RA_ERR_HIP, "cannot query the device's compute units");
+  hipError_t e = ra::launch_copy_resident(dst, src, bytes, grid, stream);
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  return RA_OK;
+}
+
 int ra_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream) {
   if (!dst || !src) return fail(RA_ERR_INVALID_ARG, "NULL pointer");
   if (bytes < 0 || bytes % 16 != 0) return fail(RA_ERR_INVALID_ARG, "bytes must be a multiple of 16");

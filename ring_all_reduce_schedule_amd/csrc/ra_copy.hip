@@ -17,6 +17,36 @@ __global__ __launch_bounds__(kBlock) void k_copy(u32x4* __restrict__ dst,
     st16<NT>(dst, v, ld16<NT>(src, v));
 }
 
+// The same copy on a resident grid of `grid` workgroups that loop over 16 KiB
+// tiles (four vectors per thread), tile t = b, b + grid, ... for workgroup b:
+// the shape of the persistent step kernels, and the ceiling they are rated
+// against.  The 16-byte vectors past the last whole tile go one per thread.
+__global__ __launch_bounds__(kBlock) void k_copy_resident(u32x4* __restrict__ dst,
+                                                          const u32x4* __restrict__ src,
+                                                          int64_t nvec) {
+  constexpr int U = 4;
+  const int64_t tiles = nvec / (kBlock * U);
+  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const int64_t base = t * kBlock * U + threadIdx.x;
+    u32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = ld16<true>(src, base + u * kBlock);
+#pragma unroll
+    for (int u = 0; u < U; ++u) st16<true>(dst, base + u * kBlock, x[u]);
+  }
+  for (int64_t v = tiles * kBlock * U + (int64_t)blockIdx.x * kBlock + threadIdx.x; v < nvec;
+       v += (int64_t)gridDim.x * kBlock)
+    st16<true>(dst, v, ld16<true>(src, v));
+}
+
+hipError_t launch_copy_resident(void* dst, const void* src, int64_t bytes, int grid, hipStream_t s) {
+  const int64_t nvec = bytes / 16;
+  if (nvec == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_copy_resident, dim3(grid), dim3(kBlock), 0, s, reinterpret_cast<u32x4*>(dst),
+                     reinterpret_cast<const u32x4*>(src), nvec);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s) {
   const int64_t nvec = bytes / 16;
   if (nvec == 0) return hipSuccess;

@@ -77,8 +77,13 @@ int64_t pipelined_slices_per_chunk(int p, int64_t n, int dtype, int64_t slice);
 // Slice length used when the caller does not choose one.
 int64_t pipelined_default_slice(int p, int64_t n, int dtype, int grid_override);
 
-// Plain streaming copy (measurement helper).
+// Plain streaming copy (measurement helpers): one-shot grid, and a resident
+// grid of `grid` workgroups looping over tiles.
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
+hipError_t launch_copy_resident(void* dst, const void* src, int64_t bytes, int grid, hipStream_t s);
+
+// Workgroups a persistent step kernel runs by default on the current device.
+int default_persistent_workgroups();
 
 // ---------------------------------------------------------------- host helpers
 

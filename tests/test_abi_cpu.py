@@ -95,6 +95,10 @@ def test_argument_errors_are_reported_before_any_gpu_work():
                                         ctypes.byref(o), None) == B.RA_ERR_INVALID_ARG
     assert lib.ra_stream_copy(None, None, 16, None) == B.RA_ERR_INVALID_ARG
     assert lib.ra_stream_copy(base, base + 4096, 15, None) == B.RA_ERR_INVALID_ARG
+    assert lib.ra_stream_copy_resident(None, None, 16, 8, None) == B.RA_ERR_INVALID_ARG
+    assert lib.ra_stream_copy_resident(base, base + 4096, 15, 8, None) == B.RA_ERR_INVALID_ARG
+    assert lib.ra_stream_copy_resident(base, base + 4096, 16, -1, None) == B.RA_ERR_INVALID_ARG
+    assert lib.ra_stream_copy_resident(base + 8, base + 4096, 16, 8, None) == B.RA_ERR_MISALIGNED
 
 
 def test_status_strings():

@@ -349,3 +349,17 @@ def test_stream_copy():
     B.ra_stream_copy(dst, src)
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
+
+
+@pytest.mark.parametrize("nbytes,grid", [(16, 1), (16 << 10, 3), ((16 << 10) + 48, 7),
+                                         ((1 << 24) + 4096 + 16, 0), (1 << 26, 1000)])
+def test_stream_copy_resident(nbytes, grid):
+    # whole 16 KiB tiles on the resident grid, the vectors past them one per thread
+    require_gpu()
+    src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros(nbytes // 4 + 64, dtype=torch.int32, device="cuda")
+    print(f"[case] resident copy bytes={nbytes} grid={grid}", flush=True)
+    B.ra_stream_copy_resident(dst, src, grid=grid)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[: nbytes // 4], src)
+    assert not dst[nbytes // 4:].any()
