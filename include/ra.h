@@ -270,6 +270,31 @@ int ra_all_gather_ex(void* const* bufs, int p, int64_t n, int dtype, int algo,
 int ra_stream_status(hipStream_t stream);
 
 /*
+ * ra_allreduce_noalloc -- ra_allreduce_ex for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, algorithms and results as
+ * ra_allreduce_ex; the call allocates nothing.  The device workspace of the
+ * persistent grids (barrier words, status word, the flag-driven pipelined
+ * ring's ready counters) is a 1 MiB array in the library's own device data,
+ * one per GPU, held until the process ends:
+ *  - ready counters: at most 258,048 per call (p times the slices per chunk of
+ *    RING_PIPELINED_FLAGS); a call that needs more returns RA_ERR_UNSUPPORTED
+ *    before enqueueing anything (larger ra_options.slice_elems need fewer);
+ *  - the array keeps what the last call left (counters are numbered per call
+ *    and reset by a kernel on the calling stream when the numbering wraps);
+ *  - every call on a GPU shares that GPU's array, so calls that overlap on one
+ *    GPU (on different streams, or from different threads) race;
+ *  - a device-side timeout is sticky in the array: later calls on that GPU do
+ *    no work until ra_stream_status (on any stream of that GPU) reports it,
+ *    which also clears it.
+ * The placement probe that lets persistent grids synchronise per XCD needs an
+ * allocation; until another call has run it on the device, these calls use
+ * device-wide barriers instead (same results).
+ */
+int ra_allreduce_noalloc(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
+                         const ra_options* opt, hipStream_t stream);
+
+/*
  * ra_select_algo -- the algorithm RA_ALGO_AUTO runs for an all-reduce of p buffers
  * of n elements of `dtype` ([InDepth] "Trade-offs": libraries choose between
  * ring and tree for each call, by the size of the message and the number of

@@ -67,6 +67,8 @@ _SIGNATURES = {
     "ra_allreduce": (_int, [ctypes.POINTER(_vp), _int, _i64, _int, _int, _vp]),
     "ra_allreduce_ex": (_int, [ctypes.POINTER(_vp), _int, _i64, _int, _int, _int,
                                ctypes.POINTER(ra_options), _vp]),
+    "ra_allreduce_noalloc": (_int, [ctypes.POINTER(_vp), _int, _i64, _int, _int, _int,
+                                    ctypes.POINTER(ra_options), _vp]),
     "ra_reduce_scatter_ex": (_int, [ctypes.POINTER(_vp), _int, _i64, _int, _int, _int,
                                     ctypes.POINTER(ra_options), _vp]),
     "ra_all_gather_ex": (_int, [ctypes.POINTER(_vp), _int, _i64, _int, _int,
@@ -243,6 +245,13 @@ def ra_allreduce_ex(tensors, algo="default", op="sum", stream=None, **opts):
     o = _options(**opts)
     return _check(lib().ra_allreduce_ex(ptrs, p, n, dt, _op(op), _algo(algo), ctypes.byref(o),
                                         _stream_handle(stream, dev)))
+
+
+def ra_allreduce_noalloc(tensors, algo="default", op="sum", stream=None, **opts):
+    ptrs, p, n, dt, dev = _marshal(tensors)
+    o = _options(**opts)
+    return _check(lib().ra_allreduce_noalloc(ptrs, p, n, dt, _op(op), _algo(algo), ctypes.byref(o),
+                                             _stream_handle(stream, dev)))
 
 
 def ra_reduce_scatter(tensors, op="sum", stream=None):

@@ -94,9 +94,9 @@ int check_args(void* const* bufs, int p, int64_t n, int dtype) {
     const uint64_t bytes = (uint64_t)n * (uint64_t)ra::elem_bytes(dtype);
     if (bytes / (uint64_t)ra::elem_bytes(dtype) != (uint64_t)n)
       return fail(RA_ERR_INVALID_ARG, "n = %lld overflows the address space", (long long)n);
-    std::vector<std::pair<uintptr_t, int>> starts;
-    for (int r = 0; r < p; ++r) starts.emplace_back(reinterpret_cast<uintptr_t>(bufs[r]), r);
-    std::sort(starts.begin(), starts.end());
+    std::pair<uintptr_t, int> starts[RA_MAX_RANKS];   // no heap: the no-alloc entry uses this too
+    for (int r = 0; r < p; ++r) starts[r] = {reinterpret_cast<uintptr_t>(bufs[r]), r};
+    std::sort(starts, starts + p);
     for (int i = 0; i + 1 < p; ++i)
       if (starts[i].first + bytes > starts[i + 1].first)
         return fail(RA_ERR_ALIAS, "buffers of ranks %d and %d overlap", starts[i].second,
@@ -183,6 +183,8 @@ struct Workspace {
   uint32_t* flags = nullptr;       // device, pipelined ready counters
   int64_t flag_cap = 0;            // entries
   uint32_t epoch = 0;              // pipelined calls so far (flag base = epoch * kFlagStride)
+  bool fixed = false;              // the device's no-alloc scratch: never reallocated, reset
+                                   // by fill kernels on the calling stream
 };
 
 constexpr uint32_t kFlagStride = 128;   // > 2(p-1) hops for p <= 64
@@ -213,6 +215,23 @@ int get_workspace(hipStream_t s, Workspace** out) {
 // from 2^31, as a stream would after about 16.7 million calls and a larger one.
 int reserve_flags(Workspace* w, int64_t entries, hipStream_t s, bool renew, uint32_t* base) {
   std::lock_guard<std::mutex> lock(g_ws_mu);
+  if (w->fixed) {
+    // the no-alloc scratch: a fixed number of counters, zeroed by a kernel on s
+    if (entries > w->flag_cap)
+      return fail(RA_ERR_UNSUPPORTED,
+                  "the call needs %lld ready counters; the no-alloc workspace holds %lld "
+                  "(use larger slices)", (long long)entries, (long long)w->flag_cap);
+    if (renew) w->epoch = (1u << 31) / kFlagStride - 1;
+    w->epoch += 1;
+    const bool wrap = (uint64_t)w->epoch * kFlagStride + kFlagStride >= 0xFFFFFFFFull;
+    if (wrap) w->epoch = 1;
+    if (renew || wrap) {
+      hipError_t e = ra::launch_fill_u32(w->flags, 0u, w->flag_cap, s);
+      if (e != hipSuccess) return fail_hip(e, "resetting flags");
+    }
+    *base = w->epoch * kFlagStride;
+    return RA_OK;
+  }
   if (renew) w->epoch = (1u << 31) / kFlagStride - 1;
   if (entries > w->flag_cap || (renew && w->flags)) {
     if (w->flags) {
@@ -241,6 +260,51 @@ int reserve_flags(Workspace* w, int64_t entries, hipStream_t s, bool renew, uint
     w->epoch = 1;
   }
   *base = w->epoch * kFlagStride;
+  return RA_OK;
+}
+
+// ---------------------------------------------------------------- no-alloc workspace
+
+// The workspace of ra_allreduce_noalloc: one array per GPU, in the library's
+// device data, so that calls which must not allocate (HIP graph capture, tight
+// serving loops) still have barrier words, a status word and ready counters.
+// Layout: the WsHeader at offset 0, the ready counters from kScratchFlagsAt on.
+// Every call on a GPU shares its array, and the array keeps what the last call
+// left; calls that overlap on one GPU race.  The array's host-side name is only
+// a stand-in for the device symbol: host code uses the address that
+// hipGetSymbolAddress returns for the current device, never the name itself.
+constexpr size_t kScratchBytes = 1u << 20;
+constexpr size_t kScratchFlagsAt = 16u << 10;
+static_assert(sizeof(ra::WsHeader) <= kScratchFlagsAt, "scratch header does not fit");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+Workspace g_scratch_ws[kMaxDevices];   // guarded by g_ws_mu; hdr == nullptr until set up
+bool g_scratch_used[kMaxDevices];
+
+// This device's scratch workspace, its address looked up once per device with
+// that device current.
+int get_scratch(Workspace** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RA_ERR_UNSUPPORTED, "device %d: the no-alloc workspace serves devices 0..%d",
+                dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace& w = g_scratch_ws[dev];
+  if (!w.hdr) {
+    unsigned char* ptr = nullptr;
+    e = hipGetSymbolAddress(reinterpret_cast<void**>(&ptr), HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+    w.hdr = reinterpret_cast<ra::WsHeader*>(ptr);
+    w.flags = reinterpret_cast<uint32_t*>(ptr + kScratchFlagsAt);
+    w.flag_cap = (int64_t)((kScratchBytes - kScratchFlagsAt) / sizeof(uint32_t));
+    w.epoch = 0;
+    w.fixed = true;
+  }
+  g_scratch_used[dev] = true;
+  *out = &w;
   return RA_OK;
 }
 
@@ -275,6 +339,7 @@ int sync_cfg(const ra_options* opt, Workspace* w, ra::SyncCfg* sc) {
   sc->grid = opt && opt->grid > 0 ? opt->grid : 0;
   sc->channels = 1;
   sc->group = 1;
+  sc->may_probe = !(w && w->fixed);
   return RA_OK;
 }
 
@@ -295,8 +360,10 @@ void debug_line(const char* call, int algo, int p, int64_t n, int dtype, int gri
 
 // Run phases [hop_begin, hop_end) (0..p-2 reduce-scatter, p-1..2p-3 all-gather)
 // with a ring algorithm.
+// noalloc: the persistent grids' workspace is this device's scratch array.
 int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
-             int hop_begin, int hop_end, const ra_options* opt, hipStream_t s) {
+             int hop_begin, int hop_end, const ra_options* opt, hipStream_t s,
+             bool noalloc = false) {
   if (algo == RA_ALGO_FUSED) {
     // the fused pass covers whole phases only
     const int mode = hop_begin == 0 && hop_end == 2 * (p - 1) ? 0 : hop_begin == 0 ? 1 : 2;
@@ -326,7 +393,7 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
   Workspace* w = nullptr;
   int rc = RA_OK;
   if (needs_workspace(algo, opt)) {
-    rc = get_workspace(s, &w);
+    rc = noalloc ? get_scratch(&w) : get_workspace(s, &w);
     if (rc != RA_OK) return rc;
   }
   ra::SyncCfg sc;
@@ -355,6 +422,69 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
   }
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   debug_line(call, algo, p, n, dtype, grid, launches);
+  return RA_OK;
+}
+
+// ra_allreduce_ex and ra_allreduce_noalloc: noalloc takes the persistent grids'
+// workspace from this device's scratch array instead of the stream's.
+int allreduce_impl(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
+                   const ra_options* opt, hipStream_t stream, bool noalloc) {
+  int rc = check_args(bufs, p, n, dtype);
+  if (rc == RA_OK) rc = check_op(op, dtype);
+  if (rc == RA_OK) rc = check_channels(opt);
+  if (rc != RA_OK) return rc;
+  if (algo == RA_ALGO_DEFAULT) algo = env_algo(RA_ALGO_FUSED);
+  if (algo < RA_ALGO_RING_STEP || algo > kLastAlgo)
+    return fail(RA_ERR_INVALID_ARG, "unknown algo %d", algo);
+  if (algo == RA_ALGO_AUTO) {
+    rc = ra_select_algo(p, n, dtype, opt, &algo);
+    if (rc != RA_OK) return rc;
+  }
+  rc = check_wide(opt, dtype, algo);
+  if (rc == RA_OK) rc = check_group(opt, p);
+  if (rc != RA_OK) return rc;
+  if (p == 1 || n == 0) return RA_OK;
+  if (phase_algo(algo))
+    return run_ring("allreduce", bufs, p, n, dtype, op, algo, 0, 2 * (p - 1), opt, stream,
+                    noalloc);
+  if (algo == RA_ALGO_HIER_FUSED) {
+    ra::RankPtrs P;
+    fill_ptrs(bufs, p, &P);
+    int grid = 0;
+    hipError_t e = ra::launch_fused_hier(P, p, n, dtype, op, hier_group(opt, p), stream, &grid);
+    if (e != hipSuccess) return fail_hip(e, "kernel launch");
+    debug_line("allreduce", algo, p, n, dtype, grid);
+    return RA_OK;
+  }
+  // bidirectional rings, tree or hierarchy: the step kernels
+  Workspace* w = nullptr;
+  if (needs_workspace(algo, opt)) {
+    rc = noalloc ? get_scratch(&w) : get_workspace(stream, &w);
+    if (rc != RA_OK) return rc;
+  }
+  ra::SyncCfg sc;
+  rc = sync_cfg(opt, w, &sc);
+  if (rc != RA_OK) return rc;
+  ra::RankPtrs P;
+  fill_ptrs(bufs, p, &P);
+  int grid = 0, launches = 1;
+  hipError_t e;
+  if (algo == RA_ALGO_RING_BIDIR) {
+    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeBidir, 0, 2 * (p - 1), sc, stream, &grid,
+                         &launches);
+  } else if (algo == RA_ALGO_HIER) {
+    sc.group = hier_group(opt, p);
+    const int m = p / sc.group;
+    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeHier, 0, 2 * (sc.group - 1) + 2 * (m - 1), sc,
+                         stream, &grid, &launches);
+  } else {
+    int levels = 0;
+    while ((1 << levels) < p) ++levels;
+    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeTree, 0, 2 * levels, sc, stream, &grid,
+                         &launches);
+  }
+  if (e != hipSuccess) return fail_hip(e, "kernel launch");
+  debug_line("allreduce", algo, p, n, dtype, grid, launches);
   return RA_OK;
 }
 
@@ -413,62 +543,12 @@ int ra_all_gather(void* const* bufs, int p, int64_t n, int dtype, hipStream_t st
 
 int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
                     const ra_options* opt, hipStream_t stream) {
-  int rc = check_args(bufs, p, n, dtype);
-  if (rc == RA_OK) rc = check_op(op, dtype);
-  if (rc == RA_OK) rc = check_channels(opt);
-  if (rc != RA_OK) return rc;
-  if (algo == RA_ALGO_DEFAULT) algo = env_algo(RA_ALGO_FUSED);
-  if (algo < RA_ALGO_RING_STEP || algo > kLastAlgo)
-    return fail(RA_ERR_INVALID_ARG, "unknown algo %d", algo);
-  if (algo == RA_ALGO_AUTO) {
-    rc = ra_select_algo(p, n, dtype, opt, &algo);
-    if (rc != RA_OK) return rc;
-  }
-  rc = check_wide(opt, dtype, algo);
-  if (rc == RA_OK) rc = check_group(opt, p);
-  if (rc != RA_OK) return rc;
-  if (p == 1 || n == 0) return RA_OK;
-  if (phase_algo(algo))
-    return run_ring("allreduce", bufs, p, n, dtype, op, algo, 0, 2 * (p - 1), opt, stream);
-  if (algo == RA_ALGO_HIER_FUSED) {
-    ra::RankPtrs P;
-    fill_ptrs(bufs, p, &P);
-    int grid = 0;
-    hipError_t e = ra::launch_fused_hier(P, p, n, dtype, op, hier_group(opt, p), stream, &grid);
-    if (e != hipSuccess) return fail_hip(e, "kernel launch");
-    debug_line("allreduce", algo, p, n, dtype, grid);
-    return RA_OK;
-  }
-  // bidirectional rings, tree or hierarchy: the step kernels
-  Workspace* w = nullptr;
-  if (needs_workspace(algo, opt)) {
-    rc = get_workspace(stream, &w);
-    if (rc != RA_OK) return rc;
-  }
-  ra::SyncCfg sc;
-  rc = sync_cfg(opt, w, &sc);
-  if (rc != RA_OK) return rc;
-  ra::RankPtrs P;
-  fill_ptrs(bufs, p, &P);
-  int grid = 0, launches = 1;
-  hipError_t e;
-  if (algo == RA_ALGO_RING_BIDIR) {
-    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeBidir, 0, 2 * (p - 1), sc, stream, &grid,
-                         &launches);
-  } else if (algo == RA_ALGO_HIER) {
-    sc.group = hier_group(opt, p);
-    const int m = p / sc.group;
-    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeHier, 0, 2 * (sc.group - 1) + 2 * (m - 1), sc,
-                         stream, &grid, &launches);
-  } else {
-    int levels = 0;
-    while ((1 << levels) < p) ++levels;
-    e = ra::launch_steps(P, p, n, dtype, op, ra::kModeTree, 0, 2 * levels, sc, stream, &grid,
-                         &launches);
-  }
-  if (e != hipSuccess) return fail_hip(e, "kernel launch");
-  debug_line("allreduce", algo, p, n, dtype, grid, launches);
-  return RA_OK;
+  return allreduce_impl(bufs, p, n, dtype, op, algo, opt, stream, false);
+}
+
+int ra_allreduce_noalloc(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,
+                         const ra_options* opt, hipStream_t stream) {
+  return allreduce_impl(bufs, p, n, dtype, op, algo, opt, stream, true);
 }
 
 int ra_allreduce(void* const* bufs, int p, int64_t n, int dtype, int op, hipStream_t stream) {
@@ -481,21 +561,26 @@ int ra_stream_status(hipStream_t stream) {
   int dev = 0;
   e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
-  ra::WsHeader* hdr = nullptr;
+  // the stream's own workspace, and the device's no-alloc scratch if a call used it
+  ra::WsHeader* hdrs[2] = {nullptr, nullptr};
   {
     std::lock_guard<std::mutex> lock(g_ws_mu);
     auto it = g_ws.find({dev, stream});
-    if (it == g_ws.end() || !it->second.hdr) return RA_OK;
-    hdr = it->second.hdr;
+    if (it != g_ws.end()) hdrs[0] = it->second.hdr;
+    if (dev >= 0 && dev < kMaxDevices && g_scratch_used[dev]) hdrs[1] = g_scratch_ws[dev].hdr;
   }
-  uint32_t status = 0;
-  e = hipMemcpy(&status, &hdr->status, sizeof status, hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return fail_hip(e, "reading device status");
-  if (status == 0) return RA_OK;
-  // clear the sticky error and the barrier words the aborted kernel left behind
-  e = hipMemset(hdr, 0, sizeof(ra::WsHeader));
-  if (e != hipSuccess) return fail_hip(e, "clearing device status");
-  return fail((int)status, "a device-side wait timed out (status %u)", status);
+  for (ra::WsHeader* hdr : hdrs) {
+    if (!hdr) continue;
+    uint32_t status = 0;
+    e = hipMemcpy(&status, &hdr->status, sizeof status, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail_hip(e, "reading device status");
+    if (status == 0) continue;
+    // clear the sticky error and the barrier words the aborted kernel left behind
+    e = hipMemset(hdr, 0, sizeof(ra::WsHeader));
+    if (e != hipSuccess) return fail_hip(e, "clearing device status");
+    return fail((int)status, "a device-side wait timed out (status %u)", status);
+  }
+  return RA_OK;
 }
 
 int ra_select_algo(int p, int64_t n, int dtype, const ra_options* opt, int* algo_out) {

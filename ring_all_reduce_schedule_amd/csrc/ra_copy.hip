@@ -47,6 +47,19 @@ hipError_t launch_copy_resident(void* dst, const void* src, int64_t bytes, int g
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(kBlock) void k_fill_u32(uint32_t* dst, uint32_t value, int64_t count) {
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * kBlock)
+    dst[i] = value;
+}
+
+hipError_t launch_fill_u32(uint32_t* dst, uint32_t value, int64_t count, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>((count + kBlock - 1) / kBlock, 1024);
+  hipLaunchKernelGGL(k_fill_u32, dim3(grid), dim3(kBlock), 0, s, dst, value, count);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s) {
   const int64_t nvec = bytes / 16;
   if (nvec == 0) return hipSuccess;

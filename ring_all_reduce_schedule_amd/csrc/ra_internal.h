@@ -28,6 +28,8 @@ struct SyncCfg {
   int grid;               // 0 = as many workgroups as are co-resident
   int channels;           // step kernels: independent channels (1 = whole grid, 0 = automatic)
   int group;              // kModeHier: ranks per node g (g divides p)
+  bool may_probe;         // may run (and allocate for) the one-time XCD placement probe;
+                          // false: an unprobed device counts as unplaced
 };
 
 // Launch descriptions return the number of workgroups used through *grid_used.
@@ -76,6 +78,10 @@ int64_t pipelined_slices_per_chunk(int p, int64_t n, int dtype, int64_t slice);
 
 // Slice length used when the caller does not choose one.
 int64_t pipelined_default_slice(int p, int64_t n, int dtype, int grid_override);
+
+// dst[0 .. count) = value, a kernel on stream s (a fill that a graph capture
+// records as a kernel, not as a memset).
+hipError_t launch_fill_u32(uint32_t* dst, uint32_t value, int64_t count, hipStream_t s);
 
 // Plain streaming copy (measurement helpers): one-shot grid, and a resident
 // grid of `grid` workgroups looping over tiles.

@@ -702,7 +702,7 @@ __global__ void k_xcc_probe(uint32_t* out) {
 // XCD of b mod 8, and blocks 0..7 must cover 8 distinct XCDs).  The two-level
 // and XCD-local synchronisation rely on it; without it everything stays on the
 // device-wide barrier.
-static hipError_t xcd_placement(bool* ok) {
+static hipError_t xcd_placement(bool* ok, bool may_probe) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -711,6 +711,10 @@ static hipError_t xcd_placement(bool* ok) {
   std::lock_guard<std::mutex> lock(mu);
   auto it = cache.find(dev);
   if (it != cache.end()) { *ok = it->second; return hipSuccess; }
+  if (!may_probe) {         // the probe needs a device buffer: without it, assume nothing
+    *ok = false;
+    return hipSuccess;
+  }
   constexpr int kProbe = 1024;
   uint32_t* d = nullptr;
   e = hipMalloc(&d, kProbe * sizeof(uint32_t));
@@ -990,7 +994,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   a.channels = std::max(1, std::min(std::min(want, kMaxChannels), grid));
   grid = grid / a.channels * a.channels;
   bool placed = false;
-  e = xcd_placement(&placed);
+  e = xcd_placement(&placed, sc.may_probe);
   if (e != hipSuccess) return e;
   // the two-level barrier pays from about 128 workgroups (measured: 4.2 against
   // 10 us at 256, 2.8 against 2.5 us at 64)
@@ -1101,7 +1105,7 @@ static hipError_t pipelined_dt(const RankPtrs& P, int p, int64_t n, int hop_begi
   int workers = (int)std::max<int64_t>(1, std::min<int64_t>(budget / p, kmax));
   if (workers * p > resident) return hipErrorInvalidConfiguration;   // p > resident
   bool placed = false;
-  e = xcd_placement(&placed);
+  e = xcd_placement(&placed, sc.may_probe);
   if (e != hipSuccess) return e;
   // a multiple of 8 workers keeps every slice on one XCD: measured on MI355X
   // (bf16, p = 9) 0.61 ms at 64 MiB per rank with 112 workers against 1.60 with
