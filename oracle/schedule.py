@@ -24,17 +24,24 @@ the ring: +1 forward, -1 mirrored.
 def chunk_bounds(n, p):
     """Half-open element ranges [start, end) of the p chunks of an n-element buffer.
 
-    [InDepth] "An implementation": chunk i starts at i*floor(n/p) + min(i, n mod p),
-    so the first n mod p chunks are one element longer.  Python ints throughout,
-    so buffers beyond 2**32 elements are exact.
+    [InDepth] "An implementation": every chunk gets floor(n/p) elements and the
+    first n mod p chunks one more, laid end to end from element 0.  Python ints
+    throughout, so buffers beyond 2**32 elements are exact.
     """
     if p < 1:
         raise ValueError("p must be >= 1")
     if n < 0:
         raise ValueError("n must be >= 0")
-    base, extra = divmod(n, p)
-    starts = [i * base + min(i, extra) for i in range(p + 1)]
-    return [(starts[i], starts[i + 1]) for i in range(p)]
+    short = n // p
+    longer = n - short * p          # chunks that take one extra element
+    bounds = []
+    lo = 0
+    for c in range(p):
+        size = short + 1 if c < longer else short
+        bounds.append((lo, lo + size))
+        lo += size
+    assert lo == n
+    return bounds
 
 
 def chunk_of(i, n, p):
