@@ -107,3 +107,67 @@ def test_as_values():
     assert oracle.as_values(np.array([3], np.int32), "int32").dtype == np.int64
     bits = f32_to_bf16_bits(np.array([1.5, -2.0], np.float32))
     assert oracle.as_values(bits, "bfloat16").tolist() == [1.5, -2.0]
+
+
+# ------------------------------------------------------------ subnormals
+
+from fractions import Fraction
+
+# (precision in bits including the leading one, smallest normal exponent)
+_FORMATS = {"float32": (24, -126), "bfloat16": (8, -126), "float16": (11, -14),
+            "float64": (53, -1022)}
+
+
+def _round_exact(v, dtype):
+    """The IEEE binary value nearest to the rational v, ties to even, with
+    gradual underflow: the spacing below 2**emin stays that of the smallest
+    binade.  Written from the format's definition, not from numpy."""
+    prec, emin = _FORMATS[dtype]
+    if v == 0:
+        return Fraction(0)
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()   # within one of floor(log2 a)
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, emin)
+    q = Fraction(2) ** (e - (prec - 1))          # spacing of representable values here
+    m = a / q
+    lo = m.numerator // m.denominator
+    rem = m - lo
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and lo % 2 == 1):
+        lo += 1
+    r = lo * q
+    return r if v > 0 else -r
+
+
+def _values(bits, dtype):
+    return [Fraction(float(x)) for x in oracle.as_values(bits, dtype)]
+
+
+@pytest.mark.parametrize("dtype", ["float32", "bfloat16", "float16", "float64"])
+def test_add_rounded_with_subnormals_matches_exact_rounding(dtype):
+    """Sums of subnormal and near-subnormal operands: the oracle's hop equals the
+    exact sum rounded once, so no operand or result is flushed to zero."""
+    prec, emin = _FORMATS[dtype]
+    rng = np.random.default_rng(prec)
+    tiny = 2.0 ** (emin - prec + 1)              # smallest subnormal
+    k = rng.integers(-3 * 2 ** (prec - 1), 3 * 2 ** (prec - 1), (2, 1500))
+    # multiples of the smallest subnormal (subnormal and just-normal values),
+    # and products with odd numbers that need rounding when they are normal
+    raw = np.concatenate([k * tiny, (2 * k + 1) * tiny * rng.integers(1, 9, (2, 1500))], axis=1)
+    if dtype == "bfloat16":
+        a = f32_to_bf16_bits(raw[0].astype(np.float32))
+        b = f32_to_bf16_bits(raw[1].astype(np.float32))
+    else:
+        t = oracle.arith.STORAGE[dtype]
+        a, b = raw[0].astype(t), raw[1].astype(t)
+    got = add_rounded(a, b, dtype)
+    va, vb, vg = _values(a, dtype), _values(b, dtype), _values(got, dtype)
+    subnormal_results = 0
+    for x, y, g in zip(va, vb, vg):
+        want = _round_exact(x + y, dtype)
+        assert g == want, (dtype, x, y, g, want)
+        subnormal_results += 0 < abs(want) < Fraction(2) ** emin
+    assert subnormal_results > 500
