@@ -14,7 +14,6 @@
 #include <mutex>
 #include <string>
 #include <utility>
-#include <vector>
 
 #include "ra_elem.h"
 #include "ra_sync.h"

@@ -29,7 +29,6 @@
 
 #include <mutex>
 #include <utility>
-#include <vector>
 #include <unordered_map>
 
 namespace ra {
@@ -850,45 +849,55 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   // segment geometry and the widest segment in vectors
   // every element range a step may work on (chunks of the ring's halves, whole
   // buffers for the tree, intra chunks and their inter pieces for the hierarchy)
-  std::vector<std::pair<int64_t, int64_t>> ranges;
+  // (enumerated on demand, not stored: a call allocates no host memory either)
   int64_t hier_intra = 0, hier_inter = 0;   // hier: widest in-node chunk, widest cross-node piece
+  const int64_t len0 = mode == kModeBidir ? (n + 1) / 2 : n;
   if (mode == kModeHier) {
     a.half[0] = a.half[1] = make_geo(0, n, a.g);
-    for (int c = 0; c < a.g; ++c) {
-      const int64_t lo = host_chunk_lo(0, n, a.g, c), hi = host_chunk_lo(0, n, a.g, c + 1);
-      ranges.emplace_back(lo, hi);
-      hier_intra = std::max(hier_intra, vecs_in(lo, hi, V));
-      for (int d = 0; d < a.m; ++d) {
-        const int64_t plo = host_chunk_lo(lo, hi - lo, a.m, d), phi = host_chunk_lo(lo, hi - lo, a.m, d + 1);
-        ranges.emplace_back(plo, phi);
-        hier_inter = std::max(hier_inter, vecs_in(plo, phi, V));
-      }
-    }
   } else if (mode == kModeTree) {
     a.half[0] = a.half[1] = make_geo(0, n, p);
-    ranges.emplace_back(0, n);
   } else {
-    const int64_t len0 = mode == kModeBidir ? (n + 1) / 2 : n;
     a.half[0] = make_geo(0, len0, p);
     a.half[1] = make_geo(len0, n - len0, p);
-    const int nh = mode == kModeBidir ? 2 : 1;
-    for (int h = 0; h < nh; ++h) {
-      const int64_t off = h ? len0 : 0, len = h ? n - len0 : len0;
-      for (int c = 0; c < p; ++c)
-        ranges.emplace_back(host_chunk_lo(off, len, p, c), host_chunk_lo(off, len, p, c + 1));
+  }
+  auto for_each_range = [&](auto fn) {
+    if (mode == kModeHier) {
+      for (int c = 0; c < a.g; ++c) {
+        const int64_t lo = host_chunk_lo(0, n, a.g, c), hi = host_chunk_lo(0, n, a.g, c + 1);
+        fn(lo, hi);
+        for (int d = 0; d < a.m; ++d)
+          fn(host_chunk_lo(lo, hi - lo, a.m, d), host_chunk_lo(lo, hi - lo, a.m, d + 1));
+      }
+    } else if (mode == kModeTree) {
+      fn((int64_t)0, n);
+    } else {
+      const int nh = mode == kModeBidir ? 2 : 1;
+      for (int h = 0; h < nh; ++h) {
+        const int64_t off = h ? len0 : 0, len = h ? n - len0 : len0;
+        for (int c = 0; c < p; ++c) fn(host_chunk_lo(off, len, p, c), host_chunk_lo(off, len, p, c + 1));
+      }
+    }
+  };
+  if (mode == kModeHier) {
+    for (int c = 0; c < a.g; ++c) {
+      const int64_t lo = host_chunk_lo(0, n, a.g, c), hi = host_chunk_lo(0, n, a.g, c + 1);
+      hier_intra = std::max(hier_intra, vecs_in(lo, hi, V));
+      for (int d = 0; d < a.m; ++d)
+        hier_inter = std::max(hier_inter, vecs_in(host_chunk_lo(lo, hi - lo, a.m, d),
+                                                  host_chunk_lo(lo, hi - lo, a.m, d + 1), V));
     }
   }
   // whole vectors of the widest part of any range cut C ways (the kernel's rule:
   // part h of [lo, hi) starts at lo + h*floor(len/C) + min(h, len mod C))
   auto widest = [&](int C) {
     int64_t w = 0;
-    for (const auto& r : ranges) {
-      const int64_t len = r.second - r.first, q = len / C, rem = len % C;
+    for_each_range([&](int64_t first, int64_t last) {
+      const int64_t len = last - first, q = len / C, rem = len % C;
       for (int h = 0; h < C; ++h) {
-        const int64_t lo = r.first + h * q + std::min<int64_t>(h, rem);
+        const int64_t lo = first + h * q + std::min<int64_t>(h, rem);
         w = std::max(w, vecs_in(lo, lo + q + (h < rem ? 1 : 0), V));
       }
-    }
+    });
     return w;
   };
   const int64_t maxvec = widest(1);
