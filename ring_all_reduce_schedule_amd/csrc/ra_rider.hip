@@ -2,9 +2,9 @@
 // into slices, and every slice carried round the ring by one workgroup.
 //
 // "Ring All-Reduce, in depth", section "What real libraries add", pipelining:
-// a chunk is cut into pieces so that a piece can move on to the next rank while
-// the one behind it is still being reduced, and the step latency hides behind
-// the transfer.  On one GPU the finest form of that is a workgroup per slice
+// chunks are cut into pieces, and a piece goes on to the next rank as soon as it
+// is done instead of waiting for its whole chunk, so per-step waiting overlaps
+// with moving data.  On one GPU the finest form of that is a workgroup per slice
 // that takes its slice through every hop itself: hop h of slice k runs as soon
 // as hop h-1 of the same slice is done (program order inside the workgroup),
 // and the slices of all chunks are in flight at once with no barrier and no

@@ -28,7 +28,7 @@ def test_library_exports_every_header_symbol():
                                            67_108_864, 8_000_000_000, 2**40 + 7)])
 def test_chunk_bounds_matches_oracle(n, p):
     starts = B.ra_chunk_bounds(n, p)
-    assert [(starts[i], starts[i + 1]) for i in range(p)] == oracle.chunk_bounds(n, p)
+    assert list(zip(starts[:-1], starts[1:])) == oracle.chunk_bounds(n, p)
 
 
 def test_chunk_bounds_errors():
