@@ -277,7 +277,7 @@ int ra_stream_status(hipStream_t stream);
  * persistent grids (barrier words, status word, the flag-driven pipelined
  * ring's ready counters) is a 1 MiB array in the library's own device data,
  * one per GPU, held until the process ends:
- *  - ready counters: at most 258,048 per call (p times the slices per chunk of
+ *  - ready counters: at most 253,952 per call (p times the slices per chunk of
  *    RING_PIPELINED_FLAGS); a call that needs more returns RA_ERR_UNSUPPORTED
  *    before enqueueing anything (larger ra_options.slice_elems need fewer);
  *  - the array keeps what the last call left (counters are numbered per call
@@ -343,11 +343,14 @@ int ra_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream
 /*
  * ra_stream_copy_resident -- the same copy on a resident grid of `grid`
  * workgroups (0 = the library's default persistent grid, 5 per compute unit)
- * that loop over 16 KiB tiles, workgroup b taking tiles b, b + grid, ...: the
- * shape of the persistent step kernels, and the streaming ceiling they are
+ * that loop over 16 KiB tiles, the workgroups of each XCD taking a contiguous
+ * range of tiles in order from a tile counter: the way the persistent step
+ * kernels take a large step's tiles, and the streaming ceiling they are
  * compared with (on MI355X a resident grid streams slower than a grid that
- * covers the data once).  Same argument rules as ra_stream_copy; grid < 0 is
- * RA_ERR_INVALID_ARG.  Not part of the all-reduce.
+ * covers the data once).  The counters live in the stream's workspace, which
+ * the first call on a stream allocates, as the all-reduce calls do.  Same
+ * argument rules as ra_stream_copy; grid < 0 is RA_ERR_INVALID_ARG.  Not part
+ * of the all-reduce.
  */
 int ra_stream_copy_resident(void* dst, const void* src, int64_t bytes, int grid,
                             hipStream_t stream);

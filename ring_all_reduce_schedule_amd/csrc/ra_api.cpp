@@ -273,7 +273,7 @@ int reserve_flags(Workspace* w, int64_t entries, hipStream_t s, bool renew, uint
 // a stand-in for the device symbol: host code uses the address that
 // hipGetSymbolAddress returns for the current device, never the name itself.
 constexpr size_t kScratchBytes = 1u << 20;
-constexpr size_t kScratchFlagsAt = 16u << 10;
+constexpr size_t kScratchFlagsAt = 32u << 10;
 static_assert(sizeof(ra::WsHeader) <= kScratchFlagsAt, "scratch header does not fit");
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
@@ -635,7 +635,10 @@ int ra_stream_copy_resident(void* dst, const void* src, int64_t bytes, int grid,
     return fail(RA_ERR_MISALIGNED, "pointers must be 16-byte aligned");
   if (grid == 0) grid = ra::default_persistent_workgroups();
   if (grid <= 0) return fail(RA_ERR_HIP, "cannot query the device's compute units");
-  hipError_t e = ra::launch_copy_resident(dst, src, bytes, grid, stream);
+  Workspace* w = nullptr;
+  int rc = get_workspace(stream, &w);
+  if (rc != RA_OK) return rc;
+  hipError_t e = ra::launch_copy_resident(dst, src, bytes, grid, &w->hdr->tiles[0][0], stream);
   if (e != hipSuccess) return fail_hip(e, "kernel launch");
   return RA_OK;
 }

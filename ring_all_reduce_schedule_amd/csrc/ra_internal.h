@@ -84,9 +84,11 @@ int64_t pipelined_default_slice(int p, int64_t n, int dtype, int grid_override);
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t value, int64_t count, hipStream_t s);
 
 // Plain streaming copy (measurement helpers): one-shot grid, and a resident
-// grid of `grid` workgroups looping over tiles.
+// grid of `grid` workgroups looping over tiles handed out in order from tile
+// counters at ctr (8 of them, 32 words apart; zeroed here, on s).
 hipError_t launch_copy(void* dst, const void* src, int64_t bytes, hipStream_t s);
-hipError_t launch_copy_resident(void* dst, const void* src, int64_t bytes, int grid, hipStream_t s);
+hipError_t launch_copy_resident(void* dst, const void* src, int64_t bytes, int grid,
+                                uint32_t* ctr, hipStream_t s);
 
 // Workgroups a persistent step kernel runs by default on the current device.
 int default_persistent_workgroups();

@@ -17,7 +17,8 @@
 //   k_steps      the same schedules in one launch: on a single workgroup (its own
 //                barrier between steps; the default for smaller steps), or on a
 //                persistent grid (every workgroup resident at once) with a grid
-//                barrier between steps
+//                barrier between steps, each XCD's workgroups taking a
+//                contiguous range of a step's tiles in order from a counter
 //                (a caller's grid, channels, step timestamps, test hooks).
 //   k_pipelined  the forward ring with chunks cut into slices; workgroups are
 //                assigned to ranks, and a rank forwards slice k as soon as its
@@ -28,6 +29,7 @@
 #include "ra_internal.h"
 
 #include <mutex>
+#include <numeric>
 #include <utility>
 #include <unordered_map>
 
@@ -283,6 +285,10 @@ __device__ __forceinline__ void hop_slice_lds(void* __restrict__ src, void* __re
 
 // ================================================================ step by step
 
+// Tiles per workgroup from which a persistent grid's step takes its tiles from
+// tile counters (in order) rather than in a fixed stride.
+constexpr int64_t kHandOutTiles = 8;
+
 struct StepArgs {
   RankPtrs P;
   ChunkGeo half[2];     // ring: half[0] = whole buffer; bidir: forward, mirrored half
@@ -296,6 +302,7 @@ struct StepArgs {
   int channels;         // C: workgroup b serves channel b mod C
   int g, m;             // hier: ranks per node, nodes (half[0] = the g-way intra partition)
   int sync;             // SyncScope of the barriers between steps
+  int qn;               // persistent grid: tile counters (workgroup groups) per channel
   uint32_t expect_extra;
   uint32_t stress;      // test hook: delays before arrivals (stress_delay)
 };
@@ -532,9 +539,35 @@ __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
   uint32_t* bar = a.ws->bar[h];
   const bool leader = b == 0;
   uint32_t extra = a.expect_extra;
+  // Steps with at least kHandOutTiles tiles per workgroup hand their tiles out
+  // in order from tile counters, one tile per grab.  The channel's workgroups
+  // form qn groups (group x = b mod qn; with one channel, group x is XCD x,
+  // since workgroup b runs on XCD b mod 8), and group x takes a contiguous range
+  // of the step's tiles, sized to its share of the channel's workgroups, from a
+  // counter of its own.  Measured at p = 8 with 16 GB per rank: a resident grid
+  // whose workgroups walk fixed strided tiles takes 95.6 ms, the same grid with
+  // in-order ranges per XCD 88.8 (one launch per step: 88.3); tiles of one
+  // counter interleaved over the XCDs gained nothing, and one counter for the
+  // whole grid doubled the time (its atomics serialise).  The host zeroes the
+  // counters before a launch that has such a step; the step advances counter x
+  // by its range's length plus one failing grab per workgroup of the group, so
+  // every workgroup knows the next step's base without reading it (the barrier
+  // between steps orders the grabs).  Smaller steps keep fixed strided tiles
+  // (workgroup b: tiles b, b + nbh, ...): there a grab's round trip costs more
+  // than the imbalance it removes (p = 9, 4 MB per rank: 0.121 against 0.095 ms
+  // with eight channels).  (Taking the next tile before moving the current one,
+  // to overlap the atomic with the loads, measured 1% slower.)
+  const int qn = a.qn;
+  const int xq = (int)(b % qn);
+  const int64_t per = nbh / qn, more = nbh % qn;
+  const int64_t w0 = xq * per + (xq < more ? xq : more);       // workgroups of groups < x
+  const int64_t wq = per + (xq < more ? 1 : 0);               // workgroups of group x
+  uint32_t* ctr = a.ws->tiles[h * qn + xq];
+  uint32_t base = 0;
+  __shared__ uint32_t grab;
   for (int step = a.step_begin; step < a.step_end; ++step) {
     const int64_t ntiles = (int64_t)step_segments(a, step) * a.T;
-    for (int64_t t = b; t < ntiles; t += nbh) {
+    auto move = [&](int64_t t) {
       const int seg = (int)(t / a.T);
       const int64_t j = t - (int64_t)seg * a.T;
       const Seg g = step_segment(a, step, seg);
@@ -545,6 +578,21 @@ __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
         hop_tile<DT, OP, U, true, NT>(a.P.b[g.src], a.P.b[g.dst], lo, hi, j, a.p, g.f);
       else
         hop_tile<DT, OP, U, false, NT>(a.P.b[g.src], a.P.b[g.dst], lo, hi, j, a.p, g.f);
+    };
+    if (ntiles < kHandOutTiles * (int64_t)nbh) {
+      for (int64_t t = b; t < ntiles; t += nbh) move(t);
+    } else {
+      const int64_t t0 = ntiles * w0 / nbh, t1 = ntiles * (w0 + wq) / nbh;
+      for (;;) {
+        if (threadIdx.x == 0)
+          grab = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - base;
+        __syncthreads();
+        const int64_t t = t0 + grab;
+        __syncthreads();              // every thread has read the grab
+        if (t >= t1) break;
+        move(t);
+      }
+      base += (uint32_t)(t1 - t0 + wq);
     }
     const bool last = step + 1 == a.step_end;
     if (!last || a.step_ts || extra) {
@@ -1012,6 +1060,22 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
            : a.channels % kXcds == 0 ? kSyncOneXcd : kSyncDevice;
   a.T = std::max<int64_t>(1, (widest(a.channels) + tv - 1) / tv);
   a.W = std::max<int64_t>(1, maxvec);
+  // tile counters per channel: one per XCD that the channel's workgroups run on
+  // (workgroup b*C + h on XCD (b*C + h) mod 8: 8 / gcd(C, 8) of them, taken in
+  // turn, so group b mod qn is one XCD), fewer when a channel has fewer
+  // workgroups (each group needs one) or the header's 64 counters would not hold
+  // them.  More groups than XCDs only split an XCD's tiles into more streams:
+  // eight channels with eight counters each took 92.5 ms at p = 8, 16 GB per
+  // rank, against 89.7 with one each.
+  const int spans = kXcds / std::gcd(a.channels, kXcds);
+  a.qn = std::max(1, std::min(std::min(spans, grid / a.channels), kMaxChannels / a.channels));
+  bool hand_out = false;
+  for (int st = step_begin; st < step_end; ++st)
+    hand_out = hand_out || (int64_t)nseg_of(st) * a.T >= kHandOutTiles * (grid / a.channels);
+  if (hand_out) {
+    e = launch_fill_u32(&sc.ws->tiles[0][0], 0u, (int64_t)a.channels * a.qn * 32, s);
+    if (e != hipSuccess) return e;
+  }
   *grid_used = grid;
   *launches = 1;
   return hipLaunchKernel(func, dim3(grid), dim3(kBlock), args, 0, s);

@@ -24,6 +24,8 @@ struct WsHeader {
                                      // (self-resetting, see grid_barrier)
   uint32_t xbar[kXcds][32];          // two-level barrier: arrivals of XCD group x
   uint32_t xflag[kXcds][32];         // two-level barrier: release count of XCD group x
+  uint32_t tiles[kMaxChannels][32];  // persistent step grids: tile counters that hand
+                                     // out a step's tiles in order (zeroed per launch)
 };
 
 // How workgroups that synchronise share the chip's caches.

@@ -352,14 +352,18 @@ def test_stream_copy():
 
 
 @pytest.mark.parametrize("nbytes,grid", [(16, 1), (16 << 10, 3), ((16 << 10) + 48, 7),
-                                         ((1 << 24) + 4096 + 16, 0), (1 << 26, 1000)])
+                                         ((1 << 24) + 4096 + 16, 0), (1 << 26, 1000),
+                                         ((1 << 22) + 80, 9), ((5 << 20) + 16, 13)])
 def test_stream_copy_resident(nbytes, grid):
-    # whole 16 KiB tiles on the resident grid, the vectors past them one per thread
+    # whole 16 KiB tiles handed out per XCD group (grids that 8 does not divide
+    # give the groups unequal shares), the vectors past them one per thread; a
+    # second, smaller call on the same stream starts from freshly zeroed counters
     require_gpu()
-    src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
-    dst = torch.zeros(nbytes // 4 + 64, dtype=torch.int32, device="cuda")
-    print(f"[case] resident copy bytes={nbytes} grid={grid}", flush=True)
-    B.ra_stream_copy_resident(dst, src, grid=grid)
-    torch.cuda.synchronize()
-    assert torch.equal(dst[: nbytes // 4], src)
-    assert not dst[nbytes // 4:].any()
+    for k, nb in enumerate((nbytes, max(16, nbytes // 2 // 16 * 16))):
+        src = torch.randint(-2**31, 2**31 - 1, (nb // 4,), dtype=torch.int32, device="cuda")
+        dst = torch.zeros(nb // 4 + 64, dtype=torch.int32, device="cuda")
+        print(f"[case] resident copy call {k} bytes={nb} grid={grid}", flush=True)
+        B.ra_stream_copy_resident(dst, src, grid=grid)
+        torch.cuda.synchronize()
+        assert torch.equal(dst[: nb // 4], src)
+        assert not dst[nb // 4:].any()
