@@ -131,16 +131,6 @@ constexpr int kStageV = kBlock * kStageU;
 // this wave are outstanding (gfx9 encoding; export and LDS counters left free).
 constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
-// One hop over the whole slice [lo, hi), staged through LDS and double-buffered
-// ("Ring All-Reduce, in depth", section "What real libraries add", pipelining:
-// the next piece is already arriving while this one is reduced and forwarded).
-// Stage t holds kStageV vectors of the incoming (src) and the receiving (dst)
-// chunk; while stage t is combined out of LDS and stored, stage t+1 is being
-// copied into the other LDS buffer by global_load_lds_dwordx4, which lands each
-// lane's 16 bytes at the wave's LDS base without passing through registers.
-// Every wave reads back only the LDS its own lanes filled, so the stages need
-// no workgroup barrier: a wave waits on its own memory counter.  Averages as in
-// hop_tile; the slice's unaligned head and tail go element by element.
 // 16-byte LDS reads that return only once the data is in registers.  The LDS
 // address is the low 32 bits of the generic address of a __shared__ object.
 __device__ __forceinline__ u32x4 lds_read(const u32x4* p) {

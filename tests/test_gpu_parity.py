@@ -190,6 +190,41 @@ def test_step_kernels_any_grid(algo, grid):
     check(xs, "bfloat16", algo, grid=grid)
 
 
+# Persistent grids take a large step's tiles (8 or more per workgroup) in order
+# from tile counters, one contiguous range per group of workgroups (one group per
+# XCD a channel runs on), and smaller steps in a fixed stride.  These shapes reach
+# the counters with 1, 2, 4 and 8 groups per channel, groups of unequal size
+# (grids that the group count does not divide), steps exactly at the threshold
+# (8 and 16 channels), and launches that mix both kinds of step (the tree's
+# levels hold 4, 2 and 1 pairs; the hierarchy's in-node and cross-node steps
+# differ in width).  A second, smaller call on the same stream starts from
+# freshly zeroed counters.
+HANDOUT = [("ring_step", {"grid": 40}), ("ring_step", {"grid": 44}), ("ring_step", {"grid": 6}),
+           ("ring_channels", {"channels": 2, "grid": 40}),
+           ("ring_channels", {"channels": 3, "grid": 45}),
+           ("ring_channels", {"channels": 5, "grid": 40}),
+           ("ring_channels", {"channels": 8, "grid": 64}),
+           ("ring_channels", {"channels": 16, "grid": 64}),
+           ("tree", {"grid": 100}), ("ring_bidir", {"grid": 24}), ("hier", {"group": 4, "grid": 56})]
+
+
+@pytest.mark.parametrize("algo,opts", HANDOUT)
+def test_persistent_tile_handout(algo, opts):
+    require_gpu()
+    for k, (p, n, dtype) in enumerate([(8, 4_000_003, "bfloat16"), (8, 1_000_037, "int32")]):
+        xs = inputs.make_inputs(p, n, dtype, seed=HANDOUT.index((algo, opts)) + 50 * k, sigma=1.0)
+        print(f"[case] tile hand-out call {k} algo={algo} {opts} p={p} n={n} {dtype}", flush=True)
+        got = run(xs, dtype, algo, **opts)
+        if algo == "hier":
+            want = oracle.hier_fold(xs, dtype, opts["group"])
+        elif algo == "ring_channels":
+            want = oracle.ring_fold(xs, dtype)
+        else:
+            want = expected(xs, dtype, algo)
+        for r, g in enumerate(got):
+            assert same_bits(g, want, dtype), f"call {k} rank {r} at {first_diff(g, want, dtype)}"
+
+
 def test_noop_cases():
     require_gpu()
     x = [torch.arange(10, dtype=torch.float32, device="cuda")]

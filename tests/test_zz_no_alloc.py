@@ -25,6 +25,7 @@ CASES = [  # (algo, options): every kind of workspace use, and none
     ("ring_step", {"grid": 64}), ("ring_step", {"grid": 1}), ("ring_channels", {}),
     ("ring_channels", {"channels": 3, "grid": 24}), ("tree", {"grid": 32}),
     ("ring_bidir", {"grid": 16}), ("hier", {"grid": 40, "group": 2}),
+    ("ring_step", {"grid": 4}), ("ring_channels", {"channels": 2, "grid": 4}),
     ("ring_step", {}), ("fused", {}), ("ring_pipelined", {}),
 ]
 
