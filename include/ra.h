@@ -149,8 +149,9 @@ typedef struct ra_options {
                            RING_PIPELINED_FLAGS: slice length in elements; 0 = library
                            default (about four slices per worker per hop, at least
                            64 KiB, but at least eight slices per chunk when they can be
-                           16 KiB or more), rounded up to a multiple of 16 bytes.  The
-                           result does not depend on it. */
+                           16 KiB or more), rounded up to whole 128-byte lines; every
+                           slice after a chunk's first starts on a line (counted from
+                           the buffer's start).  The result does not depend on it. */
   int64_t timeout_us;   /* budget of any single device-side wait; 0 = 10 s */
   int32_t grid;         /* step algorithms (RING_STEP, RING_BIDIR, TREE, HIER): 0 = the
                            library chooses (see RA_ALGO_RING_STEP).  1 with steps of at

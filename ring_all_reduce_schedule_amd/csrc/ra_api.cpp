@@ -406,8 +406,8 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
     int64_t slice = opt && opt->slice_elems > 0
                         ? opt->slice_elems
                         : ra::pipelined_default_slice(p, n, dtype, sc.grid);
-    const int64_t V = 16 / ra::elem_bytes(dtype);
-    slice = (slice + V - 1) / V * V;
+    const int64_t L = 16 / ra::elem_bytes(dtype) * ra::kLineVecs;   // whole 128-byte lines
+    slice = (slice + L - 1) / L * L;
     const int64_t kmax = ra::pipelined_slices_per_chunk(p, n, dtype, slice);
     uint32_t base = 0;
     rc = reserve_flags(w, kmax * p, s, opt && (opt->flags & RA_FLAG_RENEW_COUNTERS), &base);

@@ -12,6 +12,8 @@
 
 namespace ra {
 
+constexpr int kLineVecs = 8;              // 16-byte vectors per 128-byte cache line
+
 struct WsHeader;
 
 // Kernel families of the step-by-step schedule run by launch_steps().

@@ -643,10 +643,20 @@ struct PipeArgs {
 };
 
 // Slices of chunk [lo, hi): slice 0 starts at lo, later slices start at
-// A + k*slice with A = lo rounded up to a whole vector, the last ends at hi.
+// A + k*slice with A = lo rounded up to a whole 128-byte line (kLineVecs
+// vectors), the last ends at hi.  The slice length is a whole number of lines
+// too, so every slice after the first -- and every LDS stage in it -- starts on
+// a line.  A slice starting mid-line (measured with 3,906,256-byte slices, 80
+// bytes past a line) makes every 1 KiB wave access touch 9 lines instead of 8,
+// and the line two accesses share was fetched twice or written back in two
+// partial pieces: 7.9% more reads and 2.3% more writes than the schedule needs.
+__host__ __device__ __forceinline__ int64_t slice_origin(int64_t lo, int V) {
+  const int64_t L = (int64_t)V * kLineVecs;
+  return (lo + L - 1) / L * L;
+}
 template <int V>
 __device__ __forceinline__ int64_t n_slices(int64_t lo, int64_t hi, int64_t slice) {
-  const int64_t A = (lo + V - 1) / V * V;
+  const int64_t A = slice_origin(lo, V);
   if (A >= hi) return 1;
   const int64_t k = (hi - A + slice - 1) / slice;
   return k < 1 ? 1 : k;
@@ -681,7 +691,7 @@ __global__ __launch_bounds__(kBlock) void k_pipelined(PipeArgs a) {
     const int c = mod_p(rs ? d - 1 - s : d - s, p);
     const int64_t lo = chunk_lo(a.g, c), hi = chunk_hi(a.g, c);
     const int64_t K = n_slices<V>(lo, hi, a.slice);
-    const int64_t A = (lo + V - 1) / V * V;
+    const int64_t A = slice_origin(lo, V);
     const uint32_t done = a.base + (uint32_t)(h - a.hop_begin);
     for (int64_t k = w; k < K; k += a.workers) {
       uint32_t* f = a.flags + (int64_t)c * a.kmax + k;
@@ -1124,7 +1134,8 @@ int64_t pipelined_default_slice(int p, int64_t n, int dtype, int grid_override) 
   int64_t least = large;
   if ((chunk + small - 1) / small >= 8) least = std::max(small, std::min(large, chunk / 8));
   slice = std::max<int64_t>(slice, least);
-  return (slice + V - 1) / V * V;
+  const int64_t L = (int64_t)V * kLineVecs;
+  return (slice + L - 1) / L * L;
 }
 
 int64_t pipelined_slices_per_chunk(int p, int64_t n, int dtype, int64_t slice) {
@@ -1132,7 +1143,7 @@ int64_t pipelined_slices_per_chunk(int p, int64_t n, int dtype, int64_t slice) {
   int64_t kmax = 1;
   for (int c = 0; c < p; ++c) {
     const int64_t lo = host_chunk_lo(0, n, p, c), hi = host_chunk_lo(0, n, p, c + 1);
-    const int64_t A = (lo + V - 1) / V * V;
+    const int64_t A = slice_origin(lo, V);
     int64_t k = 1;
     if (A < hi) k = std::max<int64_t>(1, (hi - A + slice - 1) / slice);
     kmax = std::max(kmax, k);

@@ -70,9 +70,10 @@ def test_noalloc_matches_allreduce_ex_twice(algo, opts):
 def test_noalloc_refuses_more_counters_than_it_holds():
     require_gpu()
     _clear()
-    p, n = 8, 1 << 22
+    p, n = 8, 1 << 25
     t = [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
-    # 8-element slices: 65,536 per chunk, 524,288 counters
+    # slices of 8 elements round up to one 128-byte line (64 bfloat16): 65,536
+    # per chunk, 524,288 counters
     with pytest.raises(B.RaError) as e:
         B.ra_allreduce_noalloc(t, algo="ring_pipelined_flags", slice_elems=8)
     assert e.value.code == B.RA_ERR_UNSUPPORTED
