@@ -23,6 +23,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxRanks = 64;
 constexpr int kBlock = 256;               // threads per workgroup (4 wave64s)
+constexpr int kLineVecs = 8;              // 16-byte vectors per 128-byte cache line
 
 // Device pointers of the p rank buffers, passed by value in the kernel
 // arguments; a wave-uniform index into it compiles to a scalar load from the
@@ -531,8 +532,18 @@ __device__ __forceinline__ void store_all(const RankPtrs& P, int p, int64_t vt, 
 // Split [lo, hi) into a scalar head, whole 16-byte vectors, and a scalar tail.
 // All rank buffers start 16-byte aligned, so element i has the same alignment
 // in every buffer.
+// Tiles of a span count from vb, v0 rounded down to a 128-byte line (from the
+// buffer's start), so that every wave's 1 KiB access covers whole lines; the
+// vectors of the first tile below v0 belong to the span before and are left
+// alone.  Tiles counted from v0 instead start mid-line whenever the span does
+// (a chunk start that is not a multiple of 64 bfloat16), every access then
+// touches one line more and the line two tiles share is fetched twice or
+// written back in pieces: measured at p = 8 with 256 MiB of bfloat16 per rank,
+// the one-pass all-reduce took 826 us with chunk starts 6 bytes past a line
+// against 736 us with line-aligned ones.
 struct Span {
   int64_t v0, v1;       // vector indices [v0, v1)
+  int64_t vb;           // first vector of tile 0: v0 rounded down to a line
   int64_t head_hi;      // head = [lo, head_hi)
   int64_t tail_lo;      // tail = [tail_lo, hi)
 };
@@ -543,12 +554,13 @@ __device__ __forceinline__ Span split_span(int64_t lo, int64_t hi) {
   int64_t a0 = (lo + V - 1) / V * V;
   int64_t a1 = hi / V * V;
   if (a0 >= a1) {                 // no whole vector: all scalar
-    s.v0 = s.v1 = 0;
+    s.v0 = s.v1 = s.vb = 0;
     s.head_hi = hi;
     s.tail_lo = hi;
   } else {
     s.v0 = a0 / V;
     s.v1 = a1 / V;
+    s.vb = s.v0 / kLineVecs * kLineVecs;
     s.head_hi = a0;
     s.tail_lo = a1;
   }

@@ -12,8 +12,6 @@
 
 namespace ra {
 
-constexpr int kLineVecs = 8;              // 16-byte vectors per 128-byte cache line
-
 struct WsHeader;
 
 // Kernel families of the step-by-step schedule run by launch_steps().
@@ -112,6 +110,13 @@ inline int64_t vecs_in(int64_t lo, int64_t hi, int V) {
   int64_t a0 = (lo + V - 1) / V * V;
   int64_t a1 = hi / V * V;
   return a1 > a0 ? (a1 - a0) / V : 0;
+}
+
+// Vectors the tiles of [lo, hi) span, counted from the line their first tile
+// starts on (Span::vb): the whole vectors plus up to kLineVecs - 1 before them.
+inline int64_t tiled_vecs_in(int64_t lo, int64_t hi, int V) {
+  int64_t a0 = (lo + V - 1) / V, a1 = hi / V;
+  return a1 > a0 ? a1 - a0 / kLineVecs * kLineVecs : 0;
 }
 
 inline int64_t host_chunk_lo(int64_t off, int64_t len, int p, int c) {

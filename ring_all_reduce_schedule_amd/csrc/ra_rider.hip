@@ -75,22 +75,68 @@ __device__ __forceinline__ void ride_hops(u32x4& acc, const RankPtrs& P, int p, 
   }
 }
 
+// Element i of chunk c carried through its hops on its own (the chunks'
+// unaligned edges), as ride_hops does for a vector.
+template <int DT, int OP, int MODE>
+__device__ __forceinline__ void ride_element(const RankPtrs& P, int p, int c, int64_t i) {
+  typedef Elem<DT> E;
+  constexpr bool kDiv = OP == kAvg && MODE != kRideAllGather;
+  const int owner = c == 0 ? p - 1 : c - 1;
+  if (MODE == kRideAllGather) {
+    const typename E::S out = ld1<DT>(P.b[owner], i);
+    for (int r = 0; r < p; ++r)
+      if (r != owner) st1<DT>(P.b[r], i, out);
+    return;
+  }
+  typename E::S acc = ld1<DT>(P.b[c], i);
+  if (kDiv) {
+    acc = E::div1(acc, p);
+    if (MODE == kRideReduceScatter) st1<DT>(P.b[c], i, acc);
+  }
+  for (int h = 1; h < p; ++h) {
+    const int r = c + h < p ? c + h : c + h - p;
+    typename E::S x = ld1<DT>(P.b[r], i);
+    if (kDiv) x = E::div1(x, p);
+    acc = comb1<DT, OP>(acc, x);
+    st1<DT>(P.b[r], i, acc);
+  }
+  if (MODE == kRideAllReduce) {
+    asm volatile("" ::: "memory");
+    for (int r = 0; r < p; ++r)
+      if (r != owner) st1<DT>(P.b[r], i, acc);
+  }
+}
+
 // Slice q = (chunk c, slice k of that chunk): tiles k*tps .. (k+1)*tps - 1 of
 // the chunk, one 16-byte vector per thread per tile, carried through its hops
-// tile by tile.  The chunk's unaligned head and tail elements ride with slice
-// 0, one element per thread.  The partials of the reduce-scatter are written
-// before the all-gather overwrites them (a compiler barrier keeps those stores:
-// they are the step states, not dead stores).
+// tile by tile.  The partials of the reduce-scatter are written before the
+// all-gather overwrites them (a compiler barrier keeps those stores: they are
+// the step states, not dead stores).  When the chunks have unaligned edge
+// elements (edges = 1), workgroup 0 carries them all, element by element, while
+// the slices run (in each chunk's first slice they were a second chain of
+// round trips after its vectors).
 template <int DT, int OP, bool NT, int MODE>
 __global__ __launch_bounds__(kBlock) void k_rider(RankPtrs P, ChunkGeo g, int p, int64_t T,
                                                   int64_t tps, int64_t K, int64_t nslices,
-                                                  uint32_t stress) {
+                                                  int edges, uint32_t stress) {
   typedef Elem<DT> E;
   constexpr int V = E::V;
   constexpr bool kDiv = OP == kAvg && MODE != kRideAllGather;
   for (int64_t q = blockIdx.x; q < nslices; q += gridDim.x) {
-    const int c = (int)(q / K);
-    const int64_t k = q - (int64_t)c * K;
+    if (q < edges) {
+      constexpr int kPer = 2 * V - 2;
+      for (int e = threadIdx.x; e < p * kPer; e += kBlock) {
+        const int c = e / kPer, k = e - c * kPer;
+        const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
+        const Span sp = split_span<V>(lo, hi);
+        const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
+        if (k < nh + nt) ride_element<DT, OP, MODE>(P, p, c, k < nh ? lo + k : sp.tail_lo + (k - nh));
+      }
+      continue;
+    }
+    const int64_t qq = q - edges;
+    const int c = (int)(qq / K);
+    const int64_t k = qq - (int64_t)c * K;
     const int owner = c == 0 ? p - 1 : c - 1;
     const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
     const Span sp = split_span<V>(lo, hi);
@@ -98,8 +144,8 @@ __global__ __launch_bounds__(kBlock) void k_rider(RankPtrs P, ChunkGeo g, int p,
     const unsigned lane = threadIdx.x;
     stress_delay(stress, (uint32_t)q);
     for (int64_t j = k * tps; j < j1; ++j) {
-      const int64_t vt = sp.v0 + j * kBlock;        // the tile's first vector
-      if (vt + lane >= sp.v1) continue;
+      const int64_t vt = sp.vb + j * kBlock;        // the tile's first vector
+      if (vt + lane < sp.v0 || vt + lane >= sp.v1) continue;
       if (MODE == kRideAllGather) {
         const u32x4 out = ld16t<NT>(P.b[owner], vt, lane);
         store_all<NT>(P, p, vt, lane, out, owner);
@@ -117,36 +163,6 @@ __global__ __launch_bounds__(kBlock) void k_rider(RankPtrs P, ChunkGeo g, int p,
         store_all<NT>(P, p, vt, lane, acc, owner);
       }
     }
-    if (k == 0) {
-      const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
-      const int tt = threadIdx.x;
-      if (tt < nh + nt) {
-        const int64_t i = tt < nh ? lo + tt : sp.tail_lo + (tt - nh);
-        if (MODE == kRideAllGather) {
-          const typename E::S out = ld1<DT>(P.b[owner], i);
-          for (int r = 0; r < p; ++r)
-            if (r != owner) st1<DT>(P.b[r], i, out);
-        } else {
-          typename E::S acc = ld1<DT>(P.b[c], i);
-          if (kDiv) {
-            acc = E::div1(acc, p);
-            if (MODE == kRideReduceScatter) st1<DT>(P.b[c], i, acc);
-          }
-          for (int h = 1; h < p; ++h) {
-            const int r = c + h < p ? c + h : c + h - p;
-            typename E::S x = ld1<DT>(P.b[r], i);
-            if (kDiv) x = E::div1(x, p);
-            acc = comb1<DT, OP>(acc, x);
-            st1<DT>(P.b[r], i, acc);
-          }
-          if (MODE == kRideAllReduce) {
-            asm volatile("" ::: "memory");
-            for (int r = 0; r < p; ++r)
-              if (r != owner) st1<DT>(P.b[r], i, acc);
-          }
-        }
-      }
-    }
   }
 }
 
@@ -159,23 +175,25 @@ static hipError_t rider_launch(const RankPtrs& P, int p, int64_t n, int64_t slic
   const int V = Elem<DT>::V;
   const ChunkGeo g = make_geo(0, n, p);
   int64_t T = 1;
+  int edges = 0;
   for (int c = 0; c < p; ++c) {
     const int64_t lo = host_chunk_lo(0, n, p, c), hi = host_chunk_lo(0, n, p, c + 1);
-    T = std::max<int64_t>(T, (vecs_in(lo, hi, V) + kBlock - 1) / kBlock);
+    T = std::max<int64_t>(T, (tiled_vecs_in(lo, hi, V) + kBlock - 1) / kBlock);
+    if (hi > lo && (lo % V != 0 || hi % V != 0 || vecs_in(lo, hi, V) == 0)) edges = 1;
   }
   const int64_t tile_elems = (int64_t)kBlock * V;
   const int64_t tps = slice_elems > 0 ? std::max<int64_t>(1, (slice_elems + tile_elems - 1) / tile_elems)
                                       : 1;
   const int64_t K = (T + tps - 1) / tps;
-  const int64_t nslices = (int64_t)p * K;
+  const int64_t nslices = edges + (int64_t)p * K;
   const int grid = (int)std::min<int64_t>(nslices, kMaxGrid);
   *grid_used = grid;
   if (streaming(p, n, DT))
     hipLaunchKernelGGL((k_rider<DT, OP, true, MODE>), dim3(grid), dim3(kBlock), 0, s, P, g, p, T,
-                       tps, K, nslices, stress);
+                       tps, K, nslices, edges, stress);
   else
     hipLaunchKernelGGL((k_rider<DT, OP, false, MODE>), dim3(grid), dim3(kBlock), 0, s, P, g, p, T,
-                       tps, K, nslices, stress);
+                       tps, K, nslices, edges, stress);
   return hipGetLastError();
 }
 

@@ -50,20 +50,23 @@ struct HopFlags {
   bool div_src, div_dst, keep_src;
 };
 
-// The vectors [t0, t1) of one tile, U per thread.  GUARD = false: the tile is
-// whole (t1 - t0 = kBlock * U), so no access needs a bounds test and all 2U
-// loads issue back to back before the first wait; with per-access guards the
-// compiler splits them into separately waited branches.
+// The vectors of the tile that starts at vector t0, U per thread, that lie in
+// [tl, t1).  GUARD = false: the tile is whole (tl = t0, t1 - t0 = kBlock * U),
+// so no access needs a bounds test and all 2U loads issue back to back before
+// the first wait; with per-access guards the compiler splits them into
+// separately waited branches.
 template <int DT, int OP, int U, bool ADD, bool NT, bool GUARD>
 __device__ __forceinline__ void hop_vectors(void* __restrict__ src, void* __restrict__ dst,
-                                            int64_t t0, int64_t t1, int p, HopFlags f) {
+                                            int64_t t0, int64_t tl, int64_t t1, int p, HopFlags f) {
   constexpr bool kDiv = OP == kAvg && ADD;
   int64_t v[U];
+  bool in[U];
   u32x4 a[U], b[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     v[u] = t0 + u * kBlock + threadIdx.x;
-    if (!GUARD || v[u] < t1) {
+    in[u] = !GUARD || (v[u] >= tl && v[u] < t1);
+    if (in[u]) {
       a[u] = ld16<NT>(src, v[u]);
       if (ADD) b[u] = ld16<NT>(dst, v[u]);
     }
@@ -77,11 +80,11 @@ __device__ __forceinline__ void hop_vectors(void* __restrict__ src, void* __rest
   }
 #pragma unroll
   for (int u = 0; u < U; ++u)
-    if (!GUARD || v[u] < t1) st16<NT>(dst, v[u], ADD ? vcomb<DT, OP>(b[u], a[u]) : a[u]);
+    if (in[u]) st16<NT>(dst, v[u], ADD ? vcomb<DT, OP>(b[u], a[u]) : a[u]);
   if (kDiv && f.keep_src) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (!GUARD || v[u] < t1) st16<NT>(src, v[u], a[u]);
+      if (in[u]) st16<NT>(src, v[u], a[u]);
   }
 }
 
@@ -93,29 +96,35 @@ __device__ __forceinline__ void hop_tile(void* __restrict__ src, void* __restric
   constexpr bool kDiv = OP == kAvg && ADD;
   const Span sp = split_span<V>(lo, hi);
   const int64_t tv = (int64_t)kBlock * U;
-  const int64_t t0 = sp.v0 + j * tv;
+  const int64_t t0 = sp.vb + j * tv;               // tiles start on lines (Span)
+  const int64_t tl = t0 > sp.v0 ? t0 : sp.v0;
   const int64_t t1 = t0 + tv < sp.v1 ? t0 + tv : sp.v1;
-  if (t1 - t0 == tv)        // the same for the whole workgroup
-    hop_vectors<DT, OP, U, ADD, NT, false>(src, dst, t0, t1, p, f);
-  else if (t0 < t1)
-    hop_vectors<DT, OP, U, ADD, NT, true>(src, dst, t0, t1, p, f);
-  if (j == 0) {
-    const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
-    const int t = threadIdx.x;
-    if (t < nh + nt) {
-      const int64_t i = t < nh ? lo + t : sp.tail_lo + (t - nh);
-      typename E::S x = ld1<DT>(src, i);
-      if (ADD) {
-        typename E::S y = ld1<DT>(dst, i);
-        if (kDiv) {
-          if (f.div_src) x = E::div1(x, p);
-          if (f.div_dst) y = E::div1(y, p);
-        }
-        st1<DT>(dst, i, comb1<DT, OP>(y, x));
-        if (kDiv && f.keep_src) st1<DT>(src, i, x);
-      } else {
-        st1<DT>(dst, i, x);
+  // Tile 0 also takes the segment's edge elements.  Their loads go out before
+  // the vectors' (the two sets of addresses are disjoint), so that their round
+  // trip overlaps the vectors' instead of following it.
+  const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
+  const int t = threadIdx.x;
+  const bool edge = j == 0 && t < nh + nt;
+  const int64_t i = t < nh ? lo + t : sp.tail_lo + (t - nh);
+  typename E::S x = 0, y = 0;
+  if (edge) {
+    x = ld1<DT>(src, i);
+    if (ADD) y = ld1<DT>(dst, i);
+  }
+  if (tl == t0 && t1 - t0 == tv)        // the same for the whole workgroup
+    hop_vectors<DT, OP, U, ADD, NT, false>(src, dst, t0, tl, t1, p, f);
+  else if (tl < t1)
+    hop_vectors<DT, OP, U, ADD, NT, true>(src, dst, t0, tl, t1, p, f);
+  if (edge) {
+    if (ADD) {
+      if (kDiv) {
+        if (f.div_src) x = E::div1(x, p);
+        if (f.div_dst) y = E::div1(y, p);
       }
+      st1<DT>(dst, i, comb1<DT, OP>(y, x));
+      if (kDiv && f.keep_src) st1<DT>(src, i, x);
+    } else {
+      st1<DT>(dst, i, x);
     }
   }
 }
@@ -145,17 +154,18 @@ __device__ __forceinline__ void lds_read2(const u32x4* p, const u32x4* q, u32x4&
                : "=&v"(x), "=&v"(y) : "v"(a), "v"(b) : "memory");
 }
 
-// Issue the asynchronous copies of stage t into one LDS buffer (src and dst halves).
+// Issue the asynchronous copies of the stage that starts at vector v0 into one
+// LDS buffer (src and dst halves): the vectors of [vl, v1) among its kStageV.
 template <bool ADD, bool NT>
-__device__ __forceinline__ void stage_fill(const u32x4* gsrc, const u32x4* gdst, int64_t v0,
-                                           int64_t v1, u32x4* __restrict__ lsrc,
+__device__ __forceinline__ void stage_fill(const u32x4* gsrc, const u32x4* gdst, int64_t vl,
+                                           int64_t v0, int64_t v1, u32x4* __restrict__ lsrc,
                                            u32x4* __restrict__ ldst) {
   const int wave = threadIdx.x / 64;
 #pragma unroll
   for (int u = 0; u < kStageU; ++u) {
     const int64_t v = v0 + u * kBlock + threadIdx.x;
     const int base = u * kBlock + wave * 64;           // this wave's 64 slots
-    if (v < v1) {
+    if (v >= vl && v < v1) {
       __builtin_amdgcn_global_load_lds(gsrc + v, lsrc + base, 16, 0, NT ? kNtPolicy : 0);
       if (ADD) __builtin_amdgcn_global_load_lds(gdst + v, ldst + base, 16, 0, NT ? kNtPolicy : 0);
     }
@@ -171,17 +181,18 @@ __device__ __forceinline__ void stage_fill(const u32x4* gsrc, const u32x4* gdst,
 // loop's back edge), and the double buffering was lost there: measured 10-14%
 // slower at 4-16 MiB per rank.  Each read waits for its own LDS result
 // (lgkmcnt) before returning, so no later copy into the same buffer can
-// overtake it.
+// overtake it.  Vectors below vl (the slice's first, when its stages start on
+// the line before it) are skipped; only the first stage has any.
 template <int DT, int OP, bool ADD, bool NT>
-__device__ __forceinline__ void stage_step(void* src, void* dst, int64_t v0, int64_t v1,
-                                           int64_t n0, int64_t n1, int p, HopFlags f,
+__device__ __forceinline__ void stage_step(void* src, void* dst, int64_t vl, int64_t v0,
+                                           int64_t v1, int64_t n0, int64_t n1, int p, HopFlags f,
                                            u32x4* __restrict__ cur_src, u32x4* __restrict__ cur_dst,
                                            u32x4* __restrict__ nxt_src, u32x4* __restrict__ nxt_dst) {
   constexpr bool kDiv = OP == kAvg && ADD;
   constexpr int kLoads = ADD ? 2 * kStageU : kStageU;    // copies per thread per stage
   if (n0 < n1) {
     stage_fill<ADD, NT>(reinterpret_cast<const u32x4*>(src), reinterpret_cast<const u32x4*>(dst),
-                        n0, n1, nxt_src, nxt_dst);
+                        vl, n0, n1, nxt_src, nxt_dst);
     // The current stage has landed once no more than the next stage's copies are
     // outstanding -- but only if this wave issued all kLoads of them.  A short
     // next stage (the slice's last) leaves some waves with fewer or none, and
@@ -197,7 +208,7 @@ __device__ __forceinline__ void stage_step(void* src, void* dst, int64_t v0, int
 #pragma unroll
   for (int u = 0; u < kStageU; ++u) {
     const int64_t v = v0 + u * kBlock + threadIdx.x;
-    if (v < v1) {
+    if (v >= vl && v < v1) {
       const int i = u * kBlock + threadIdx.x;
       u32x4 a, y;
       if (ADD)
@@ -236,20 +247,22 @@ __device__ __forceinline__ void hop_slice_lds(void* __restrict__ src, void* __re
   constexpr int V = E::V;
   constexpr bool kDiv = OP == kAvg && ADD;
   const Span sp = split_span<V>(lo, hi);
-  const int64_t nst = (sp.v1 - sp.v0 + kStageV - 1) / kStageV;
-  auto first = [&](int64_t t) { return sp.v0 + t * kStageV; };
+  // stages start on lines (Span): stage t is [vb + t*kStageV, ...) within [v0, v1)
+  const int64_t nst = sp.v1 > sp.v0 ? (sp.v1 - sp.vb + kStageV - 1) / kStageV : 0;
+  auto first = [&](int64_t t) { return sp.vb + t * kStageV; };
   auto last = [&](int64_t t) { return first(t) + kStageV < sp.v1 ? first(t) + kStageV : sp.v1; };
+  const int64_t vl = sp.v0;
   if (nst > 0)
     stage_fill<ADD, NT>(reinterpret_cast<const u32x4*>(src), reinterpret_cast<const u32x4*>(dst),
-                        first(0), last(0), stage[0][0], stage[0][1]);
+                        vl, first(0), last(0), stage[0][0], stage[0][1]);
   // stages alternate between buffer 0 and 1: two steps per trip so that each
   // step names its current and next buffer explicitly
   for (int64_t t = 0; t < nst; t += 2) {
-    stage_step<DT, OP, ADD, NT>(src, dst, first(t), last(t), first(t + 1),
+    stage_step<DT, OP, ADD, NT>(src, dst, vl, first(t), last(t), first(t + 1),
                                 t + 1 < nst ? last(t + 1) : first(t + 1), p, f,
                                 stage[0][0], stage[0][1], stage[1][0], stage[1][1]);
     if (t + 1 < nst)
-      stage_step<DT, OP, ADD, NT>(src, dst, first(t + 1), last(t + 1), first(t + 2),
+      stage_step<DT, OP, ADD, NT>(src, dst, vl, first(t + 1), last(t + 1), first(t + 2),
                                   t + 2 < nst ? last(t + 2) : first(t + 2), p, f,
                                   stage[1][0], stage[1][1], stage[0][0], stage[0][1]);
   }
@@ -929,26 +942,27 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   if (mode == kModeHier) {
     for (int c = 0; c < a.g; ++c) {
       const int64_t lo = host_chunk_lo(0, n, a.g, c), hi = host_chunk_lo(0, n, a.g, c + 1);
-      hier_intra = std::max(hier_intra, vecs_in(lo, hi, V));
+      hier_intra = std::max(hier_intra, tiled_vecs_in(lo, hi, V));
       for (int d = 0; d < a.m; ++d)
-        hier_inter = std::max(hier_inter, vecs_in(host_chunk_lo(lo, hi - lo, a.m, d),
-                                                  host_chunk_lo(lo, hi - lo, a.m, d + 1), V));
+        hier_inter = std::max(hier_inter, tiled_vecs_in(host_chunk_lo(lo, hi - lo, a.m, d),
+                                                        host_chunk_lo(lo, hi - lo, a.m, d + 1), V));
     }
   }
   // whole vectors of the widest part of any range cut C ways (the kernel's rule:
-  // part h of [lo, hi) starts at lo + h*floor(len/C) + min(h, len mod C))
-  auto widest = [&](int C) {
+  // part h of [lo, hi) starts at lo + h*floor(len/C) + min(h, len mod C)); tiled:
+  // counted from the line its first tile starts on, what the tile count needs
+  auto widest = [&](int C, bool tiled) {
     int64_t w = 0;
     for_each_range([&](int64_t first, int64_t last) {
       const int64_t len = last - first, q = len / C, rem = len % C;
       for (int h = 0; h < C; ++h) {
-        const int64_t lo = first + h * q + std::min<int64_t>(h, rem);
-        w = std::max(w, vecs_in(lo, lo + q + (h < rem ? 1 : 0), V));
+        const int64_t lo = first + h * q + std::min<int64_t>(h, rem), hi = lo + q + (h < rem ? 1 : 0);
+        w = std::max(w, tiled ? tiled_vecs_in(lo, hi, V) : vecs_in(lo, hi, V));
       }
     });
     return w;
   };
-  const int64_t maxvec = widest(1);
+  const int64_t maxvec = widest(1, false), maxtiled = widest(1, true);
   // segments (independent chunk transfers) of step st, as step_segments counts them
   auto nseg_of = [&](int st) {
     if (mode == kModeHier) return p;
@@ -987,7 +1001,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
     for (int st = step_begin; st < step_end; ++st) {
       // tiles per segment for this step's widest segment (the hierarchy's
       // cross-node steps move pieces m times smaller than its in-node steps)
-      int64_t w = maxvec;
+      int64_t w = maxtiled;
       if (mode == kModeHier)
         w = st < a.g - 1 || st >= a.g - 1 + 2 * (a.m - 1) ? hier_intra : hier_inter;
       const bool two = w >= kCopyU2Vecs && step_copies(mode, st, p, a.levels, a.g, a.m);
@@ -1039,7 +1053,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   const int64_t tv = (int64_t)kBlock * kStepU;
   // no more workgroups than whole-segment tiles: on small buffers every extra
   // workgroup only adds to each barrier's cost
-  const int64_t most = (int64_t)most_seg * std::max<int64_t>(1, (maxvec + tv - 1) / tv);
+  const int64_t most = (int64_t)most_seg * std::max<int64_t>(1, (maxtiled + tv - 1) / tv);
   grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, most));
   // channels share that grid, the same number of workgroups each, at least one.
   // Unspecified (0): 8, one per XCD (each channel then lives in one XCD's L2 and
@@ -1058,7 +1072,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   a.sync = !placed ? kSyncDevice
            : a.channels == 1 ? (grid >= kTwoLevelMinGrid ? kSyncXcdGroups : kSyncDevice)
            : a.channels % kXcds == 0 ? kSyncOneXcd : kSyncDevice;
-  a.T = std::max<int64_t>(1, (widest(a.channels) + tv - 1) / tv);
+  a.T = std::max<int64_t>(1, (widest(a.channels, true) + tv - 1) / tv);
   a.W = std::max<int64_t>(1, maxvec);
   // tile counters per channel: one per XCD that the channel's workgroups run on
   // (workgroup b*C + h on XCD (b*C + h) mod 8: 8 / gcd(C, 8) of them, taken in
