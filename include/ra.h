@@ -310,9 +310,10 @@ int ra_allreduce_noalloc(void* const* bufs, int p, int64_t n, int dtype, int op,
  *   Otherwise (no link model): RA_ALGO_FUSED.  Over buffers that share one GPU's
  *   memory it moves the least data (2pS bytes), and on MI355X it was the fastest
  *   all-reduce, or tied with the fastest, at every size from 1 KiB to 64 MiB per rank
- *   and every p from 2 to 64 measured: where another algorithm's median beat it, it did
- *   so by 0.1-2 us at the launch floor (about 6 us per call), and the winner changed
- *   from run to run.
+ *   and every p from 2 to 64 measured: where another algorithm's median beat it (the
+ *   slice-carrying pipelined ring, whose partial writes partly merge in the caches),
+ *   it did so by 0.1-2 us, mostly at the launch floor (about 6 us per call), and the
+ *   sizes where it happened changed from run to run.
  * Writes the ra_algo value to *algo_out.  Host only, no GPU needed.
  * RA_ERR_INVALID_ARG for p < 1, n < 0, an unknown dtype, NULL algo_out, or a
  * negative or non-finite link parameter; RA_ERR_UNSUPPORTED for p > RA_MAX_RANKS.
