@@ -45,15 +45,23 @@
  *  flag-driven pipelined and channel algorithms, and the step algorithms when
  *  ra_options.grid or step_ts is set, run persistent grids: ordinary launches
  *  whose workgroups wait for each other, so all of them must be resident at
- *  once.  Such a grid is sized to what the GPU can hold of it (by default 4
- *  workgroups per compute unit), so overlapping such calls should each set
- *  ra_options.grid to their share; a call that cannot get all its workgroups
- *  resident times out (RA_ERR_TIMEOUT from ra_stream_status) instead of
- *  hanging.  The one-pass algorithms (FUSED, HIER_FUSED), the pipelined ring
+ *  once.  Such a grid is sized to what the GPU can hold of it (by default 5
+ *  workgroups per compute unit, 4 for RING_PIPELINED_FLAGS, whose LDS stages
+ *  allow no more), so overlapping such calls should each set ra_options.grid
+ *  to their share; a call that cannot get all its workgroups resident times
+ *  out (RA_ERR_TIMEOUT from ra_stream_status) instead of hanging.
+ *
+ *  HIP graphs.  The one-pass algorithms (FUSED, HIER_FUSED), the pipelined ring
  *  (RING_PIPELINED) and the step algorithms' default launches (one per step,
- *  or one workgroup) are grids with no device-side waits, and can be captured
- *  in a HIP graph; RING_PIPELINED_FLAGS cannot (its ready counters are
- *  numbered per call on the host).
+ *  or one workgroup) are grids with no device-side waits and no workspace, and
+ *  can be captured on any stream.  Calls that run persistent grids can be
+ *  captured on a stream that has made such a call before (its workspace is
+ *  allocated then, and cannot be during capture: RA_ERR_UNSUPPORTED); their
+ *  counters are reset by kernels that the graph holds, and a captured
+ *  RING_PIPELINED_FLAGS call numbers its ready counters from 0 after zeroing
+ *  them, so replays and eager calls may alternate on the stream.  A replay uses
+ *  the capturing stream's workspace: it must not overlap other calls of that
+ *  stream.
  *
  * Return codes are ra_status values; ra_status_string() names them and
  * ra_last_error() gives the calling thread's last error message.

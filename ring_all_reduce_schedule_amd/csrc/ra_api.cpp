@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <vector>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -184,7 +185,15 @@ struct Workspace {
   uint32_t epoch = 0;              // pipelined calls so far (flag base = epoch * kFlagStride)
   bool fixed = false;              // the device's no-alloc scratch: never reallocated, reset
                                    // by fill kernels on the calling stream
+  bool captured = false;           // a HIP graph holds `flags`: never freed from then on
+  std::vector<void*> retired;      // counter buffers replaced after a capture (kept alive)
 };
+
+// Whether work enqueued on s is being captured into a HIP graph.
+bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
+}
 
 constexpr uint32_t kFlagStride = 128;   // > 2(p-1) hops for p <= 64
 
@@ -197,6 +206,10 @@ int get_workspace(hipStream_t s, Workspace** out) {
   if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
   std::lock_guard<std::mutex> lock(g_ws_mu);
   Workspace& w = g_ws[{dev, s}];
+  if (!w.hdr && stream_capturing(s))
+    return fail(RA_ERR_UNSUPPORTED,
+                "this call needs the stream's workspace, which the first such call on a stream "
+                "allocates: make one outside graph capture first");
   if (!w.hdr) {
     void* p = nullptr;
     e = hipMalloc(&p, sizeof(ra::WsHeader));
@@ -234,12 +247,17 @@ int reserve_flags(Workspace* w, int64_t entries, hipStream_t s, bool renew, uint
   if (renew) w->epoch = (1u << 31) / kFlagStride - 1;
   if (entries > w->flag_cap || (renew && w->flags)) {
     if (w->flags) {
-      // the old counters may still be read by queued work on this stream
+      // the old counters may still be read by queued work on this stream, or by
+      // a captured graph (those are kept until the process ends)
       hipError_t e = hipStreamSynchronize(s);
       if (e != hipSuccess) return fail_hip(e, "hipStreamSynchronize");
-      (void)hipFree(w->flags);
+      if (w->captured)
+        w->retired.push_back(w->flags);
+      else
+        (void)hipFree(w->flags);
       w->flags = nullptr;
       w->flag_cap = 0;
+      w->captured = false;
     }
     const int64_t cap = std::max<int64_t>(entries, 4096);
     void* p = nullptr;
@@ -259,6 +277,22 @@ int reserve_flags(Workspace* w, int64_t entries, hipStream_t s, bool renew, uint
     w->epoch = 1;
   }
   *base = w->epoch * kFlagStride;
+  return RA_OK;
+}
+
+// The ready counters of a call being captured into a HIP graph: the buffer must
+// already hold `entries` (it cannot be allocated, nor an old one freed, during
+// capture), is kept alive from now on, and is zeroed by a captured fill kernel.
+int capture_flags(Workspace* w, int64_t entries, hipStream_t s) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if (entries > w->flag_cap)
+    return fail(RA_ERR_UNSUPPORTED,
+                "under graph capture the stream's ready counters cannot grow: the call needs "
+                "%lld, the stream holds %lld (make the same call once outside capture first)",
+                (long long)entries, (long long)w->flag_cap);
+  if (!w->fixed) w->captured = true;
+  hipError_t e = ra::launch_fill_u32(w->flags, 0u, entries, s);
+  if (e != hipSuccess) return fail_hip(e, "zeroing ready counters");
   return RA_OK;
 }
 
@@ -320,7 +354,7 @@ bool needs_workspace(int algo, const ra_options* opt) {
                  (opt->flags & (RA_FLAG_FORCE_TIMEOUT | RA_FLAG_STRESS)) != 0);
 }
 
-int sync_cfg(const ra_options* opt, Workspace* w, ra::SyncCfg* sc) {
+int sync_cfg(const ra_options* opt, Workspace* w, hipStream_t s, ra::SyncCfg* sc) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
@@ -338,7 +372,9 @@ int sync_cfg(const ra_options* opt, Workspace* w, ra::SyncCfg* sc) {
   sc->grid = opt && opt->grid > 0 ? opt->grid : 0;
   sc->channels = 1;
   sc->group = 1;
-  sc->may_probe = !(w && w->fixed);
+  // the placement probe allocates and copies: not in a call that must not
+  // allocate, nor under graph capture
+  sc->may_probe = !(w && w->fixed) && !stream_capturing(s);
   return RA_OK;
 }
 
@@ -380,7 +416,7 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
     ra::RankPtrs P;
     fill_ptrs(bufs, p, &P);
     ra::SyncCfg sc;
-    int rc = sync_cfg(opt, nullptr, &sc);
+    int rc = sync_cfg(opt, nullptr, s, &sc);
     if (rc != RA_OK) return rc;
     int grid = 0;
     hipError_t e = ra::launch_rider(P, p, n, dtype, op, mode, opt ? opt->slice_elems : 0, sc.stress,
@@ -396,7 +432,7 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
     if (rc != RA_OK) return rc;
   }
   ra::SyncCfg sc;
-  rc = sync_cfg(opt, w, &sc);
+  rc = sync_cfg(opt, w, s, &sc);
   if (rc != RA_OK) return rc;
   ra::RankPtrs P;
   fill_ptrs(bufs, p, &P);
@@ -410,8 +446,18 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
     slice = (slice + L - 1) / L * L;
     const int64_t kmax = ra::pipelined_slices_per_chunk(p, n, dtype, slice);
     uint32_t base = 0;
-    rc = reserve_flags(w, kmax * p, s, opt && (opt->flags & RA_FLAG_RENEW_COUNTERS), &base);
-    if (rc != RA_OK) return rc;
+    if (stream_capturing(s)) {
+      // Under HIP graph capture the call cannot take a number from the host:
+      // every replay would reuse it, and the counters its last replay left would
+      // read as already reached.  It zeroes the counters with a fill kernel (a
+      // node of the graph) and numbers itself from 0.  Eager calls number from
+      // 128 up, above anything a replay leaves (at most 2(p-1)), so the two mix.
+      rc = capture_flags(w, kmax * p, s);
+      if (rc != RA_OK) return rc;
+    } else {
+      rc = reserve_flags(w, kmax * p, s, opt && (opt->flags & RA_FLAG_RENEW_COUNTERS), &base);
+      if (rc != RA_OK) return rc;
+    }
     e = ra::launch_pipelined(P, p, n, dtype, op, hop_begin, hop_end, slice, kmax, w->flags, base,
                              sc, s, &grid);
   } else {
@@ -462,7 +508,7 @@ int allreduce_impl(void* const* bufs, int p, int64_t n, int dtype, int op, int a
     if (rc != RA_OK) return rc;
   }
   ra::SyncCfg sc;
-  rc = sync_cfg(opt, w, &sc);
+  rc = sync_cfg(opt, w, stream, &sc);
   if (rc != RA_OK) return rc;
   ra::RankPtrs P;
   fill_ptrs(bufs, p, &P);

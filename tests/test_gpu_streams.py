@@ -11,6 +11,10 @@
   kernels with no workspace, so they can be captured into a HIP graph -- on a
   stream that has never run a call; every replay (with eager work and
   synchronisation in between) must equal the eager result.
+* Persistent grids (a caller's grid, channels, the flag-driven pipelined ring)
+  are captured on a stream that has made such a call; replays alternate with
+  eager flag-driven calls on the same stream.  Capturing one on a stream with no
+  workspace fails cleanly.
 """
 
 import numpy as np
@@ -122,3 +126,79 @@ def test_graph_capture_and_replay(call):
         torch.cuda.synchronize()
         for r, got in enumerate(from_dev(bufs, dtype)):
             assert same_bits(got, eager[r], dtype), f"replay {k} rank {r} at {first_diff(got, eager[r], dtype)}"
+
+
+# Calls that run persistent grids use the stream's workspace (barrier words, tile
+# counters, ready counters), so the stream must have made such a call once before
+# capture; the flag-driven ring, captured, zeroes its ready counters with a
+# captured fill kernel and numbers itself from 0, while eager calls keep numbering
+# from 128 up.  Replays alternate with eager calls of the same kind on the same
+# stream, and each must equal the eager result.
+PERSISTENT_CALLS = {"allreduce_ring_pipelined_flags": ("ring_pipelined_flags", {}),
+                    "allreduce_ring_pipelined_flags_small_slices":
+                        ("ring_pipelined_flags", {"slice_elems": 2048, "grid": 64}),
+                    "allreduce_ring_channels": ("ring_channels", {"channels": 8}),
+                    "allreduce_ring_step_grid": ("ring_step", {"grid": 40}),
+                    "allreduce_tree_grid": ("tree", {"grid": 48})}
+
+
+@pytest.mark.parametrize("call", list(PERSISTENT_CALLS) + ["rs_then_ag_ring_pipelined_flags"])
+def test_graph_capture_persistent_grids(call):
+    require_gpu()
+    p, n, dtype = 8, 1_000_003, "bfloat16"
+    xs = inputs.make_inputs(p, n, dtype, seed=11)
+    src = to_dev(xs, dtype)
+    bufs = [torch.empty_like(s) for s in src]
+    other = to_dev(inputs.make_inputs(p, 300_007, dtype, seed=12), dtype)
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+
+    def run():
+        if call == "rs_then_ag_ring_pipelined_flags":
+            B.ra_reduce_scatter_ex(bufs, algo="ring_pipelined_flags")
+            B.ra_all_gather_ex(bufs, algo="ring_pipelined_flags")
+        else:
+            algo, opts = PERSISTENT_CALLS[call]
+            B.ra_allreduce_ex(bufs, algo=algo, **opts)
+
+    algo = "tree" if call == "allreduce_tree_grid" else "ring"
+    want = oracle.tree_allreduce(xs, dtype)[0][0] if algo == "tree" else oracle.ring_fold(xs, dtype)
+    with torch.cuda.stream(cap):
+        for b, s in zip(bufs, src):
+            b.copy_(s)
+        run()                                   # eager, on the capture stream
+        B.ra_stream_status(stream=cap)
+    eager = from_dev(bufs, dtype)
+    assert all(same_bits(e, want, dtype) for e in eager)
+    g = torch.cuda.CUDAGraph()
+    print(f"[case] graph capture {call}", flush=True)
+    with torch.cuda.graph(g, stream=cap):
+        run()
+    torch.cuda.synchronize()
+    for k in range(4):
+        with torch.cuda.stream(cap):
+            # an eager flag-driven call on the same stream between replays
+            B.ra_allreduce_ex(other, algo="ring_pipelined_flags")
+            for b, s in zip(bufs, src):
+                b.copy_(s)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        B.ra_stream_status(stream=cap)
+        for r, got in enumerate(from_dev(bufs, dtype)):
+            assert same_bits(got, eager[r], dtype), f"replay {k} rank {r} at {first_diff(got, eager[r], dtype)}"
+
+
+def test_graph_capture_needs_the_streams_workspace():
+    """A persistent-grid call captured on a stream that never made one cannot
+    allocate its workspace during capture: it fails before enqueueing anything."""
+    require_gpu()
+    bufs = to_dev(inputs.make_inputs(8, 100_003, "float32", seed=13), "float32")
+    fresh = torch.cuda.Stream()
+    fresh.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(B.RaError) as e:
+        with torch.cuda.graph(g, stream=fresh):
+            B.ra_allreduce_ex(bufs, algo="ring_pipelined_flags")
+    assert e.value.code == B.RA_ERR_UNSUPPORTED
+    torch.cuda.synchronize()

@@ -125,7 +125,8 @@ def test_noalloc_timeout_is_sticky_until_reported():
 
 
 @pytest.mark.parametrize("algo,opts", [("ring_step", {"grid": 64}), ("fused", {}),
-                                       ("ring_pipelined", {})])
+                                       ("ring_pipelined", {}), ("ring_pipelined_flags", {}),
+                                       ("ring_channels", {"channels": 8, "grid": 64})])
 def test_noalloc_in_a_hip_graph(algo, opts):
     """Captured once, replayed three times with eager work and synchronisation
     between the replays; the maximum is idempotent, so every replay must give
