@@ -45,9 +45,7 @@ __global__ __launch_bounds__(kBlock) void k_copy_resident(u32x4* __restrict__ ds
     if (t >= t1) break;
     const int64_t base = t * kBlock * U + threadIdx.x;
     u32x4 x[U];
-#pragma unroll
     for (int u = 0; u < U; ++u) x[u] = ld16<true>(src, base + u * kBlock);
-#pragma unroll
     for (int u = 0; u < U; ++u) st16<true>(dst, base + u * kBlock, x[u]);
   }
   for (int64_t v = tiles * kBlock * U + b * kBlock + threadIdx.x; v < nvec; v += nb * kBlock)
