@@ -306,6 +306,8 @@ struct StepArgs {
   int g, m;             // hier: ranks per node, nodes (half[0] = the g-way intra partition)
   int sync;             // SyncScope of the barriers between steps
   int qn;               // persistent grid: tile counters (workgroup groups) per channel
+  int handout;          // persistent grid: the parts fill whole tiles (tile counters may pay)
+  int edges;            // one workgroup: some segment has elements outside whole vectors
   uint32_t expect_extra;
   uint32_t stress;      // test hook: delays before arrivals (stress_delay)
 };
@@ -487,7 +489,13 @@ __device__ __forceinline__ void block_step(const StepArgs& a, const RankPtrs& P,
       st16<NT>(P.b[g[u].dst], v[u], o);
     }
   }
-  const int etotal = nseg * E2;
+  // edge elements: only when some segment has them.  With every chunk on whole
+  // vectors, working out the geometry of p*E2 empty items was most of a step's
+  // time on one workgroup (one wave per SIMD, nothing to hide latency behind):
+  // p = 64 with 1 KiB per rank took 2.6 us per step with it and 1.0 without.
+  // (Copying all ranks into LDS and running the steps there gained nothing:
+  // the plain pointer accesses reach LDS through the vector-memory path.)
+  const int etotal = a.edges ? nseg * E2 : 0;
   for (int f = (int)threadIdx.x; f < etotal; f += kBlock) {
     const int seg = f / E2;
     const int e = f - seg * E2;
@@ -542,8 +550,9 @@ __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
   uint32_t* bar = a.ws->bar[h];
   const bool leader = b == 0;
   uint32_t extra = a.expect_extra;
-  // Steps with at least kHandOutTiles tiles per workgroup hand their tiles out
-  // in order from tile counters, one tile per grab.  The channel's workgroups
+  // Steps with at least kHandOutTiles tiles per workgroup, on parts that fill
+  // whole tiles (a.handout), hand their tiles out in order from tile counters,
+  // one tile per grab.  The channel's workgroups
   // form qn groups (group x = b mod qn; with one channel, group x is XCD x,
   // since workgroup b runs on XCD b mod 8), and group x takes a contiguous range
   // of the step's tiles, sized to its share of the channel's workgroups, from a
@@ -582,7 +591,7 @@ __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
       else
         hop_tile<DT, OP, U, false, NT>(a.P.b[g.src], a.P.b[g.dst], lo, hi, j, a.p, g.f);
     };
-    if (ntiles < kHandOutTiles * (int64_t)nbh) {
+    if (!a.handout || ntiles < kHandOutTiles * (int64_t)nbh) {
       for (int64_t t = b; t < ntiles; t += nbh) move(t);
     } else {
       const int64_t t0 = ntiles * w0 / nbh, t1 = ntiles * (w0 + wq) / nbh;
@@ -963,6 +972,11 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
     return w;
   };
   const int64_t maxvec = widest(1, false), maxtiled = widest(1, true);
+  a.handout = 0;
+  a.edges = 0;
+  for_each_range([&](int64_t lo, int64_t hi) {
+    if (hi > lo && (lo % V != 0 || hi % V != 0 || vecs_in(lo, hi, V) == 0)) a.edges = 1;
+  });
   // segments (independent chunk transfers) of step st, as step_segments counts them
   auto nseg_of = [&](int st) {
     if (mode == kModeHier) return p;
@@ -1083,9 +1097,15 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   // rank, against 89.7 with one each.
   const int spans = kXcds / std::gcd(a.channels, kXcds);
   a.qn = std::max(1, std::min(std::min(spans, grid / a.channels), kMaxChannels / a.channels));
+  // counters only where the channel's parts fill whole tiles: with a part of a
+  // few hundred bytes the tiles are nearly empty, and a grab costs more than
+  // the part (p = 64 with 1 KiB per rank, 8 channels: 11.9 us per step with
+  // the counters, 8 without)
+  a.handout = widest(a.channels, true) >= tv ? 1 : 0;
   bool hand_out = false;
   for (int st = step_begin; st < step_end; ++st)
     hand_out = hand_out || (int64_t)nseg_of(st) * a.T >= kHandOutTiles * (grid / a.channels);
+  hand_out = hand_out && a.handout;
   if (hand_out) {
     e = launch_fill_u32(&sc.ws->tiles[0][0], 0u, (int64_t)a.channels * a.qn * 32, s);
     if (e != hipSuccess) return e;
