@@ -667,9 +667,9 @@ def main():
                                      "tree")]
         runs += [(a, a, {"group": hier_group(p)}) for a in ("hier", "hier_fused")]
         # the step ring on one persistent grid with device-wide barriers between
-        # steps (the library's default persistent grid: 5 workgroups per CU)
+        # steps (the library's default persistent grid: 3 workgroups per CU)
         cus = torch.cuda.get_device_properties(0).multi_processor_count
-        runs += [("ring_step_persistent", "ring_step", {"grid": 5 * cus})]
+        runs += [("ring_step_persistent", "ring_step", {"grid": 3 * cus})]
         runs += [("fused_wide_fp32_accumulate", "fused", {"wide": True}),
                  ("fused_avg", "fused", {"op": "avg"}), ("fused_max", "fused", {"op": "max"})]
         for name, algo, kw in runs:

@@ -45,7 +45,7 @@
  *  flag-driven pipelined and channel algorithms, and the step algorithms when
  *  ra_options.grid or step_ts is set, run persistent grids: ordinary launches
  *  whose workgroups wait for each other, so all of them must be resident at
- *  once.  Such a grid is sized to what the GPU can hold of it (by default 5
+ *  once.  Such a grid is sized to what the GPU can hold of it (by default 3
  *  workgroups per compute unit, 4 for RING_PIPELINED_FLAGS, whose LDS stages
  *  allow no more), so overlapping such calls should each set ra_options.grid
  *  to their share; a call that cannot get all its workgroups resident times
@@ -352,7 +352,7 @@ int ra_stream_copy(void* dst, const void* src, int64_t bytes, hipStream_t stream
 
 /*
  * ra_stream_copy_resident -- the same copy on a resident grid of `grid`
- * workgroups (0 = the library's default persistent grid, 5 per compute unit)
+ * workgroups (0 = the library's default persistent grid, 3 per compute unit)
  * that loop over 16 KiB tiles, the workgroups of each XCD taking a contiguous
  * range of tiles in order from a tile counter: the way the persistent step
  * kernels take a large step's tiles, and the streaming ceiling they are

@@ -823,12 +823,21 @@ static hipError_t xcd_placement(bool* ok, bool may_probe) {
 // The kernels' actual use is below that (compiler resource report: at most
 // 106 SGPRs and 117 VGPRs per wave among the persistent kernels).
 static constexpr int kSgprWavesPerSimd = 7;
-// Of the resident maximum, the grid a persistent kernel takes by default:
-// 5 workgroups per CU.  Measured on MI355X, persistent step ring at 8 x 16 GB
-// bf16: 103.3 ms with 4 per CU, 97.3 with 5, 98.7 with 6 (the flag-driven
-// pipelined kernel's 32 KiB of LDS per workgroup allows only 4 anyway).  A
-// caller's ra_options.grid may ask for up to the resident maximum.
-static constexpr int kPersistentPerCU = 5;
+// Of the resident maximum, the grid a persistent step kernel takes by default:
+// 3 workgroups per CU.  Fewer workgroups each take more tiles, and a barrier
+// costs more the more workgroups wait at it.  Measured on MI355X with the
+// tiles handed out in order, ms per all-reduce at 2 / 3 / 4 / 5 per CU (bf16
+// unless noted): ring at 8 x 16 GB 93.4 / 86.9 / 87.6 / 87.6 (one launch per
+// step: 87.2); 8 x 1 GiB 12.7 / 12.1 / 12.5 / 12.6; 8 x 64 MiB float32 1.70 /
+// 1.63 / 1.68 / 1.68; 8 x 16 MiB 0.253 / 0.271 / 0.289 / 0.289; channels at
+// 8 x 16 GB 93.6 / 88.2 / 89.5 / 89.6.  (Before the in-order hand-out, 5 per CU
+// was best: 103.3 ms with 4, 97.3 with 5, 98.7 with 6.)  A caller's
+// ra_options.grid may ask for up to the resident maximum.
+static constexpr int kPersistentPerCU = 3;
+// The flag-driven pipelined kernel's default budget of workgroups, and the
+// worker count its default slice length is sized for: 5 per CU, of which its
+// 32 KiB of LDS per workgroup lets 4 be resident.
+static constexpr int kPipelinedPerCU = 5;
 
 // Workgroups of `func` that can be resident at once on the current device.
 static hipError_t resident_blocks(const void* func, int* out) {
@@ -856,8 +865,8 @@ int default_persistent_workgroups() {
 }
 
 
-// Step-by-step kernels run on a persistent grid capped at 4 workgroups per CU
-// (see kPersistentPerCU), so each thread keeps more bytes in flight: measured at
+// Step-by-step kernels run on a persistent grid of a few workgroups per CU (see
+// kPersistentPerCU), so each thread keeps more bytes in flight: measured at
 // 8 x 16 GB bf16, four vectors per thread ran 103.8 ms against 107.3 with two.
 static constexpr int kStepU = 4;
 
@@ -1154,7 +1163,7 @@ int64_t pipelined_default_slice(int p, int64_t n, int dtype, int grid_override) 
   int cus = 0;
   int64_t workers = 64;
   if (device_cus(&cus) == hipSuccess && cus > 0) {
-    const int64_t budget = grid_override > 0 ? grid_override : (int64_t)cus * kPersistentPerCU;
+    const int64_t budget = grid_override > 0 ? grid_override : (int64_t)cus * kPipelinedPerCU;
     workers = std::max<int64_t>(1, budget / p);
   }
   const int64_t chunk = n / p + 1;
@@ -1209,7 +1218,10 @@ static hipError_t pipelined_dt(const RankPtrs& P, int p, int64_t n, int hop_begi
   int resident = 0;
   hipError_t e = resident_blocks(func, &resident);
   if (e != hipSuccess) return e;
-  int budget = sc.grid > 0 ? std::min(sc.grid, resident) : default_persistent_grid(resident);
+  int cus = 0;
+  e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  int budget = sc.grid > 0 ? std::min(sc.grid, resident) : std::min(resident, kPipelinedPerCU * cus);
   int workers = (int)std::max<int64_t>(1, std::min<int64_t>(budget / p, kmax));
   if (workers * p > resident) return hipErrorInvalidConfiguration;   // p > resident
   bool placed = false;
