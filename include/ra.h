@@ -46,10 +46,13 @@
  *  ra_options.grid or step_ts is set, run persistent grids: ordinary launches
  *  whose workgroups wait for each other, so all of them must be resident at
  *  once.  Such a grid is sized to what the GPU can hold of it (by default 3
- *  workgroups per compute unit, 4 for RING_PIPELINED_FLAGS, whose LDS stages
- *  allow no more), so overlapping such calls should each set ra_options.grid
- *  to their share; a call that cannot get all its workgroups resident times
- *  out (RA_ERR_TIMEOUT from ra_stream_status) instead of hanging.
+ *  workgroups of 256 threads per compute unit -- or, for the step algorithms
+ *  on 4 MiB to 256 MiB per rank, 2 of 512 or 1 of 1024 threads, so that fewer
+ *  workgroups wait at each barrier -- and 4 for RING_PIPELINED_FLAGS, whose
+ *  LDS stages allow no more), so overlapping such calls should each set
+ *  ra_options.grid (in 256-thread workgroups) to their share; a call that
+ *  cannot get all its workgroups resident times out (RA_ERR_TIMEOUT from
+ *  ra_stream_status) instead of hanging.
  *
  *  HIP graphs.  The one-pass algorithms (FUSED, HIER_FUSED), the pipelined ring
  *  (RING_PIPELINED) and the step algorithms' default launches (one per step,
@@ -164,14 +167,17 @@ typedef struct ra_options {
   int32_t grid;         /* step algorithms (RING_STEP, RING_BIDIR, TREE, HIER): 0 = the
                            library chooses (see RA_ALGO_RING_STEP).  1 with steps of at
                            most 256 vectors: the single workgroup.  Otherwise a value
-                           above 0 runs one persistent grid of that many workgroups (at
-                           most as many as fit the GPU) with a device-wide barrier
-                           between steps.  RING_PIPELINED_FLAGS, RING_CHANNELS: an upper
-                           bound on the workgroups of their persistent grid (the flag
-                           ring uses the same number per rank, rounded down to a
-                           multiple of 8 when 8 or more fit); 0 = 4 per compute unit.
-                           Values above what fits the GPU are cut to that.  Other
-                           algorithms ignore it. */
+                           above 0 runs one persistent grid of that many 256-thread
+                           workgroups (at most as many as fit the GPU) with a
+                           device-wide barrier between steps.  RING_PIPELINED_FLAGS,
+                           RING_CHANNELS: an upper bound on the 256-thread workgroups
+                           of their persistent grid (the flag ring uses the same number
+                           per rank, rounded down to a multiple of 8 when 8 or more
+                           fit); 0 = the library's choice (the flag ring 4 per compute
+                           unit; channels 3 per compute unit, or 2 of 512 threads from
+                           4 MiB per rank and 1 of 1024 threads from 16 MiB to 256 MiB,
+                           64 MiB above 16 ranks).  Values above what fits the GPU are
+                           cut to that.  Other algorithms ignore it. */
   uint32_t flags;       /* RA_FLAG_* */
   uint64_t* step_ts;    /* optional DEVICE array of (steps + 1) uint64: device wall-clock
                            ticks at kernel start and as each step's barrier releases

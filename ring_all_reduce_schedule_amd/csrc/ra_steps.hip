@@ -38,8 +38,8 @@ namespace ra {
 // ================================================================ hop on one tile
 
 // Tile j of the segment [lo, hi): dst[i] = dst[i] (op) src[i] (ADD) or
-// dst[i] = src[i].  A tile covers kBlock*U consecutive vectors; tile 0 also takes
-// the scalar head and tail of the segment.
+// dst[i] = src[i].  A tile covers BS*U consecutive vectors (BS threads, U
+// vectors each); tile 0 also takes the scalar head and tail of the segment.
 //
 // Averages ([InDepth] "Failure modes": pre-divide) divide every rank's
 // contribution by p exactly once, at the first hop that reads it: div_src and
@@ -51,11 +51,11 @@ struct HopFlags {
 };
 
 // The vectors of the tile that starts at vector t0, U per thread, that lie in
-// [tl, t1).  GUARD = false: the tile is whole (tl = t0, t1 - t0 = kBlock * U),
+// [tl, t1).  GUARD = false: the tile is whole (tl = t0, t1 - t0 = BS * U),
 // so no access needs a bounds test and all 2U loads issue back to back before
 // the first wait; with per-access guards the compiler splits them into
 // separately waited branches.
-template <int DT, int OP, int U, bool ADD, bool NT, bool GUARD>
+template <int DT, int OP, int U, bool ADD, bool NT, bool GUARD, int BS>
 __device__ __forceinline__ void hop_vectors(void* __restrict__ src, void* __restrict__ dst,
                                             int64_t t0, int64_t tl, int64_t t1, int p, HopFlags f) {
   constexpr bool kDiv = OP == kAvg && ADD;
@@ -64,7 +64,7 @@ __device__ __forceinline__ void hop_vectors(void* __restrict__ src, void* __rest
   u32x4 a[U], b[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    v[u] = t0 + u * kBlock + threadIdx.x;
+    v[u] = t0 + u * BS + threadIdx.x;
     in[u] = !GUARD || (v[u] >= tl && v[u] < t1);
     if (in[u]) {
       a[u] = ld16<NT>(src, v[u]);
@@ -88,14 +88,14 @@ __device__ __forceinline__ void hop_vectors(void* __restrict__ src, void* __rest
   }
 }
 
-template <int DT, int OP, int U, bool ADD, bool NT>
+template <int DT, int OP, int U, bool ADD, bool NT, int BS = kBlock>
 __device__ __forceinline__ void hop_tile(void* __restrict__ src, void* __restrict__ dst,
                                          int64_t lo, int64_t hi, int64_t j, int p, HopFlags f) {
   typedef Elem<DT> E;
   constexpr int V = E::V;
   constexpr bool kDiv = OP == kAvg && ADD;
   const Span sp = split_span<V>(lo, hi);
-  const int64_t tv = (int64_t)kBlock * U;
+  const int64_t tv = (int64_t)BS * U;
   const int64_t t0 = sp.vb + j * tv;               // tiles start on lines (Span)
   const int64_t tl = t0 > sp.v0 ? t0 : sp.v0;
   const int64_t t1 = t0 + tv < sp.v1 ? t0 + tv : sp.v1;
@@ -112,9 +112,9 @@ __device__ __forceinline__ void hop_tile(void* __restrict__ src, void* __restric
     if (ADD) y = ld1<DT>(dst, i);
   }
   if (tl == t0 && t1 - t0 == tv)        // the same for the whole workgroup
-    hop_vectors<DT, OP, U, ADD, NT, false>(src, dst, t0, tl, t1, p, f);
+    hop_vectors<DT, OP, U, ADD, NT, false, BS>(src, dst, t0, tl, t1, p, f);
   else if (tl < t1)
-    hop_vectors<DT, OP, U, ADD, NT, true>(src, dst, t0, tl, t1, p, f);
+    hop_vectors<DT, OP, U, ADD, NT, true, BS>(src, dst, t0, tl, t1, p, f);
   if (edge) {
     if (ADD) {
       if (kDiv) {
@@ -525,11 +525,11 @@ __device__ __forceinline__ void block_step(const StepArgs& a, const RankPtrs& P,
 // lo + h*floor(len/C) + min(h, len mod C) -- and its workgroups wait only for
 // each other between steps.  Every element still takes the same hops in the same
 // order, so the result does not depend on C; C = 1 is the plain step-by-step ring.
-template <int DT, int OP, int U, bool NT>
-__global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
+template <int DT, int OP, int U, bool NT, int BS>
+__global__ __launch_bounds__(BS) void k_steps(StepArgs a) {
   if (ws_failed(a.ws)) return;
   if (a.step_ts && blockIdx.x == 0 && threadIdx.x == 0) a.step_ts[0] = now_ticks();
-  if (a.sync == kSyncBlock) {
+  if constexpr (BS == kBlock) if (a.sync == kSyncBlock) {
     // one workgroup: its own barrier (with workgroup-scope release and acquire,
     // enough for threads of one CU) separates the steps.  The rank pointers,
     // indexed per lane here, are read from a copy in LDS.
@@ -587,9 +587,9 @@ __global__ __launch_bounds__(kBlock) void k_steps(StepArgs a) {
       const int64_t lo = g.lo + h * q + (h < rem ? h : rem);
       const int64_t hi = lo + q + (h < rem ? 1 : 0);
       if (g.add)
-        hop_tile<DT, OP, U, true, NT>(a.P.b[g.src], a.P.b[g.dst], lo, hi, j, a.p, g.f);
+        hop_tile<DT, OP, U, true, NT, BS>(a.P.b[g.src], a.P.b[g.dst], lo, hi, j, a.p, g.f);
       else
-        hop_tile<DT, OP, U, false, NT>(a.P.b[g.src], a.P.b[g.dst], lo, hi, j, a.p, g.f);
+        hop_tile<DT, OP, U, false, NT, BS>(a.P.b[g.src], a.P.b[g.dst], lo, hi, j, a.p, g.f);
     };
     if (!a.handout || ntiles < kHandOutTiles * (int64_t)nbh) {
       for (int64_t t = b; t < ntiles; t += nbh) move(t);
@@ -819,12 +819,15 @@ static hipError_t xcd_placement(bool* ok, bool may_probe) {
 //  * the scalar-register bound: a gfx9 SIMD holds 800 SGPRs and a wave's
 //    allocation is at most 112 (the 102 addressable, VCC and the trap and
 //    flat-scratch registers, in granules of 16), so at least 7 waves per SIMD
-//    always fit -- 7 workgroups of 256 threads (one wave per SIMD each) per CU.
+//    always fit -- 7 workgroups of 256 threads (one wave per SIMD each) per CU,
+//    3 of 512, 1 of 1024.
 // The kernels' actual use is below that (compiler resource report: at most
 // 106 SGPRs and 117 VGPRs per wave among the persistent kernels).
 static constexpr int kSgprWavesPerSimd = 7;
-// Of the resident maximum, the grid a persistent step kernel takes by default:
-// 3 workgroups per CU.  Fewer workgroups each take more tiles, and a barrier
+// Of the resident maximum, the grid a persistent step kernel of 256-thread
+// workgroups takes by default: 3 per CU (the shape of large buffers and of
+// every caller-sized grid; smaller buffers take larger workgroups, see
+// persistent_shape).  Fewer workgroups each take more tiles, and a barrier
 // costs more the more workgroups wait at it.  Measured on MI355X with the
 // tiles handed out in order, ms per all-reduce at 2 / 3 / 4 / 5 per CU (bf16
 // unless noted): ring at 8 x 16 GB 93.4 / 86.9 / 87.6 / 87.6 (one launch per
@@ -840,22 +843,41 @@ static constexpr int kPersistentPerCU = 3;
 static constexpr int kPipelinedPerCU = 5;
 
 // Workgroups of `func` that can be resident at once on the current device.
-static hipError_t resident_blocks(const void* func, int* out) {
+// Workgroups of `func` (`threads` each) that can be resident at once on the
+// current device.
+static hipError_t resident_blocks(const void* func, int* out, int threads = kBlock) {
   int cus = 0;
   hipError_t e = device_cus(&cus);
   if (e != hipSuccess) return e;
   int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, func, kBlock, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, func, threads, 0);
   if (e != hipSuccess) return e;
-  *out = std::max(1, std::min(per_cu, kSgprWavesPerSimd)) * cus;
+  *out = std::max(1, std::min(per_cu, kSgprWavesPerSimd * kBlock / threads)) * cus;
   return hipSuccess;
 }
 
-// The grid a persistent kernel runs by default, at most `resident`.
-static int default_persistent_grid(int resident) {
-  int cus = 0;
-  if (device_cus(&cus) != hipSuccess || cus <= 0) return resident;
-  return std::min(resident, kPersistentPerCU * cus);
+// Shape of a persistent step grid that the library sizes itself (no
+// ra_options.grid): threads per workgroup and workgroups per CU, by bytes per
+// rank.  A barrier's cost grows with the workgroups that wait at it (each one
+// invalidates its XCD's L2 on the way out), so where a step moves little, the
+// same threads in fewer, larger workgroups win; where steps are large, 256
+// threads x 3 per CU stream best.  Measured on MI355X, bf16, ms per all-reduce
+// at 256 x 3 / 512 x 2 / 1024 x 1 (channels chosen automatically):
+//   p = 8:  4 MiB per rank 0.069 / 0.063 / 0.076; 16 MiB 0.239 / 0.164 / 0.117;
+//           256 MiB 1.587 / 1.597 / 1.560; 1 GiB 6.02 / 6.20 / 6.08;
+//   p = 16: 8 MiB 0.232 / 0.160 / 0.161; 16 MiB 0.504 / 0.336 / 0.227;
+//           256 MiB 3.37 / 3.39 / 3.30; 512 MiB 6.50 / 6.64 / 6.61;
+//   p = 64: 8 MiB 1.27 / 0.94 / 1.02; 64 MiB 4.52 / 4.22 / 4.13;
+//           128 MiB 7.70 / 7.52 / 8.45;
+//   p = 4 to 64 at 2 MiB per rank: 256 x 3 best or within 1%.
+struct GridShape {
+  int threads, per_cu;
+};
+static GridShape persistent_shape(int64_t rank_bytes, int p) {
+  constexpr int64_t kMiB = 1ll << 20;
+  if (rank_bytes >= 4 * kMiB && rank_bytes < 16 * kMiB) return {512, 2};
+  if (rank_bytes >= 16 * kMiB && rank_bytes <= (p > 16 ? 64 : 256) * kMiB) return {1024, 1};
+  return {kBlock, kPersistentPerCU};
 }
 
 int default_persistent_workgroups() {
@@ -901,6 +923,19 @@ static bool step_copies(StepMode mode, int st, int p, int levels, int g, int m) 
     return st >= inter0 && st - inter0 >= m - 1;
   }
   return st >= p - 1;
+}
+
+// The step kernel with `threads` threads per workgroup (256, 512 or 1024).
+template <int DT, int OP>
+static const void* steps_kernel(bool nt, int threads) {
+  if (threads == 1024)
+    return nt ? reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, true, 1024>)
+              : reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, false, 1024>);
+  if (threads == 512)
+    return nt ? reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, true, 512>)
+              : reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, false, 512>);
+  return nt ? reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, true, kBlock>)
+            : reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, false, kBlock>);
 }
 
 template <int DT, int OP>
@@ -1050,9 +1085,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
     *launches = step_end - step_begin;
     return hipSuccess;
   }
-  const void* func = streaming(p, n, DT)
-                         ? reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, true>)
-                         : reinterpret_cast<const void*>(&k_steps<DT, OP, kStepU, false>);
+  const bool nt = streaming(p, n, DT);
   void* args[] = {&a};
   // Small steps run on one workgroup with its own barrier between steps: a
   // device-wide barrier costs microseconds (L2 write-back, atomics across XCDs,
@@ -1065,15 +1098,21 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
     a.W = std::max<int64_t>(1, maxvec);
     *grid_used = 1;
     *launches = 1;
-    return hipLaunchKernel(func, dim3(1), dim3(kBlock), args, 0, s);
+    return hipLaunchKernel(steps_kernel<DT, OP>(nt, kBlock), dim3(1), dim3(kBlock), args, 0, s);
   }
   // the persistent grid's barriers live in the stream's workspace
   if (sc.ws == nullptr) return hipErrorInvalidValue;
-  int resident = 0;
-  hipError_t e = resident_blocks(func, &resident);
+  // a caller's grid counts workgroups of 256 threads
+  const GridShape shape = sc.grid > 0 ? GridShape{kBlock, kPersistentPerCU}
+                                      : persistent_shape(n * elem_bytes(DT), p);
+  const void* func = steps_kernel<DT, OP>(nt, shape.threads);
+  int resident = 0, cus = 0;
+  hipError_t e = resident_blocks(func, &resident, shape.threads);
   if (e != hipSuccess) return e;
-  int grid = sc.grid > 0 ? std::min(sc.grid, resident) : default_persistent_grid(resident);
-  const int64_t tv = (int64_t)kBlock * kStepU;
+  e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  int grid = std::min(resident, sc.grid > 0 ? sc.grid : shape.per_cu * cus);
+  const int64_t tv = (int64_t)shape.threads * kStepU;
   // no more workgroups than whole-segment tiles: on small buffers every extra
   // workgroup only adds to each barrier's cost
   const int64_t most = (int64_t)most_seg * std::max<int64_t>(1, (maxtiled + tv - 1) / tv);
@@ -1121,7 +1160,7 @@ static hipError_t steps_dt(const RankPtrs& P, int p, int64_t n, StepMode mode, i
   }
   *grid_used = grid;
   *launches = 1;
-  return hipLaunchKernel(func, dim3(grid), dim3(kBlock), args, 0, s);
+  return hipLaunchKernel(func, dim3(grid), dim3(shape.threads), args, 0, s);
 }
 
 // (dtype, op) pairs that exist: avg needs a float type.

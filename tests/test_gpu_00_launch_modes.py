@@ -8,6 +8,8 @@ the documented choices:
 * larger steps: one launch per step (2(p-1) for the ring, 2*ceil(log2 p) for
   the tree);
 * a caller's grid, or channels: one persistent launch of that many workgroups;
+* the library's own persistent grids: 256-thread workgroups, 512-thread ones
+  from 4 MiB per rank, 1024-thread ones from 16 MiB (1 per compute unit);
 * the slice-carrying pipelined ring: one launch, one workgroup per 4 KiB slice
   of every chunk.
 
@@ -22,6 +24,7 @@ import subprocess
 import sys
 
 import pytest
+import torch
 
 from tests.gpu_util import require_gpu
 
@@ -41,6 +44,8 @@ B.ra_allreduce_ex(bufs(8, 1 << 20), algo="tree")
 B.ra_allreduce_ex(bufs(8, 1 << 20), algo="ring_step", grid=16)   # caller's grid: persistent
 B.ra_allreduce_ex(bufs(8, 1 << 20), algo="ring_channels", channels=8)
 B.ra_allreduce_ex(bufs(8, 1 << 20), algo="ring_pipelined")       # one launch, a slice per workgroup
+B.ra_allreduce_ex(bufs(8, 3 << 20), algo="ring_channels")        # 6 MiB per rank: 512 threads
+B.ra_allreduce_ex(bufs(8, 10 << 20), algo="ring_channels")       # 20 MiB per rank: 1024 threads
 B.ra_stream_status()
 torch.cuda.synchronize()
 """
@@ -59,7 +64,7 @@ def test_step_launch_choices():
         m = re.search(r"algo=(\w+) p=(\d+) n=(\d+) dtype=\d+ grid=(\d+) launches=(\d+)", ln)
         assert m, ln
         got.append((m.group(1), int(m.group(3)), int(m.group(4)), int(m.group(5))))
-    assert len(got) == 6, lines
+    assert len(got) == 8, lines
     (a0, n0, g0, l0), (a1, n1, g1, l1), (a2, n2, g2, l2), (a3, n3, g3, l3), (a4, n4, g4, l4) = got[:5]
     assert (a0, g0, l0) == ("ring_step", 1, 1)
     assert (a1, l1) == ("ring_step", 14) and g1 > 1
@@ -68,3 +73,8 @@ def test_step_launch_choices():
     assert a4 == "ring_channels" and l4 == 1 and g4 % 8 == 0
     # 2^20 bf16 per rank: 8 chunks of 16384 vectors, 64 tiles of 256 each
     assert got[5] == ("ring_pipelined", 1 << 20, 8 * 64, 1)
+    # 3 Mi bf16 per rank: chunks of 49,152 vectors, 24 tiles of 512 x 4 each, 8 chunks
+    assert got[6] == ("ring_channels", 3 << 20, 8 * 24, 1)
+    # 10 Mi bf16 per rank: 40 tiles of 1024 x 4 per chunk, one workgroup per compute unit
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert got[7] == ("ring_channels", 10 << 20, min(cus, 8 * 40), 1)

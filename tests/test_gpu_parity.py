@@ -225,6 +225,40 @@ def test_persistent_tile_handout(algo, opts):
             assert same_bits(g, want, dtype), f"call {k} rank {r} at {first_diff(g, want, dtype)}"
 
 
+# Persistent grids the library sizes itself take 512-thread workgroups from 4 MiB per
+# rank and 1024-thread ones from 16 MiB (up to 256 MiB, 64 MiB above 16 ranks); ragged
+# sizes, every mode that reaches such a grid without a caller-set grid.
+SHAPES = [("ring_channels", {"channels": 0}, 8, 2_500_003, "float32"),
+          ("ring_channels", {"channels": 3}, 5, 3_000_001, "bfloat16"),
+          ("ring_step", {"step_ts": True}, 9, 1_500_007, "int32"),
+          ("ring_channels", {"channels": 0}, 8, 5_000_011, "float32"),
+          ("ring_channels", {"channels": 8}, 4, 10_000_019, "bfloat16"),
+          ("ring_channels", {"channels": 0, "flags": B.RA_FLAG_STRESS}, 8, 4_200_017, "int32"),
+          ("ring_step", {"step_ts": True}, 17, 4_500_001, "float32"),
+          ("ring_bidir", {"step_ts": True}, 8, 4_400_009, "float32"),
+          ("tree", {"step_ts": True}, 6, 4_300_013, "float32"),
+          ("hier", {"group": 4, "step_ts": True}, 8, 4_100_003, "bfloat16")]
+
+
+@pytest.mark.parametrize("case", range(len(SHAPES)))
+def test_persistent_workgroup_shapes(case):
+    require_gpu()
+    algo, opts, p, n, dtype = SHAPES[case]
+    opts = dict(opts)
+    if opts.pop("step_ts", False):
+        opts["step_ts"] = torch.zeros(512, dtype=torch.int64, device="cuda")
+    xs = inputs.make_inputs(p, n, dtype, seed=70 + case, sigma=1.0)
+    got = run(xs, dtype, algo, **opts)
+    if algo == "hier":
+        want = oracle.hier_fold(xs, dtype, opts["group"])
+    elif algo == "ring_channels":
+        want = oracle.ring_fold(xs, dtype)
+    else:
+        want = expected(xs, dtype, algo)
+    for r, g in enumerate(got):
+        assert same_bits(g, want, dtype), f"rank {r} at {first_diff(g, want, dtype)}"
+
+
 def test_noop_cases():
     require_gpu()
     x = [torch.arange(10, dtype=torch.float32, device="cuda")]
