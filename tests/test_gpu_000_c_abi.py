@@ -3,12 +3,13 @@ from hipMalloc, no Python binding and no torch.  It checks every algorithm's int
 all-reduce against the closed-form sum, the reduce-scatter's owned chunks, the
 all-gather, and the argument errors.
 
-The check runs as a child process before this test process touches the GPU (the
-module sorts first among the GPU tests and imports no GPU library)."""
+The check runs as a child process.  The module sorts first among the GPU tests and
+imports no GPU library, so the child normally has the GPU to itself; every launch
+the library makes is an ordinary one, so it also runs beside a test process that
+already holds the GPU."""
 
 import os
 import subprocess
-import sys
 
 import pytest
 
@@ -19,9 +20,6 @@ BIN = os.path.join(ROOT, "tests", "c", "abi_check")
 
 
 def test_c_program_uses_the_abi():
-    torch = sys.modules.get("torch")
-    if torch is not None and torch.cuda.is_initialized():
-        pytest.skip("the GPU is already initialised in this process; run this module first")
     assert os.path.exists(BIN), "tests/c/abi_check is missing: run build() first"
     print("[case] tests/c/abi_check", flush=True)
     res = subprocess.run([BIN], capture_output=True, text=True, timeout=120)
