@@ -417,6 +417,7 @@ __device__ __forceinline__ void st1(void* base, int64_t i, typename Elem<DT>::S 
   reinterpret_cast<typename Elem<DT>::S*>(base)[i] = v;
 }
 
+
 // Vector vt + lane of every rank (vt wave-uniform), folded or stored.
 //
 // The rank index is wave-uniform, so each rank's pointer is a scalar load from
@@ -527,6 +528,56 @@ __device__ __forceinline__ void store_all(const RankPtrs& P, int p, int64_t vt, 
       default: break;
     }
   }
+}
+
+// ---------------------------------------------------------------- single elements
+// Chunk edges that fall inside a 16-byte vector are folded one element per
+// thread, each lane serving its own chunk, so a lane's ranks differ from its
+// neighbours': the pointers come from an LDS copy of the table, and every
+// element's loads go out a batch of ring positions at a time, all in flight
+// before the first is used.  Fetched one rank at a time, a pointer and then a
+// value, an element waited for 2p memory round trips in a row, longer than the
+// tiles of a small call take.
+
+// Copy the p rank pointers to LDS (every thread of the workgroup calls this).
+__device__ __forceinline__ void load_rank_table(void** lp, const RankPtrs& P, int p) {
+  if (threadIdx.x < (unsigned)p) lp[threadIdx.x] = P.b[threadIdx.x];
+  __syncthreads();
+}
+
+// x[u] = element i of rank base + (c + first + u) mod m for the ring positions
+// first + u < end; positions from `end` on repeat position end - 1 (loaded, not
+// to be used), so the loads need no guard.  c < m and end <= m.
+template <int DT>
+__device__ __forceinline__ void load_positions(typename Elem<DT>::S (&x)[kRankBatch],
+                                               void* const* lp, int base, int m, int c, int first,
+                                               int end, int64_t i) {
+#pragma unroll
+  for (int u = 0; u < kRankBatch; ++u) {
+    const int k = first + u < end ? first + u : end - 1;
+    const int r = c + k;
+    x[u] = ld1<DT>(lp[base + (r >= m ? r - m : r)], i);
+  }
+}
+
+// Element i folded over ranks base + c, base + c + 1, ..., base + c + m - 1
+// (positions mod m) in that order, F's rounding at every hop.
+template <class F, int DT>
+__device__ __forceinline__ typename F::A1 fold_element(void* const* lp, int base, int m, int c,
+                                                       int64_t i, int p) {
+  typename F::A1 acc{};
+  for (int k0 = 0; k0 < m; k0 += kRankBatch) {
+    typename Elem<DT>::S x[kRankBatch];
+    load_positions<DT>(x, lp, base, m, c, k0, m, i);
+#pragma unroll
+    for (int u = 0; u < kRankBatch; ++u) {
+      if (k0 + u == 0)
+        acc = F::start1(x[u], p);
+      else if (k0 + u < m)
+        acc = F::step1(acc, x[u], p);
+    }
+  }
+  return acc;
 }
 
 // Split [lo, hi) into a scalar head, whole 16-byte vectors, and a scalar tail.

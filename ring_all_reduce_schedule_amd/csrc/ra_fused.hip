@@ -28,29 +28,24 @@ namespace ra {
 enum FusedMode { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
 
 // Element i of chunk c folded and stored on its own (the chunks' unaligned
-// edges: elements that share a 16-byte vector with the neighbouring chunk).
+// edges: elements that share a 16-byte vector with the neighbouring chunk).  lp
+// is the LDS copy of the rank pointers; the fold issues its loads in batches
+// (fold_element).
 template <int DT, int OP, bool WIDE, int MODE>
-__device__ __forceinline__ void fused_element(const RankPtrs& P, int p, int c, int64_t i) {
+__device__ __forceinline__ void fused_element(void* const* lp, int p, int c, int64_t i) {
   typedef Elem<DT> E;
   typedef Fold<DT, OP, WIDE> F;
   const int owner = c == 0 ? p - 1 : c - 1;
   typename E::S out;
-  if (MODE == kAllGather) {
-    out = ld1<DT>(P.b[owner], i);
-  } else {
-    typename F::A1 acc = F::start1(ld1<DT>(P.b[c], i), p);
-    for (int k = 1; k < p; ++k) {
-      int r = c + k;
-      r = r >= p ? r - p : r;
-      acc = F::step1(acc, ld1<DT>(P.b[r], i), p);
-    }
-    out = F::finish1(acc);
-  }
+  if (MODE == kAllGather)
+    out = ld1<DT>(lp[owner], i);
+  else
+    out = F::finish1(fold_element<F, DT>(lp, 0, p, c, i, p));
   if (MODE == kReduceScatter) {
-    st1<DT>(P.b[owner], i, out);
+    st1<DT>(lp[owner], i, out);
   } else {
     for (int r = 0; r < p; ++r)
-      if (!(MODE == kAllGather && r == owner)) st1<DT>(P.b[r], i, out);
+      if (!(MODE == kAllGather && r == owner)) st1<DT>(lp[r], i, out);
   }
 }
 
@@ -61,13 +56,15 @@ template <int DT, int OP, bool WIDE, int MODE>
 __device__ __forceinline__ void fused_edges(const RankPtrs& P, const ChunkGeo& g, int p) {
   constexpr int V = Elem<DT>::V;
   constexpr int kPer = 2 * V - 2;
+  __shared__ void* lp[kMaxRanks];
+  load_rank_table(lp, P, p);
   for (int e = threadIdx.x; e < p * kPer; e += kBlock) {
     const int c = e / kPer, k = e - c * kPer;
     const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
     const Span sp = split_span<V>(lo, hi);
     const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
     if (k < nh + nt)
-      fused_element<DT, OP, WIDE, MODE>(P, p, c, k < nh ? lo + k : sp.tail_lo + (k - nh));
+      fused_element<DT, OP, WIDE, MODE>(lp, p, c, k < nh ? lo + k : sp.tail_lo + (k - nh));
   }
 }
 
@@ -201,24 +198,20 @@ __device__ __forceinline__ void hier_segment(const ChunkGeo& gi, int M, int seg,
   *hi = chunk_hi(sg, *d);
 }
 
-// Element i of segment (c, d) in the two-level order, stored to every rank.
+// Element i of segment (c, d) in the two-level order, stored to every rank (lp:
+// the LDS copy of the rank pointers).
 template <int DT, int OP>
-__device__ __forceinline__ void hier_element(const RankPtrs& P, int p, int G, int M, int c, int d,
+__device__ __forceinline__ void hier_element(void* const* lp, int p, int G, int M, int c, int d,
                                              int64_t i) {
   typedef Elem<DT> E;
   typedef Fold<DT, OP, false> F;
   typename E::S total = 0;
   for (int k2 = 0; k2 < M; ++k2) {
     const int q = d + k2 < M ? d + k2 : d + k2 - M;
-    typename E::S acc = F::start1(ld1<DT>(P.b[q * G + c], i), p);
-    for (int k1 = 1; k1 < G; ++k1) {
-      int l = c + k1;
-      l = l >= G ? l - G : l;
-      acc = F::step1(acc, ld1<DT>(P.b[q * G + l], i), p);
-    }
+    const typename E::S acc = fold_element<F, DT>(lp, q * G, G, c, i, p);
     total = k2 == 0 ? acc : comb1<DT, OP>(total, acc);
   }
-  for (int r = 0; r < p; ++r) st1<DT>(P.b[r], i, total);
+  for (int r = 0; r < p; ++r) st1<DT>(lp[r], i, total);
 }
 
 // Tiles as in k_fused, over the G*M segments; the segments' edge elements, when
@@ -234,13 +227,15 @@ __global__ __launch_bounds__(kBlock) void k_fused_hier(RankPtrs P, ChunkGeo gi, 
     int64_t lo, hi;
     if (t < edges) {
       constexpr int kPer = 2 * V - 2;
+      __shared__ void* lp[kMaxRanks];
+      load_rank_table(lp, P, p);
       for (int e = threadIdx.x; e < G * M * kPer; e += kBlock) {
         const int seg = e / kPer, k = e - seg * kPer;
         hier_segment(gi, M, seg, &c, &d, &lo, &hi);
         const Span sp = split_span<V>(lo, hi);
         const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
         if (k < nh + nt)
-          hier_element<DT, OP>(P, p, G, M, c, d, k < nh ? lo + k : sp.tail_lo + (k - nh));
+          hier_element<DT, OP>(lp, p, G, M, c, d, k < nh ? lo + k : sp.tail_lo + (k - nh));
       }
       continue;
     }

@@ -84,34 +84,40 @@ __device__ __forceinline__ void ride_hops(u32x4& acc, const RankPtrs& P, int p, 
 }
 
 // Element i of chunk c carried through its hops on its own (the chunks'
-// unaligned edges), as ride_hops does for a vector.
+// unaligned edges), as ride_hops does for a vector: the receivers of a batch of
+// hops are loaded together (load_positions), then each is combined with the
+// running partial and written back.  lp is the LDS copy of the rank pointers.
 template <int DT, int OP, int MODE>
-__device__ __forceinline__ void ride_element(const RankPtrs& P, int p, int c, int64_t i) {
+__device__ __forceinline__ void ride_element(void* const* lp, int p, int c, int64_t i) {
   typedef Elem<DT> E;
   constexpr bool kDiv = OP == kAvg && MODE != kRideAllGather;
   const int owner = c == 0 ? p - 1 : c - 1;
   if (MODE == kRideAllGather) {
-    const typename E::S out = ld1<DT>(P.b[owner], i);
+    const typename E::S out = ld1<DT>(lp[owner], i);
     for (int r = 0; r < p; ++r)
-      if (r != owner) st1<DT>(P.b[r], i, out);
+      if (r != owner) st1<DT>(lp[r], i, out);
     return;
   }
-  typename E::S acc = ld1<DT>(P.b[c], i);
+  typename E::S acc = ld1<DT>(lp[c], i);
   if (kDiv) {
     acc = E::div1(acc, p);
-    if (MODE == kRideReduceScatter) st1<DT>(P.b[c], i, acc);
+    if (MODE == kRideReduceScatter) st1<DT>(lp[c], i, acc);
   }
-  for (int h = 1; h < p; ++h) {
-    const int r = c + h < p ? c + h : c + h - p;
-    typename E::S x = ld1<DT>(P.b[r], i);
-    if (kDiv) x = E::div1(x, p);
-    acc = comb1<DT, OP>(acc, x);
-    st1<DT>(P.b[r], i, acc);
+  for (int h0 = 1; h0 < p; h0 += kRankBatch) {
+    typename E::S x[kRankBatch];
+    load_positions<DT>(x, lp, 0, p, c, h0, p, i);
+#pragma unroll
+    for (int u = 0; u < kRankBatch; ++u) {
+      if (h0 + u >= p) break;
+      const int r = c + h0 + u < p ? c + h0 + u : c + h0 + u - p;
+      acc = comb1<DT, OP>(acc, kDiv ? E::div1(x[u], p) : x[u]);
+      st1<DT>(lp[r], i, acc);
+    }
   }
   if (MODE == kRideAllReduce) {
     asm volatile("" ::: "memory");
     for (int r = 0; r < p; ++r)
-      if (r != owner) st1<DT>(P.b[r], i, acc);
+      if (r != owner) st1<DT>(lp[r], i, acc);
   }
 }
 
@@ -133,12 +139,14 @@ __global__ __launch_bounds__(kBlock) void k_rider(RankPtrs P, ChunkGeo g, int p,
   for (int64_t q = blockIdx.x; q < nslices; q += gridDim.x) {
     if (q < edges) {
       constexpr int kPer = 2 * V - 2;
+      __shared__ void* lp[kMaxRanks];
+      load_rank_table(lp, P, p);
       for (int e = threadIdx.x; e < p * kPer; e += kBlock) {
         const int c = e / kPer, k = e - c * kPer;
         const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
         const Span sp = split_span<V>(lo, hi);
         const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
-        if (k < nh + nt) ride_element<DT, OP, MODE>(P, p, c, k < nh ? lo + k : sp.tail_lo + (k - nh));
+        if (k < nh + nt) ride_element<DT, OP, MODE>(lp, p, c, k < nh ? lo + k : sp.tail_lo + (k - nh));
       }
       continue;
     }
