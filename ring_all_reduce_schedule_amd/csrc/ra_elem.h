@@ -530,56 +530,6 @@ __device__ __forceinline__ void store_all(const RankPtrs& P, int p, int64_t vt, 
   }
 }
 
-// ---------------------------------------------------------------- single elements
-// Chunk edges that fall inside a 16-byte vector are folded one element per
-// thread, each lane serving its own chunk, so a lane's ranks differ from its
-// neighbours': the pointers come from an LDS copy of the table, and every
-// element's loads go out a batch of ring positions at a time, all in flight
-// before the first is used.  Fetched one rank at a time, a pointer and then a
-// value, an element waited for 2p memory round trips in a row, longer than the
-// tiles of a small call take.
-
-// Copy the p rank pointers to LDS (every thread of the workgroup calls this).
-__device__ __forceinline__ void load_rank_table(void** lp, const RankPtrs& P, int p) {
-  if (threadIdx.x < (unsigned)p) lp[threadIdx.x] = P.b[threadIdx.x];
-  __syncthreads();
-}
-
-// x[u] = element i of rank base + (c + first + u) mod m for the ring positions
-// first + u < end; positions from `end` on repeat position end - 1 (loaded, not
-// to be used), so the loads need no guard.  c < m and end <= m.
-template <int DT>
-__device__ __forceinline__ void load_positions(typename Elem<DT>::S (&x)[kRankBatch],
-                                               void* const* lp, int base, int m, int c, int first,
-                                               int end, int64_t i) {
-#pragma unroll
-  for (int u = 0; u < kRankBatch; ++u) {
-    const int k = first + u < end ? first + u : end - 1;
-    const int r = c + k;
-    x[u] = ld1<DT>(lp[base + (r >= m ? r - m : r)], i);
-  }
-}
-
-// Element i folded over ranks base + c, base + c + 1, ..., base + c + m - 1
-// (positions mod m) in that order, F's rounding at every hop.
-template <class F, int DT>
-__device__ __forceinline__ typename F::A1 fold_element(void* const* lp, int base, int m, int c,
-                                                       int64_t i, int p) {
-  typename F::A1 acc{};
-  for (int k0 = 0; k0 < m; k0 += kRankBatch) {
-    typename Elem<DT>::S x[kRankBatch];
-    load_positions<DT>(x, lp, base, m, c, k0, m, i);
-#pragma unroll
-    for (int u = 0; u < kRankBatch; ++u) {
-      if (k0 + u == 0)
-        acc = F::start1(x[u], p);
-      else if (k0 + u < m)
-        acc = F::step1(acc, x[u], p);
-    }
-  }
-  return acc;
-}
-
 // Split [lo, hi) into a scalar head, whole 16-byte vectors, and a scalar tail.
 // All rank buffers start 16-byte aligned, so element i has the same alignment
 // in every buffer.
@@ -616,6 +566,88 @@ __device__ __forceinline__ Span split_span(int64_t lo, int64_t hi) {
     s.tail_lo = a1;
   }
   return s;
+}
+
+// ---------------------------------------------------------------- edge elements
+// A segment's edge elements -- at most V - 1 before its first whole vector and
+// V - 1 after its last (2V - 2 when it holds no whole vector) -- share a 16-byte
+// vector with the neighbouring segment, whose fold order differs, so they are
+// folded one by one.  One wave carries all of a segment's edge elements:
+//  1. lane r loads rank r's copy of every edge element, all loads in flight at
+//     once, into LDS: x[k][r];
+//  2. lane k folds element k in the segment's order from LDS, leaves in x[k][r]
+//     the value rank r is to store and in mask[k] the ranks that store;
+//  3. lane r stores its rank's values.
+// The loads take one memory round trip.  One element per thread, each lane
+// fetching its ranks one after another, an element waited for p round trips in
+// a row (2p while the pointers came from the kernel arguments), longer than the
+// tiles of a small call take: p = 64 with 524,365 bfloat16 per rank, 172 us per
+// one-pass all-reduce with 2p, 55 with batches of eight ranks, against 25 us
+// for 524,288 elements (no edges).
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kEdgePass = 4;
+
+template <int DT>
+struct EdgeSlab {
+  typedef typename Elem<DT>::S S;
+  static constexpr int K = 2 * Elem<DT>::V - 2;
+  // rows padded by one 32-bit word (or one element): lanes 0..K-1 reading the
+  // same column of different rows then meet different LDS banks
+  static constexpr int kRow = kMaxRanks + (sizeof(S) < 4 ? 4 / (int)sizeof(S) : 1);
+  S x[K][kRow];
+  uint64_t mask[K];
+};
+
+// Bit r set for every rank r < p.
+__device__ __forceinline__ uint64_t all_ranks(int p) {
+  return p >= 64 ? ~0ull : (1ull << p) - 1;
+}
+
+// Copy the p rank pointers to LDS (every thread of the workgroup calls this).
+__device__ __forceinline__ void load_rank_table(void** lp, const RankPtrs& P, int p) {
+  if (threadIdx.x < (unsigned)p) lp[threadIdx.x] = P.b[threadIdx.x];
+  __syncthreads();
+}
+
+// The edge elements of [lo, hi) (lo == hi: none), carried by the calling wave
+// with its own slab; lp is the LDS copy of the p rank pointers.  Every thread of
+// the workgroup calls this, since it holds workgroup barriers.  fold(slab, k)
+// runs on lane k for each edge element k.
+template <int DT, class FoldLane>
+__device__ __forceinline__ void edge_wave(void* const* lp, int p, int64_t lo, int64_t hi,
+                                          EdgeSlab<DT>& sl, FoldLane fold) {
+  constexpr int V = Elem<DT>::V, K = EdgeSlab<DT>::K;
+  const Span sp = split_span<V>(lo, hi);
+  const int64_t nh = sp.head_hi - lo;
+  const int ne = (int)(nh + (hi - sp.tail_lo));
+  const int lane = (int)(threadIdx.x % kWave);
+  auto index = [&](int k) { return k < nh ? lo + k : sp.tail_lo + (k - nh); };
+  if (ne > 0 && lane < p) {
+    // kEdgePass elements' loads at a time: all K at once would raise every
+    // kernel's register count (the one-pass kernel's from 45 to 68 for bfloat16,
+    // one wave per SIMD less).  Elements past the last repeat it (loaded, not
+    // used), so the loads need no guard.
+    for (int k0 = 0; k0 < ne; k0 += kEdgePass) {
+      typename Elem<DT>::S v[kEdgePass];
+#pragma unroll
+      for (int u = 0; u < kEdgePass; ++u)
+        v[u] = ld1<DT>(lp[lane], index(k0 + u < ne ? k0 + u : ne - 1));
+#pragma unroll
+      for (int u = 0; u < kEdgePass; ++u)
+        if (k0 + u < ne) sl.x[k0 + u][lane] = v[u];
+    }
+  }
+  __syncthreads();
+  if (lane < ne) fold(sl, lane);
+  __syncthreads();
+  if (ne > 0 && lane < p) {
+    // one element at a time: stores need no wait, and unrolled, the addresses
+    // of all K elements held at once cost registers in every kernel that calls this
+#pragma unroll 1
+    for (int k = 0; k < ne; ++k)
+      if ((sl.mask[k] >> lane) & 1) st1<DT>(lp[lane], index(k), sl.x[k][lane]);
+  }
 }
 
 }  // namespace ra

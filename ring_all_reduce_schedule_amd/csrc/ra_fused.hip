@@ -27,45 +27,43 @@ namespace ra {
 // "Trade-offs"), each move the least their output needs.
 enum FusedMode { kAllReduce = 0, kReduceScatter = 1, kAllGather = 2 };
 
-// Element i of chunk c folded and stored on its own (the chunks' unaligned
-// edges: elements that share a 16-byte vector with the neighbouring chunk).  lp
-// is the LDS copy of the rank pointers; the fold issues its loads in batches
-// (fold_element).
+// The chunks' edge elements (those that share a 16-byte vector with the
+// neighbouring chunk), one chunk per wave (edge_wave): edge workgroup w carries
+// chunks 4w .. 4w + 3.  Lane k folds element k of chunk c in ring order and
+// leaves what each rank stores.
 template <int DT, int OP, bool WIDE, int MODE>
-__device__ __forceinline__ void fused_element(void* const* lp, int p, int c, int64_t i) {
+__device__ __forceinline__ void fused_edges(const RankPtrs& P, const ChunkGeo& g, int p,
+                                            int64_t w) {
   typedef Elem<DT> E;
   typedef Fold<DT, OP, WIDE> F;
-  const int owner = c == 0 ? p - 1 : c - 1;
-  typename E::S out;
-  if (MODE == kAllGather)
-    out = ld1<DT>(lp[owner], i);
-  else
-    out = F::finish1(fold_element<F, DT>(lp, 0, p, c, i, p));
-  if (MODE == kReduceScatter) {
-    st1<DT>(lp[owner], i, out);
-  } else {
-    for (int r = 0; r < p; ++r)
-      if (!(MODE == kAllGather && r == owner)) st1<DT>(lp[r], i, out);
-  }
-}
-
-// Every chunk's edge elements, in one workgroup: a chunk has at most V - 1 before
-// its first whole vector and V - 1 after its last (2V - 2 when it holds no whole
-// vector at all).
-template <int DT, int OP, bool WIDE, int MODE>
-__device__ __forceinline__ void fused_edges(const RankPtrs& P, const ChunkGeo& g, int p) {
-  constexpr int V = Elem<DT>::V;
-  constexpr int kPer = 2 * V - 2;
   __shared__ void* lp[kMaxRanks];
+  __shared__ EdgeSlab<DT> slab[kWavesPerBlock];
   load_rank_table(lp, P, p);
-  for (int e = threadIdx.x; e < p * kPer; e += kBlock) {
-    const int c = e / kPer, k = e - c * kPer;
-    const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
-    const Span sp = split_span<V>(lo, hi);
-    const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
-    if (k < nh + nt)
-      fused_element<DT, OP, WIDE, MODE>(lp, p, c, k < nh ? lo + k : sp.tail_lo + (k - nh));
-  }
+  const int wave = (int)(threadIdx.x / kWave);
+  const int64_t cw = w * kWavesPerBlock + wave;
+  const int c = cw < p ? (int)cw : 0;
+  const int64_t lo = cw < p ? chunk_lo(g, c) : 0, hi = cw < p ? chunk_hi(g, c) : 0;
+  const int owner = c == 0 ? p - 1 : c - 1;
+  edge_wave<DT>(lp, p, lo, hi, slab[wave], [&](EdgeSlab<DT>& sl, int k) {
+    typename E::S out;
+    if (MODE == kAllGather) {
+      out = sl.x[k][owner];
+    } else {
+      typename F::A1 acc = F::start1(sl.x[k][c], p);
+      for (int j = 1; j < p; ++j) {
+        const int r = c + j < p ? c + j : c + j - p;
+        acc = F::step1(acc, sl.x[k][r], p);
+      }
+      out = F::finish1(acc);
+    }
+    if (MODE == kReduceScatter) {
+      sl.x[k][owner] = out;
+      sl.mask[k] = 1ull << owner;
+    } else {
+      for (int r = 0; r < p; ++r) sl.x[k][r] = out;
+      sl.mask[k] = all_ranks(p) & ~(MODE == kAllGather ? 1ull << owner : 0ull);
+    }
+  });
 }
 
 // Tile t = (chunk c, tile j of that chunk), one 16-byte vector per thread.
@@ -73,21 +71,25 @@ __device__ __forceinline__ void fused_edges(const RankPtrs& P, const ChunkGeo& g
 // acc = acc + x_{c+p-1} (indices mod p, rounding each addition), the order in
 // which the step-by-step ring accumulates chunk c, so the bits match.  OP and
 // WIDE choose the reduction and the accumulation type (Fold in ra_elem.h).
-// When the chunks have edge elements (edges = 1), workgroup 0 folds them all
-// while the tiles run: left in each chunk's first tile they were a second
-// memory round trip after its vectors, and in a launch whose workgroups all run
-// at once the slowest workgroup sets the time (p = 9, 1,000,003 int32 per
-// rank: 19.4 us against 17.4 with chunk starts on lines, before the move).
+// When the chunks have edge elements, the first `edges` workgroups fold them,
+// one chunk per wave, while the tiles run: left in each chunk's first tile they
+// were a second memory round trip after its vectors, and in a launch whose
+// workgroups all run at once the slowest workgroup sets the time (p = 9,
+// 1,000,003 int32 per rank: 19.4 us against 17.4 with chunk starts on lines,
+// before the move).
 template <int DT, int OP, bool WIDE, bool NT, int MODE>
 __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p, int64_t T,
                                                   int64_t ntiles, int edges) {
   typedef Fold<DT, OP, WIDE> F;
   constexpr int V = Elem<DT>::V;
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    if (t < edges) {
-      fused_edges<DT, OP, WIDE, MODE>(P, g, p);
-      continue;
-    }
+  int64_t t0 = blockIdx.x;
+  // the edge workgroups first, outside the tile loop: inside it, values the
+  // compiler keeps live across the loop added to the edge code's registers
+  if (t0 < edges) {
+    fused_edges<DT, OP, WIDE, MODE>(P, g, p, t0);
+    t0 += gridDim.x;
+  }
+  for (int64_t t = t0; t < ntiles; t += gridDim.x) {
     const int64_t tt = t - edges;
     const int c = (int)(tt / T);
     const int64_t j = tt - (int64_t)c * T;
@@ -126,7 +128,8 @@ static hipError_t fused_launch(const RankPtrs& P, int p, int64_t n, hipStream_t 
   for (int c = 0; c < p; ++c) {
     const int64_t lo = host_chunk_lo(0, n, p, c), hi = host_chunk_lo(0, n, p, c + 1);
     T = std::max<int64_t>(T, (tiled_vecs_in(lo, hi, V) + kBlock - 1) / kBlock);
-    if (hi > lo && (lo % V != 0 || hi % V != 0 || vecs_in(lo, hi, V) == 0)) edges = 1;
+    if (hi > lo && (lo % V != 0 || hi % V != 0 || vecs_in(lo, hi, V) == 0))
+      edges = (p + kWavesPerBlock - 1) / kWavesPerBlock;     // a wave per chunk
   }
   const int64_t ntiles = edges + (int64_t)p * T;
   const int grid = (int)std::min<int64_t>(ntiles, kMaxGrid);
@@ -198,47 +201,55 @@ __device__ __forceinline__ void hier_segment(const ChunkGeo& gi, int M, int seg,
   *hi = chunk_hi(sg, *d);
 }
 
-// Element i of segment (c, d) in the two-level order, stored to every rank (lp:
-// the LDS copy of the rank pointers).
+// The segments' edge elements, one segment per wave (edge_wave): edge workgroup
+// w carries segments 4w .. 4w + 3.  Lane k folds element k of segment (c, d) in
+// the two-level order and stores the result to every rank.
 template <int DT, int OP>
-__device__ __forceinline__ void hier_element(void* const* lp, int p, int G, int M, int c, int d,
-                                             int64_t i) {
+__device__ __forceinline__ void hier_edges(const RankPtrs& P, const ChunkGeo& gi, int p, int G,
+                                           int M, int64_t w) {
   typedef Elem<DT> E;
   typedef Fold<DT, OP, false> F;
-  typename E::S total = 0;
-  for (int k2 = 0; k2 < M; ++k2) {
-    const int q = d + k2 < M ? d + k2 : d + k2 - M;
-    const typename E::S acc = fold_element<F, DT>(lp, q * G, G, c, i, p);
-    total = k2 == 0 ? acc : comb1<DT, OP>(total, acc);
-  }
-  for (int r = 0; r < p; ++r) st1<DT>(lp[r], i, total);
+  __shared__ void* lp[kMaxRanks];
+  __shared__ EdgeSlab<DT> slab[kWavesPerBlock];
+  load_rank_table(lp, P, p);
+  const int wave = (int)(threadIdx.x / kWave);
+  const int64_t sw = w * kWavesPerBlock + wave;
+  int c = 0, d = 0;
+  int64_t lo = 0, hi = 0;
+  if (sw < (int64_t)G * M) hier_segment(gi, M, (int)sw, &c, &d, &lo, &hi);
+  edge_wave<DT>(lp, p, lo, hi, slab[wave], [&](EdgeSlab<DT>& sl, int k) {
+    typename E::S total = 0;
+    for (int k2 = 0; k2 < M; ++k2) {
+      const int q = d + k2 < M ? d + k2 : d + k2 - M;
+      typename E::S acc = F::start1(sl.x[k][q * G + c], p);
+      for (int k1 = 1; k1 < G; ++k1) {
+        const int l = c + k1 < G ? c + k1 : c + k1 - G;
+        acc = F::step1(acc, sl.x[k][q * G + l], p);
+      }
+      total = k2 == 0 ? acc : comb1<DT, OP>(total, acc);
+    }
+    for (int r = 0; r < p; ++r) sl.x[k][r] = total;
+    sl.mask[k] = all_ranks(p);
+  });
 }
 
 // Tiles as in k_fused, over the G*M segments; the segments' edge elements, when
-// there are any (edges = 1), all go to workgroup 0 as in k_fused.
+// there are any, go to the first `edges` workgroups, a segment per wave, as in
+// k_fused.
 template <int DT, int OP, bool NT>
 __global__ __launch_bounds__(kBlock) void k_fused_hier(RankPtrs P, ChunkGeo gi, int p, int G,
                                                        int M, int64_t T, int64_t ntiles,
                                                        int edges) {
   typedef Fold<DT, OP, false> F;
   constexpr int V = Elem<DT>::V;
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+  int64_t t0 = blockIdx.x;
+  if (t0 < edges) {             // edge workgroups first, outside the tile loop (as in k_fused)
+    hier_edges<DT, OP>(P, gi, p, G, M, t0);
+    t0 += gridDim.x;
+  }
+  for (int64_t t = t0; t < ntiles; t += gridDim.x) {
     int c, d;
     int64_t lo, hi;
-    if (t < edges) {
-      constexpr int kPer = 2 * V - 2;
-      __shared__ void* lp[kMaxRanks];
-      load_rank_table(lp, P, p);
-      for (int e = threadIdx.x; e < G * M * kPer; e += kBlock) {
-        const int seg = e / kPer, k = e - seg * kPer;
-        hier_segment(gi, M, seg, &c, &d, &lo, &hi);
-        const Span sp = split_span<V>(lo, hi);
-        const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
-        if (k < nh + nt)
-          hier_element<DT, OP>(lp, p, G, M, c, d, k < nh ? lo + k : sp.tail_lo + (k - nh));
-      }
-      continue;
-    }
     const int64_t tt = t - edges;
     const int seg = (int)(tt / T);
     const int64_t j = tt - (int64_t)seg * T;
@@ -274,7 +285,8 @@ static hipError_t fused_hier_launch(const RankPtrs& P, int p, int64_t n, int G, 
     for (int d = 0; d < M; ++d) {
       const int64_t lo = host_chunk_lo(clo, len, M, d), hi = host_chunk_lo(clo, len, M, d + 1);
       T = std::max<int64_t>(T, (tiled_vecs_in(lo, hi, V) + kBlock - 1) / kBlock);
-      if (hi > lo && (lo % V != 0 || hi % V != 0 || vecs_in(lo, hi, V) == 0)) edges = 1;
+      if (hi > lo && (lo % V != 0 || hi % V != 0 || vecs_in(lo, hi, V) == 0))
+        edges = (G * M + kWavesPerBlock - 1) / kWavesPerBlock;   // a wave per segment
     }
   }
   const int64_t ntiles = edges + (int64_t)G * M * T;

@@ -83,42 +83,55 @@ __device__ __forceinline__ void ride_hops(u32x4& acc, const RankPtrs& P, int p, 
   }
 }
 
-// Element i of chunk c carried through its hops on its own (the chunks'
-// unaligned edges), as ride_hops does for a vector: the receivers of a batch of
-// hops are loaded together (load_positions), then each is combined with the
-// running partial and written back.  lp is the LDS copy of the rank pointers.
+// The chunks' edge elements carried through their hops, one chunk per wave
+// (edge_wave): edge workgroup w carries chunks 4w .. 4w + 3.  Lane k runs
+// element k of chunk c through the hops as ride_hops does for a vector and
+// leaves what each rank ends with: a reduce-scatter's partials (each receiver's
+// after its hop, and the sender's divided term for an average), the finished
+// sum everywhere for an all-reduce (its partials are overwritten by the
+// all-gather), the owner's copy for an all-gather.
 template <int DT, int OP, int MODE>
-__device__ __forceinline__ void ride_element(void* const* lp, int p, int c, int64_t i) {
+__device__ __forceinline__ void ride_edges(const RankPtrs& P, const ChunkGeo& g, int p,
+                                           int64_t w) {
   typedef Elem<DT> E;
   constexpr bool kDiv = OP == kAvg && MODE != kRideAllGather;
+  __shared__ void* lp[kMaxRanks];
+  __shared__ EdgeSlab<DT> slab[kWavesPerBlock];
+  load_rank_table(lp, P, p);
+  const int wave = (int)(threadIdx.x / kWave);
+  const int64_t cw = w * kWavesPerBlock + wave;
+  const int c = cw < p ? (int)cw : 0;
+  const int64_t lo = cw < p ? chunk_lo(g, c) : 0, hi = cw < p ? chunk_hi(g, c) : 0;
   const int owner = c == 0 ? p - 1 : c - 1;
-  if (MODE == kRideAllGather) {
-    const typename E::S out = ld1<DT>(lp[owner], i);
-    for (int r = 0; r < p; ++r)
-      if (r != owner) st1<DT>(lp[r], i, out);
-    return;
-  }
-  typename E::S acc = ld1<DT>(lp[c], i);
-  if (kDiv) {
-    acc = E::div1(acc, p);
-    if (MODE == kRideReduceScatter) st1<DT>(lp[c], i, acc);
-  }
-  for (int h0 = 1; h0 < p; h0 += kRankBatch) {
-    typename E::S x[kRankBatch];
-    load_positions<DT>(x, lp, 0, p, c, h0, p, i);
-#pragma unroll
-    for (int u = 0; u < kRankBatch; ++u) {
-      if (h0 + u >= p) break;
-      const int r = c + h0 + u < p ? c + h0 + u : c + h0 + u - p;
-      acc = comb1<DT, OP>(acc, kDiv ? E::div1(x[u], p) : x[u]);
-      st1<DT>(lp[r], i, acc);
+  edge_wave<DT>(lp, p, lo, hi, slab[wave], [&](EdgeSlab<DT>& sl, int k) {
+    if (MODE == kRideAllGather) {
+      const typename E::S out = sl.x[k][owner];
+      for (int r = 0; r < p; ++r) sl.x[k][r] = out;
+      sl.mask[k] = all_ranks(p) & ~(1ull << owner);
+      return;
     }
-  }
-  if (MODE == kRideAllReduce) {
-    asm volatile("" ::: "memory");
-    for (int r = 0; r < p; ++r)
-      if (r != owner) st1<DT>(lp[r], i, acc);
-  }
+    typename E::S acc = sl.x[k][c];
+    uint64_t m = 0;
+    if (kDiv) {
+      acc = E::div1(acc, p);
+      if (MODE == kRideReduceScatter) {
+        sl.x[k][c] = acc;
+        m |= 1ull << c;
+      }
+    }
+    for (int h = 1; h < p; ++h) {
+      const int r = c + h < p ? c + h : c + h - p;
+      const typename E::S x = sl.x[k][r];
+      acc = comb1<DT, OP>(acc, kDiv ? E::div1(x, p) : x);
+      sl.x[k][r] = acc;
+      m |= 1ull << r;
+    }
+    if (MODE == kRideAllReduce) {
+      for (int r = 0; r < p; ++r) sl.x[k][r] = acc;
+      m = all_ranks(p);
+    }
+    sl.mask[k] = m;
+  });
 }
 
 // Slice q = (chunk c, slice k of that chunk): tiles k*tps .. (k+1)*tps - 1 of
@@ -126,9 +139,9 @@ __device__ __forceinline__ void ride_element(void* const* lp, int p, int c, int6
 // tile by tile.  The partials of the reduce-scatter are written before the
 // all-gather overwrites them (a compiler barrier keeps those stores: they are
 // the step states, not dead stores).  When the chunks have unaligned edge
-// elements (edges = 1), workgroup 0 carries them all, element by element, while
-// the slices run (in each chunk's first slice they were a second chain of
-// round trips after its vectors).
+// elements, the first `edges` workgroups carry them, a chunk per wave, while
+// the slices run (in each chunk's first slice they were a second chain of round
+// trips after its vectors).
 template <int DT, int OP, int MODE>
 __global__ __launch_bounds__(kBlock) void k_rider(RankPtrs P, ChunkGeo g, int p, int64_t T,
                                                   int64_t tps, int64_t K, int64_t nslices,
@@ -136,20 +149,12 @@ __global__ __launch_bounds__(kBlock) void k_rider(RankPtrs P, ChunkGeo g, int p,
   typedef Elem<DT> E;
   constexpr int V = E::V;
   constexpr bool kDiv = OP == kAvg && MODE != kRideAllGather;
-  for (int64_t q = blockIdx.x; q < nslices; q += gridDim.x) {
-    if (q < edges) {
-      constexpr int kPer = 2 * V - 2;
-      __shared__ void* lp[kMaxRanks];
-      load_rank_table(lp, P, p);
-      for (int e = threadIdx.x; e < p * kPer; e += kBlock) {
-        const int c = e / kPer, k = e - c * kPer;
-        const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
-        const Span sp = split_span<V>(lo, hi);
-        const int64_t nh = sp.head_hi - lo, nt = hi - sp.tail_lo;
-        if (k < nh + nt) ride_element<DT, OP, MODE>(lp, p, c, k < nh ? lo + k : sp.tail_lo + (k - nh));
-      }
-      continue;
-    }
+  int64_t q0 = blockIdx.x;
+  if (q0 < edges) {             // edge workgroups first, outside the slice loop (as in k_fused)
+    ride_edges<DT, OP, MODE>(P, g, p, q0);
+    q0 += gridDim.x;
+  }
+  for (int64_t q = q0; q < nslices; q += gridDim.x) {
     const int64_t qq = q - edges;
     const int c = (int)(qq / K);
     const int64_t k = qq - (int64_t)c * K;
@@ -195,7 +200,8 @@ static hipError_t rider_launch(const RankPtrs& P, int p, int64_t n, int64_t slic
   for (int c = 0; c < p; ++c) {
     const int64_t lo = host_chunk_lo(0, n, p, c), hi = host_chunk_lo(0, n, p, c + 1);
     T = std::max<int64_t>(T, (tiled_vecs_in(lo, hi, V) + kBlock - 1) / kBlock);
-    if (hi > lo && (lo % V != 0 || hi % V != 0 || vecs_in(lo, hi, V) == 0)) edges = 1;
+    if (hi > lo && (lo % V != 0 || hi % V != 0 || vecs_in(lo, hi, V) == 0))
+      edges = (p + kWavesPerBlock - 1) / kWavesPerBlock;     // a wave per chunk
   }
   const int64_t tile_elems = (int64_t)kBlock * V;
   const int64_t tps = slice_elems > 0 ? std::max<int64_t>(1, (slice_elems + tile_elems - 1) / tile_elems)

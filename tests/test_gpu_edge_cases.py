@@ -10,6 +10,10 @@
   rank holds +0, so every algorithm's one inexact hop is that tie, and half of
   the ties round down to even, half up;
 * int32 sums that wrap past 2**31 both ways;
+* chunk edges: sizes where most chunks start and end inside a 16-byte vector,
+  up to p = 64, so the one-pass, two-level and slice-carrying kernels fold edge
+  elements in every edge wave of several edge workgroups, in each of their
+  modes (all-reduce, reduce-scatter, all-gather) and reductions;
 * p = 2 with 35 * 2**30 bfloat16 elements per rank (70 GiB, 140 GiB in all):
   more tiles than one dispatch can hold, so the one-pass, pipelined and step
   kernels take their grid-stride loops; checked on windows against the oracle.
@@ -143,6 +147,61 @@ def test_int32_wraps(algo):
     exact = np.sum(np.stack(xs).astype(np.int64), axis=0)
     assert np.array_equal(want.astype(np.int64), (exact + 2 ** 31) % 2 ** 32 - 2 ** 31)
     assert np.count_nonzero(np.abs(exact) >= 2 ** 31) > n // 4
+
+
+# ------------------------------------------------------------ chunk edges
+
+VEC = {"int32": 4, "float32": 4, "bfloat16": 8, "float16": 8, "float64": 2, "int64": 2}
+EDGE_CASES = [(2, 37, "bfloat16", "sum"), (5, 1_003, "int64", "sum"),
+              (13, 20_011, "float16", "avg"), (33, 10_007, "float64", "avg"),
+              (63, 65_537, "bfloat16", "sum"), (64, 4_133, "float32", "max"),
+              (64, 524_365, "bfloat16", "sum")]
+
+
+def _edge_chunks(n, p, dtype):
+    v = VEC[dtype]
+    return sum(1 for lo, hi in oracle.chunk_bounds(n, p) if hi > lo and (lo % v or hi % v))
+
+
+@pytest.mark.parametrize("p,n,dtype,op", EDGE_CASES)
+def test_chunk_edges_every_mode(p, n, dtype, op):
+    require_gpu()
+    # the case is what it claims: most chunks have edge elements
+    assert _edge_chunks(n, p, dtype) >= p // 2
+    xs = inputs.make_inputs(p, n, dtype, seed=p * 7 + n, sigma=1.0)
+    g = next(d for d in range(2, p + 1) if p % d == 0)      # ranks per node
+    ring = oracle.ring_fold(xs, dtype, op=op)
+    for algo, want in (("fused", ring), ("ring_pipelined", ring),
+                       ("hier_fused", oracle.hier_fold(xs, dtype, g, op=op))):
+        t = to_dev(xs, dtype)
+        print(f"[case] edges AR algo={algo} p={p} n={n} {dtype} {op}", flush=True)
+        B.ra_allreduce_ex(t, algo=algo, op=op, **({"group": g} if algo == "hier_fused" else {}))
+        B.ra_stream_status()
+        for r, got in enumerate(from_dev(t, dtype)):
+            assert same_bits(got, want, dtype), f"{algo} rank {r} at {first_diff(got, want, dtype)}"
+    # reduce-scatter: the one-pass kernel writes owned chunks only, the
+    # slice-carrying ring leaves the step-by-step partials (checked where the
+    # oracle's closed form for every rank stays quick)
+    for algo in ("fused", "ring_pipelined"):
+        if algo == "ring_pipelined" and p * p * n > 50_000_000:
+            continue
+        t = to_dev(xs, dtype)
+        print(f"[case] edges RS algo={algo} p={p} n={n} {dtype} {op}", flush=True)
+        B.ra_reduce_scatter_ex(t, algo=algo, op=op)
+        B.ra_stream_status()
+        for r, got in enumerate(from_dev(t, dtype)):
+            want = (oracle.rs_owned(xs, dtype, r, op=op) if algo == "fused"
+                    else oracle.rs_partial(xs, dtype, r, op=op))
+            assert same_bits(got, want, dtype), f"{algo} RS rank {r} at {first_diff(got, want, dtype)}"
+    # all-gather on arbitrary buffers: only owned chunks may be read
+    gathered, _ = oracle.all_gather(xs, dtype)
+    for algo in ("fused", "ring_pipelined"):
+        t = to_dev(xs, dtype)
+        print(f"[case] edges AG algo={algo} p={p} n={n} {dtype}", flush=True)
+        B.ra_all_gather_ex(t, algo=algo)
+        B.ra_stream_status()
+        for r, got in enumerate(from_dev(t, dtype)):
+            assert same_bits(got, gathered[r], dtype), f"{algo} AG rank {r} at {first_diff(got, gathered[r], dtype)}"
 
 
 # ------------------------------------------------------------ beyond one dispatch
