@@ -599,6 +599,21 @@ struct EdgeSlab {
   uint64_t mask[K];
 };
 
+// LDS of an edge workgroup: the rank-pointer table and one slab per wave.  It
+// is the kernel's dynamic LDS, sized at launch (sizeof, or 0 when no chunk has
+// edge elements), so launches without edge elements allocate none.
+template <int DT>
+struct EdgeLds {
+  void* lp[kMaxRanks];
+  EdgeSlab<DT> slab[kWavesPerBlock];
+};
+
+template <int DT>
+__device__ __forceinline__ EdgeLds<DT>& edge_lds() {
+  extern __shared__ __align__(16) unsigned char ra_dynamic_lds[];
+  return *reinterpret_cast<EdgeLds<DT>*>(ra_dynamic_lds);
+}
+
 // Bit r set for every rank r < p.
 __device__ __forceinline__ uint64_t all_ranks(int p) {
   return p >= 64 ? ~0ull : (1ull << p) - 1;

@@ -36,15 +36,15 @@ __device__ __forceinline__ void fused_edges(const RankPtrs& P, const ChunkGeo& g
                                             int64_t w) {
   typedef Elem<DT> E;
   typedef Fold<DT, OP, WIDE> F;
-  __shared__ void* lp[kMaxRanks];
-  __shared__ EdgeSlab<DT> slab[kWavesPerBlock];
+  EdgeLds<DT>& L = edge_lds<DT>();
+  void** lp = L.lp;
   load_rank_table(lp, P, p);
   const int wave = (int)(threadIdx.x / kWave);
   const int64_t cw = w * kWavesPerBlock + wave;
   const int c = cw < p ? (int)cw : 0;
   const int64_t lo = cw < p ? chunk_lo(g, c) : 0, hi = cw < p ? chunk_hi(g, c) : 0;
   const int owner = c == 0 ? p - 1 : c - 1;
-  edge_wave<DT>(lp, p, lo, hi, slab[wave], [&](EdgeSlab<DT>& sl, int k) {
+  edge_wave<DT>(lp, p, lo, hi, L.slab[wave], [&](EdgeSlab<DT>& sl, int k) {
     typename E::S out;
     if (MODE == kAllGather) {
       out = sl.x[k][owner];
@@ -133,12 +133,13 @@ static hipError_t fused_launch(const RankPtrs& P, int p, int64_t n, hipStream_t 
   }
   const int64_t ntiles = edges + (int64_t)p * T;
   const int grid = (int)std::min<int64_t>(ntiles, kMaxGrid);
+  const unsigned lds = edges ? (unsigned)sizeof(EdgeLds<DT>) : 0u;
   *grid_used = grid;
   if (streaming(p, n, DT))
-    hipLaunchKernelGGL((k_fused<DT, OP, WIDE, true, MODE>), dim3(grid), dim3(kBlock), 0, s, P, g,
+    hipLaunchKernelGGL((k_fused<DT, OP, WIDE, true, MODE>), dim3(grid), dim3(kBlock), lds, s, P, g,
                        p, T, ntiles, edges);
   else
-    hipLaunchKernelGGL((k_fused<DT, OP, WIDE, false, MODE>), dim3(grid), dim3(kBlock), 0, s, P, g,
+    hipLaunchKernelGGL((k_fused<DT, OP, WIDE, false, MODE>), dim3(grid), dim3(kBlock), lds, s, P, g,
                        p, T, ntiles, edges);
   return hipGetLastError();
 }
@@ -209,15 +210,15 @@ __device__ __forceinline__ void hier_edges(const RankPtrs& P, const ChunkGeo& gi
                                            int M, int64_t w) {
   typedef Elem<DT> E;
   typedef Fold<DT, OP, false> F;
-  __shared__ void* lp[kMaxRanks];
-  __shared__ EdgeSlab<DT> slab[kWavesPerBlock];
+  EdgeLds<DT>& L = edge_lds<DT>();
+  void** lp = L.lp;
   load_rank_table(lp, P, p);
   const int wave = (int)(threadIdx.x / kWave);
   const int64_t sw = w * kWavesPerBlock + wave;
   int c = 0, d = 0;
   int64_t lo = 0, hi = 0;
   if (sw < (int64_t)G * M) hier_segment(gi, M, (int)sw, &c, &d, &lo, &hi);
-  edge_wave<DT>(lp, p, lo, hi, slab[wave], [&](EdgeSlab<DT>& sl, int k) {
+  edge_wave<DT>(lp, p, lo, hi, L.slab[wave], [&](EdgeSlab<DT>& sl, int k) {
     typename E::S total = 0;
     for (int k2 = 0; k2 < M; ++k2) {
       const int q = d + k2 < M ? d + k2 : d + k2 - M;
@@ -291,12 +292,13 @@ static hipError_t fused_hier_launch(const RankPtrs& P, int p, int64_t n, int G, 
   }
   const int64_t ntiles = edges + (int64_t)G * M * T;
   const int grid = (int)std::min<int64_t>(ntiles, kMaxGrid);
+  const unsigned lds = edges ? (unsigned)sizeof(EdgeLds<DT>) : 0u;
   *grid_used = grid;
   if (streaming(p, n, DT))
-    hipLaunchKernelGGL((k_fused_hier<DT, OP, true>), dim3(grid), dim3(kBlock), 0, s, P, gi, p, G,
+    hipLaunchKernelGGL((k_fused_hier<DT, OP, true>), dim3(grid), dim3(kBlock), lds, s, P, gi, p, G,
                        M, T, ntiles, edges);
   else
-    hipLaunchKernelGGL((k_fused_hier<DT, OP, false>), dim3(grid), dim3(kBlock), 0, s, P, gi, p, G,
+    hipLaunchKernelGGL((k_fused_hier<DT, OP, false>), dim3(grid), dim3(kBlock), lds, s, P, gi, p, G,
                        M, T, ntiles, edges);
   return hipGetLastError();
 }

@@ -95,15 +95,15 @@ __device__ __forceinline__ void ride_edges(const RankPtrs& P, const ChunkGeo& g,
                                            int64_t w) {
   typedef Elem<DT> E;
   constexpr bool kDiv = OP == kAvg && MODE != kRideAllGather;
-  __shared__ void* lp[kMaxRanks];
-  __shared__ EdgeSlab<DT> slab[kWavesPerBlock];
+  EdgeLds<DT>& L = edge_lds<DT>();
+  void** lp = L.lp;
   load_rank_table(lp, P, p);
   const int wave = (int)(threadIdx.x / kWave);
   const int64_t cw = w * kWavesPerBlock + wave;
   const int c = cw < p ? (int)cw : 0;
   const int64_t lo = cw < p ? chunk_lo(g, c) : 0, hi = cw < p ? chunk_hi(g, c) : 0;
   const int owner = c == 0 ? p - 1 : c - 1;
-  edge_wave<DT>(lp, p, lo, hi, slab[wave], [&](EdgeSlab<DT>& sl, int k) {
+  edge_wave<DT>(lp, p, lo, hi, L.slab[wave], [&](EdgeSlab<DT>& sl, int k) {
     if (MODE == kRideAllGather) {
       const typename E::S out = sl.x[k][owner];
       for (int r = 0; r < p; ++r) sl.x[k][r] = out;
@@ -210,7 +210,8 @@ static hipError_t rider_launch(const RankPtrs& P, int p, int64_t n, int64_t slic
   const int64_t nslices = edges + (int64_t)p * K;
   const int grid = (int)std::min<int64_t>(nslices, kMaxGrid);
   *grid_used = grid;
-  hipLaunchKernelGGL((k_rider<DT, OP, MODE>), dim3(grid), dim3(kBlock), 0, s, P, g, p, T, tps, K,
+  const unsigned lds = edges ? (unsigned)sizeof(EdgeLds<DT>) : 0u;
+  hipLaunchKernelGGL((k_rider<DT, OP, MODE>), dim3(grid), dim3(kBlock), lds, s, P, g, p, T, tps, K,
                      nslices, edges, stress);
   return hipGetLastError();
 }
