@@ -417,7 +417,6 @@ __device__ __forceinline__ void st1(void* base, int64_t i, typename Elem<DT>::S 
   reinterpret_cast<typename Elem<DT>::S*>(base)[i] = v;
 }
 
-
 // Vector vt + lane of every rank (vt wave-uniform), folded or stored.
 //
 // The rank index is wave-uniform, so each rank's pointer is a scalar load from
@@ -639,10 +638,11 @@ __device__ __forceinline__ void edge_wave(void* const* lp, int p, int64_t lo, in
   const int lane = (int)(threadIdx.x % kWave);
   auto index = [&](int k) { return k < nh ? lo + k : sp.tail_lo + (k - nh); };
   if (ne > 0 && lane < p) {
-    // kEdgePass elements' loads at a time: all K at once would raise every
-    // kernel's register count (the one-pass kernel's from 45 to 68 for bfloat16,
-    // one wave per SIMD less).  Elements past the last repeat it (loaded, not
-    // used), so the loads need no guard.
+    // kEdgePass elements' loads at a time, which keeps the callers at their tile
+    // code's register counts (all K at once took up to 61 registers and ran no
+    // faster: p = 64 with 524,365 bfloat16 per rank, 31.0 us either way).
+    // Elements past the last repeat it (loaded, not used), so the loads need no
+    // guard.
     for (int k0 = 0; k0 < ne; k0 += kEdgePass) {
       typename Elem<DT>::S v[kEdgePass];
 #pragma unroll
@@ -657,9 +657,6 @@ __device__ __forceinline__ void edge_wave(void* const* lp, int p, int64_t lo, in
   if (lane < ne) fold(sl, lane);
   __syncthreads();
   if (ne > 0 && lane < p) {
-    // one element at a time: stores need no wait, and unrolled, the addresses
-    // of all K elements held at once cost registers in every kernel that calls this
-#pragma unroll 1
     for (int k = 0; k < ne; ++k)
       if ((sl.mask[k] >> lane) & 1) st1<DT>(lp[lane], index(k), sl.x[k][lane]);
   }
