@@ -66,33 +66,33 @@ __device__ __forceinline__ void fused_edges(const RankPtrs& P, const ChunkGeo& g
   });
 }
 
-// Tile t = (chunk c, tile j of that chunk), one 16-byte vector per thread.
-// For every element of the tile: acc = x_c; acc = acc + x_{c+1}; ...;
-// acc = acc + x_{c+p-1} (indices mod p, rounding each addition), the order in
-// which the step-by-step ring accumulates chunk c, so the bits match.  OP and
-// WIDE choose the reduction and the accumulation type (Fold in ra_elem.h).
-// When the chunks have edge elements, the first `edges` workgroups fold them,
-// one chunk per wave, while the tiles run: left in each chunk's first tile they
-// were a second memory round trip after its vectors, and in a launch whose
-// workgroups all run at once the slowest workgroup sets the time (p = 9,
-// 1,000,003 int32 per rank: 19.4 us against 17.4 with chunk starts on lines,
-// before the move).
+// Tile t = (chunk c, tile j of that chunk), one 16-byte vector per thread,
+// numbered by tile_of.  For every element of the tile: acc = x_c;
+// acc = acc + x_{c+1}; ...; acc = acc + x_{c+p-1} (indices mod p, rounding each
+// addition), the order in which the step-by-step ring accumulates chunk c, so
+// the bits match.  OP and WIDE choose the reduction and the accumulation type
+// (Fold in ra_elem.h).  When the chunks have edge elements, edge workgroups
+// e0 .. e0 + edges - 1 (placed by edge_start) fold them, one chunk per wave,
+// while the tiles run, and the other workgroups take the tiles in order: left in
+// each chunk's first tile they were a second memory round trip after its
+// vectors, and in a launch whose workgroups all run at once the slowest
+// workgroup sets the time (p = 9, 1,000,003 int32 per rank: 19.4 us against
+// 17.4 with chunk starts on lines, before the move).
 template <int DT, int OP, bool WIDE, bool NT, int MODE>
 __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p, int64_t T,
-                                                  int64_t ntiles, int edges) {
+                                                  int64_t ntiles, int edges, int64_t e0,
+                                                  int tail_last) {
   typedef Fold<DT, OP, WIDE> F;
   constexpr int V = Elem<DT>::V;
-  int64_t t0 = blockIdx.x;
-  // the edge workgroups first, outside the tile loop: inside it, values the
+  const int64_t b = blockIdx.x;
+  // the edge workgroups' work outside the tile loop: inside it, values the
   // compiler keeps live across the loop added to the edge code's registers
-  if (t0 < edges) {
-    fused_edges<DT, OP, WIDE, MODE>(P, g, p, t0);
-    t0 += gridDim.x;
-  }
-  for (int64_t t = t0; t < ntiles; t += gridDim.x) {
-    const int64_t tt = t - edges;
-    const int c = (int)(tt / T);
-    const int64_t j = tt - (int64_t)c * T;
+  if (b >= e0 && b < e0 + edges) fused_edges<DT, OP, WIDE, MODE>(P, g, p, b - e0);
+  for (int64_t v = b; v < ntiles + edges; v += gridDim.x) {
+    if (v >= e0 && v < e0 + edges) continue;
+    int c;
+    int64_t j;
+    tile_of(v < e0 ? v : v - edges, T, p, tail_last, &c, &j);
     const int owner = c == 0 ? p - 1 : c - 1;
     const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
     const Span sp = split_span<V>(lo, hi);
@@ -123,24 +123,27 @@ template <int DT, int OP, bool WIDE, int MODE>
 static hipError_t fused_launch(const RankPtrs& P, int p, int64_t n, hipStream_t s, int* grid_used) {
   const int V = Elem<DT>::V;
   const ChunkGeo g = make_geo(0, n, p);
-  int64_t T = 1;
+  int64_t widest = 0;
   int edges = 0;
   for (int c = 0; c < p; ++c) {
     const int64_t lo = host_chunk_lo(0, n, p, c), hi = host_chunk_lo(0, n, p, c + 1);
-    T = std::max<int64_t>(T, (tiled_vecs_in(lo, hi, V) + kBlock - 1) / kBlock);
+    widest = std::max<int64_t>(widest, tiled_vecs_in(lo, hi, V));
     if (hi > lo && (lo % V != 0 || hi % V != 0 || vecs_in(lo, hi, V) == 0))
       edges = (p + kWavesPerBlock - 1) / kWavesPerBlock;     // a wave per chunk
   }
-  const int64_t ntiles = edges + (int64_t)p * T;
-  const int grid = (int)std::min<int64_t>(ntiles, kMaxGrid);
+  const int64_t T = std::max<int64_t>(1, (widest + kBlock - 1) / kBlock);
+  const int tail_last = short_tail(widest, kBlock);          // the chunks' last tiles are short
+  const int64_t ntiles = (int64_t)p * T;
+  const int grid = (int)std::min<int64_t>(ntiles + edges, kMaxGrid);
+  const int64_t e0 = edge_start(ntiles, p, tail_last, edges, grid);
   const unsigned lds = edges ? (unsigned)sizeof(EdgeLds<DT>) : 0u;
   *grid_used = grid;
   if (streaming(p, n, DT))
     hipLaunchKernelGGL((k_fused<DT, OP, WIDE, true, MODE>), dim3(grid), dim3(kBlock), lds, s, P, g,
-                       p, T, ntiles, edges);
+                       p, T, ntiles, edges, e0, tail_last);
   else
     hipLaunchKernelGGL((k_fused<DT, OP, WIDE, false, MODE>), dim3(grid), dim3(kBlock), lds, s, P, g,
-                       p, T, ntiles, edges);
+                       p, T, ntiles, edges, e0, tail_last);
   return hipGetLastError();
 }
 
@@ -235,25 +238,23 @@ __device__ __forceinline__ void hier_edges(const RankPtrs& P, const ChunkGeo& gi
 }
 
 // Tiles as in k_fused, over the G*M segments; the segments' edge elements, when
-// there are any, go to the first `edges` workgroups, a segment per wave, as in
-// k_fused.
+// there are any, go to edge workgroups e0 .. e0 + edges - 1, a segment per wave,
+// as in k_fused.
 template <int DT, int OP, bool NT>
 __global__ __launch_bounds__(kBlock) void k_fused_hier(RankPtrs P, ChunkGeo gi, int p, int G,
                                                        int M, int64_t T, int64_t ntiles,
-                                                       int edges) {
+                                                       int edges, int64_t e0, int tail_last) {
   typedef Fold<DT, OP, false> F;
   constexpr int V = Elem<DT>::V;
-  int64_t t0 = blockIdx.x;
-  if (t0 < edges) {             // edge workgroups first, outside the tile loop (as in k_fused)
-    hier_edges<DT, OP>(P, gi, p, G, M, t0);
-    t0 += gridDim.x;
-  }
-  for (int64_t t = t0; t < ntiles; t += gridDim.x) {
+  const int64_t b = blockIdx.x;
+  if (b >= e0 && b < e0 + edges) hier_edges<DT, OP>(P, gi, p, G, M, b - e0);
+  for (int64_t v = b; v < ntiles + edges; v += gridDim.x) {
+    if (v >= e0 && v < e0 + edges) continue;
     int c, d;
     int64_t lo, hi;
-    const int64_t tt = t - edges;
-    const int seg = (int)(tt / T);
-    const int64_t j = tt - (int64_t)seg * T;
+    int seg;
+    int64_t j;
+    tile_of(v < e0 ? v : v - edges, T, G * M, tail_last, &seg, &j);
     hier_segment(gi, M, seg, &c, &d, &lo, &hi);
     const Span sp = split_span<V>(lo, hi);
     const int64_t vt = sp.vb + j * kBlock;          // the tile's first vector
@@ -279,27 +280,30 @@ static hipError_t fused_hier_launch(const RankPtrs& P, int p, int64_t n, int G, 
   const int V = Elem<DT>::V;
   const int M = p / G;
   const ChunkGeo gi = make_geo(0, n, G);
-  int64_t T = 1;
+  int64_t widest = 0;
   int edges = 0;
   for (int c = 0; c < G; ++c) {
     const int64_t clo = host_chunk_lo(0, n, G, c), len = host_chunk_lo(0, n, G, c + 1) - clo;
     for (int d = 0; d < M; ++d) {
       const int64_t lo = host_chunk_lo(clo, len, M, d), hi = host_chunk_lo(clo, len, M, d + 1);
-      T = std::max<int64_t>(T, (tiled_vecs_in(lo, hi, V) + kBlock - 1) / kBlock);
+      widest = std::max<int64_t>(widest, tiled_vecs_in(lo, hi, V));
       if (hi > lo && (lo % V != 0 || hi % V != 0 || vecs_in(lo, hi, V) == 0))
         edges = (G * M + kWavesPerBlock - 1) / kWavesPerBlock;   // a wave per segment
     }
   }
-  const int64_t ntiles = edges + (int64_t)G * M * T;
-  const int grid = (int)std::min<int64_t>(ntiles, kMaxGrid);
+  const int64_t T = std::max<int64_t>(1, (widest + kBlock - 1) / kBlock);
+  const int tail_last = short_tail(widest, kBlock);
+  const int64_t ntiles = (int64_t)G * M * T;
+  const int grid = (int)std::min<int64_t>(ntiles + edges, kMaxGrid);
+  const int64_t e0 = edge_start(ntiles, (int64_t)G * M, tail_last, edges, grid);
   const unsigned lds = edges ? (unsigned)sizeof(EdgeLds<DT>) : 0u;
   *grid_used = grid;
   if (streaming(p, n, DT))
     hipLaunchKernelGGL((k_fused_hier<DT, OP, true>), dim3(grid), dim3(kBlock), lds, s, P, gi, p, G,
-                       M, T, ntiles, edges);
+                       M, T, ntiles, edges, e0, tail_last);
   else
     hipLaunchKernelGGL((k_fused_hier<DT, OP, false>), dim3(grid), dim3(kBlock), lds, s, P, gi, p, G,
-                       M, T, ntiles, edges);
+                       M, T, ntiles, edges, e0, tail_last);
   return hipGetLastError();
 }
 

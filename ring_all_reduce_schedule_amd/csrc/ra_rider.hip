@@ -134,30 +134,31 @@ __device__ __forceinline__ void ride_edges(const RankPtrs& P, const ChunkGeo& g,
   });
 }
 
-// Slice q = (chunk c, slice k of that chunk): tiles k*tps .. (k+1)*tps - 1 of
-// the chunk, one 16-byte vector per thread per tile, carried through its hops
-// tile by tile.  The partials of the reduce-scatter are written before the
-// all-gather overwrites them (a compiler barrier keeps those stores: they are
-// the step states, not dead stores).  When the chunks have unaligned edge
-// elements, the first `edges` workgroups carry them, a chunk per wave, while
-// the slices run (in each chunk's first slice they were a second chain of round
-// trips after its vectors).
+// Slice q = (chunk c, slice k of that chunk), numbered by tile_of: tiles
+// k*tps .. (k+1)*tps - 1 of the chunk, one 16-byte vector per thread per tile,
+// carried through its hops tile by tile.  The partials of the reduce-scatter
+// are written before the all-gather overwrites them (a compiler barrier keeps
+// those stores: they are the step states, not dead stores).  When the chunks
+// have unaligned edge elements, edge workgroups (placed by edge_start) carry
+// them, a chunk per wave, while the slices run (in each chunk's first slice
+// they were a second chain of round trips after its vectors).
 template <int DT, int OP, int MODE>
 __global__ __launch_bounds__(kBlock) void k_rider(RankPtrs P, ChunkGeo g, int p, int64_t T,
                                                   int64_t tps, int64_t K, int64_t nslices,
-                                                  int edges, uint32_t stress) {
+                                                  int edges, int64_t e0, int tail_last,
+                                                  uint32_t stress) {
   typedef Elem<DT> E;
   constexpr int V = E::V;
   constexpr bool kDiv = OP == kAvg && MODE != kRideAllGather;
-  int64_t q0 = blockIdx.x;
-  if (q0 < edges) {             // edge workgroups first, outside the slice loop (as in k_fused)
-    ride_edges<DT, OP, MODE>(P, g, p, q0);
-    q0 += gridDim.x;
-  }
-  for (int64_t q = q0; q < nslices; q += gridDim.x) {
-    const int64_t qq = q - edges;
-    const int c = (int)(qq / K);
-    const int64_t k = qq - (int64_t)c * K;
+  // edge workgroups e0 .. e0 + edges - 1 carry the edge elements, outside the
+  // slice loop (as in k_fused); the other workgroups take the slices in order
+  const int64_t b = blockIdx.x;
+  if (b >= e0 && b < e0 + edges) ride_edges<DT, OP, MODE>(P, g, p, b - e0);
+  for (int64_t q = b; q < nslices + edges; q += gridDim.x) {
+    if (q >= e0 && q < e0 + edges) continue;
+    int c;
+    int64_t k;
+    tile_of(q < e0 ? q : q - edges, K, p, tail_last, &c, &k);
     const int owner = c == 0 ? p - 1 : c - 1;
     const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
     const Span sp = split_span<V>(lo, hi);
@@ -195,24 +196,27 @@ static hipError_t rider_launch(const RankPtrs& P, int p, int64_t n, int64_t slic
                                uint32_t stress, hipStream_t s, int* grid_used) {
   const int V = Elem<DT>::V;
   const ChunkGeo g = make_geo(0, n, p);
-  int64_t T = 1;
+  int64_t widest = 0;
   int edges = 0;
   for (int c = 0; c < p; ++c) {
     const int64_t lo = host_chunk_lo(0, n, p, c), hi = host_chunk_lo(0, n, p, c + 1);
-    T = std::max<int64_t>(T, (tiled_vecs_in(lo, hi, V) + kBlock - 1) / kBlock);
+    widest = std::max<int64_t>(widest, tiled_vecs_in(lo, hi, V));
     if (hi > lo && (lo % V != 0 || hi % V != 0 || vecs_in(lo, hi, V) == 0))
       edges = (p + kWavesPerBlock - 1) / kWavesPerBlock;     // a wave per chunk
   }
+  const int64_t T = std::max<int64_t>(1, (widest + kBlock - 1) / kBlock);
   const int64_t tile_elems = (int64_t)kBlock * V;
   const int64_t tps = slice_elems > 0 ? std::max<int64_t>(1, (slice_elems + tile_elems - 1) / tile_elems)
                                       : 1;
   const int64_t K = (T + tps - 1) / tps;
-  const int64_t nslices = edges + (int64_t)p * K;
-  const int grid = (int)std::min<int64_t>(nslices, kMaxGrid);
+  const int tail_last = short_tail(widest, kBlock * tps);    // the chunks' last slices are short
+  const int64_t nslices = (int64_t)p * K;
+  const int grid = (int)std::min<int64_t>(nslices + edges, kMaxGrid);
+  const int64_t e0 = edge_start(nslices, p, tail_last, edges, grid);
   *grid_used = grid;
   const unsigned lds = edges ? (unsigned)sizeof(EdgeLds<DT>) : 0u;
   hipLaunchKernelGGL((k_rider<DT, OP, MODE>), dim3(grid), dim3(kBlock), lds, s, P, g, p, T, tps, K,
-                     nslices, edges, stress);
+                     nslices, edges, e0, tail_last, stress);
   return hipGetLastError();
 }
 
