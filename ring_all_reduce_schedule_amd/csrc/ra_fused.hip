@@ -85,14 +85,7 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
   typedef Fold<DT, OP, WIDE> F;
   constexpr int V = Elem<DT>::V;
   const int64_t b = blockIdx.x;
-  // the edge workgroups' work outside the tile loop: inside it, values the
-  // compiler keeps live across the loop added to the edge code's registers
-  if (b >= e0 && b < e0 + edges) fused_edges<DT, OP, WIDE, MODE>(P, g, p, b - e0);
-  for (int64_t v = b; v < ntiles + edges; v += gridDim.x) {
-    if (v >= e0 && v < e0 + edges) continue;
-    int c;
-    int64_t j;
-    tile_of(v < e0 ? v : v - edges, T, p, tail_last, &c, &j);
+  auto tile = [&](int c, int64_t j) {
     const int owner = c == 0 ? p - 1 : c - 1;
     const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
     const Span sp = split_span<V>(lo, hi);
@@ -112,6 +105,28 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
       else
         store_all<NT>(P, p, vt, lane, out, MODE == kAllGather ? owner : -1);
     }
+  };
+  // launches with no edge elements and whole last tiles take a loop with none
+  // of the placement arithmetic: at one tile per workgroup it was a visible part
+  // of a small call (p = 64 with 8,192 bfloat16 per chunk: 25.9 us with this
+  // loop, 26.3 through the general one)
+  if (edges == 0 && !tail_last) {
+    const uint32_t T32 = (uint32_t)T;
+    for (int64_t t = b; t < ntiles; t += gridDim.x) {
+      const uint32_t c = (uint32_t)t / T32;
+      tile((int)c, (int64_t)((uint32_t)t - c * T32));
+    }
+    return;
+  }
+  // the edge workgroups' work outside the tile loop: inside it, values the
+  // compiler keeps live across the loop added to the edge code's registers
+  if (b >= e0 && b < e0 + edges) fused_edges<DT, OP, WIDE, MODE>(P, g, p, b - e0);
+  for (int64_t v = b; v < ntiles + edges; v += gridDim.x) {
+    if (v >= e0 && v < e0 + edges) continue;
+    int c;
+    int64_t j;
+    tile_of((uint32_t)(v < e0 ? v : v - edges), (uint32_t)T, (uint32_t)p, tail_last, &c, &j);
+    tile(c, j);
   }
 }
 
@@ -132,8 +147,10 @@ static hipError_t fused_launch(const RankPtrs& P, int p, int64_t n, hipStream_t 
       edges = (p + kWavesPerBlock - 1) / kWavesPerBlock;     // a wave per chunk
   }
   const int64_t T = std::max<int64_t>(1, (widest + kBlock - 1) / kBlock);
-  const int tail_last = short_tail(widest, kBlock);          // the chunks' last tiles are short
   const int64_t ntiles = (int64_t)p * T;
+  // the chunks' last tiles are short, in a launch whose tiles are all resident
+  const int tail_last = ntiles <= kResidentTiles && short_tail(widest, kBlock);
+  if (ntiles + edges > 0xFFFFFFFFll) return hipErrorInvalidValue;   // tile_of decodes 32 bits
   const int grid = (int)std::min<int64_t>(ntiles + edges, kMaxGrid);
   const int64_t e0 = edge_start(ntiles, p, tail_last, edges, grid);
   const unsigned lds = edges ? (unsigned)sizeof(EdgeLds<DT>) : 0u;
@@ -254,7 +271,8 @@ __global__ __launch_bounds__(kBlock) void k_fused_hier(RankPtrs P, ChunkGeo gi, 
     int64_t lo, hi;
     int seg;
     int64_t j;
-    tile_of(v < e0 ? v : v - edges, T, G * M, tail_last, &seg, &j);
+    tile_of((uint32_t)(v < e0 ? v : v - edges), (uint32_t)T, (uint32_t)(G * M), tail_last, &seg,
+            &j);
     hier_segment(gi, M, seg, &c, &d, &lo, &hi);
     const Span sp = split_span<V>(lo, hi);
     const int64_t vt = sp.vb + j * kBlock;          // the tile's first vector
@@ -292,8 +310,9 @@ static hipError_t fused_hier_launch(const RankPtrs& P, int p, int64_t n, int G, 
     }
   }
   const int64_t T = std::max<int64_t>(1, (widest + kBlock - 1) / kBlock);
-  const int tail_last = short_tail(widest, kBlock);
   const int64_t ntiles = (int64_t)G * M * T;
+  const int tail_last = ntiles <= kResidentTiles && short_tail(widest, kBlock);
+  if (ntiles + edges > 0xFFFFFFFFll) return hipErrorInvalidValue;   // tile_of decodes 32 bits
   const int grid = (int)std::min<int64_t>(ntiles + edges, kMaxGrid);
   const int64_t e0 = edge_start(ntiles, (int64_t)G * M, tail_last, edges, grid);
   const unsigned lds = edges ? (unsigned)sizeof(EdgeLds<DT>) : 0u;

@@ -128,6 +128,13 @@ inline int short_tail(int64_t vecs, int64_t tile) {
   return rem != 0 && 2 * rem <= tile;
 }
 
+// The most workgroups of 256 threads an MI355X holds at once (256 compute units,
+// 8 each).  Up to that many, a launch's workgroups are all placed in the first
+// rounds of the dispatcher, and which compute unit gets which tile is decided by
+// their order; beyond it, workgroups wait for free slots and the order of the
+// short tiles no longer decides anything (launches keep the plain order).
+constexpr int64_t kResidentTiles = 2048;
+
 // Where a launch's edge workgroups sit in its workgroup order (e0):
 // first, so their chains of round trips start at once, or -- when the segments'
 // last tiles are short (tail_last) -- right after the other tiles and before the

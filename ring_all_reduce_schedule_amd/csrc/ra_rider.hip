@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kBlock) void k_rider(RankPtrs P, ChunkGeo g, int p,
     if (q >= e0 && q < e0 + edges) continue;
     int c;
     int64_t k;
-    tile_of(q < e0 ? q : q - edges, K, p, tail_last, &c, &k);
+    tile_of((uint32_t)(q < e0 ? q : q - edges), (uint32_t)K, (uint32_t)p, tail_last, &c, &k);
     const int owner = c == 0 ? p - 1 : c - 1;
     const int64_t lo = chunk_lo(g, c), hi = chunk_hi(g, c);
     const Span sp = split_span<V>(lo, hi);
@@ -209,8 +209,10 @@ static hipError_t rider_launch(const RankPtrs& P, int p, int64_t n, int64_t slic
   const int64_t tps = slice_elems > 0 ? std::max<int64_t>(1, (slice_elems + tile_elems - 1) / tile_elems)
                                       : 1;
   const int64_t K = (T + tps - 1) / tps;
-  const int tail_last = short_tail(widest, kBlock * tps);    // the chunks' last slices are short
   const int64_t nslices = (int64_t)p * K;
+  // the chunks' last slices are short, in a launch whose slices are all resident
+  const int tail_last = nslices <= kResidentTiles && short_tail(widest, kBlock * tps);
+  if (nslices + edges > 0xFFFFFFFFll) return hipErrorInvalidValue;  // tile_of decodes 32 bits
   const int grid = (int)std::min<int64_t>(nslices + edges, kMaxGrid);
   const int64_t e0 = edge_start(nslices, p, tail_last, edges, grid);
   *grid_used = grid;
