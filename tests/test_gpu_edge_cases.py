@@ -14,6 +14,9 @@
   up to p = 64, so the one-pass, two-level and slice-carrying kernels fold edge
   elements in every edge wave of several edge workgroups, in each of their
   modes (all-reduce, reduce-scatter, all-gather) and reductions;
+* short last tiles: sizes at which those launches number each chunk's short
+  last tile after the others, with and without edge workgroups, and sizes just
+  outside that rule;
 * p = 2 with 35 * 2**30 bfloat16 elements per rank (70 GiB, 140 GiB in all):
   more tiles than one dispatch can hold, so the one-pass, pipelined and step
   kernels take their grid-stride loops; checked on windows against the oracle.
@@ -202,6 +205,48 @@ def test_chunk_edges_every_mode(p, n, dtype, op):
         B.ra_stream_status()
         for r, got in enumerate(from_dev(t, dtype)):
             assert same_bits(got, gathered[r], dtype), f"{algo} AG rank {r} at {first_diff(got, gathered[r], dtype)}"
+
+
+# Sizes at which the one-pass, two-level and slice-carrying launches number each
+# chunk's short last tile after the others (at most 2048 tiles, last tiles at
+# most half full), with and without edge workgroups between the whole and the
+# short tiles, and one where the last tiles are fuller and the order is plain.
+SHORT_TAIL_CASES = [(64, 528_384, "bfloat16"),      # 5 tiles per chunk, the last 8 vectors
+                    (64, 524_365, "bfloat16"),      # the same with edge elements
+                    (16, 2_097_215, "float32"),     # 129 tiles per chunk: more than 2048 in all
+                    (64, 1_000_003, "bfloat16"),    # last tiles 62% full, edge elements
+                    (5, 5 * 1029 * 4, "int32")]     # 5 tiles per chunk, the last a few vectors
+
+
+@pytest.mark.parametrize("p,n,dtype", SHORT_TAIL_CASES)
+def test_short_last_tiles_every_mode(p, n, dtype):
+    require_gpu()
+    xs = inputs.make_inputs(p, n, dtype, seed=p * 13 + n, sigma=1.0)
+    g = next(d for d in range(2, p + 1) if p % d == 0)
+    ring = oracle.ring_fold(xs, dtype)
+    for algo, want in (("fused", ring), ("ring_pipelined", ring),
+                       ("hier_fused", oracle.hier_fold(xs, dtype, g))):
+        t = to_dev(xs, dtype)
+        print(f"[case] short tail AR algo={algo} p={p} n={n} {dtype}", flush=True)
+        B.ra_allreduce_ex(t, algo=algo, **({"group": g} if algo == "hier_fused" else {}))
+        B.ra_stream_status()
+        for r, got in enumerate(from_dev(t, dtype)):
+            assert same_bits(got, want, dtype), f"{algo} rank {r} at {first_diff(got, want, dtype)}"
+    t = to_dev(xs, dtype)
+    print(f"[case] short tail RS fused p={p} n={n} {dtype}", flush=True)
+    B.ra_reduce_scatter_ex(t, algo="fused")
+    B.ra_stream_status()
+    for r, got in enumerate(from_dev(t, dtype)):
+        want = oracle.rs_owned(xs, dtype, r)
+        assert same_bits(got, want, dtype), f"fused RS rank {r} at {first_diff(got, want, dtype)}"
+    gathered, _ = oracle.all_gather(xs, dtype)
+    for algo in ("fused", "ring_pipelined"):
+        t = to_dev(xs, dtype)
+        print(f"[case] short tail AG algo={algo} p={p} n={n} {dtype}", flush=True)
+        B.ra_all_gather_ex(t, algo=algo)
+        B.ra_stream_status()
+        for r, got in enumerate(from_dev(t, dtype)):
+            assert same_bits(got, gathered[r], dtype), f"{algo} AG rank {r}"
 
 
 # ------------------------------------------------------------ beyond one dispatch
