@@ -162,18 +162,20 @@ def time_calls(fn, k, torch, flush=None):
 
 
 def read_traffic(sha, launch_bytes):
-    """HBM bytes per launch from the committed counter summary, if it matches."""
+    """(HBM bytes per launch, kernel name) from the committed counter summary, if
+    it was taken on the current kernel sources and this workload's bytes."""
     if not os.path.exists(TRAFFIC_SUMMARY):
-        return None
+        return None, None
     text = open(TRAFFIC_SUMMARY).read()
     m_sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", text)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     m_wb = re.search(r"workload_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_k = re.search(r"kernel_name:\s*(\S+)", text)
     if not (m_sha and m_b and m_wb) or m_sha.group(1) != sha:
-        return None
+        return None, None
     if abs(float(m_wb.group(1)) - launch_bytes) > 1:
-        return None
-    return float(m_b.group(1))
+        return None, None
+    return float(m_b.group(1)), (m_k.group(1) if m_k else None)
 
 
 def cpu_baseline(bufs, w, sample, torch):
@@ -625,7 +627,10 @@ def main():
     achieved = kernel_bytes / (launch_ms * 1e-3) / 1e9
     sha = kernel_source_sha()
     # the committed counter summary covers the fused kernel only
-    traffic = read_traffic(sha, min_bytes) if args.algo == "fused" else None
+    traffic, traced = read_traffic(sha, min_bytes) if args.algo == "fused" else (None, None)
+    # the kernel the counter run traced; without one, the one-pass family (the
+    # library runs it in read/write phases where those pay, see include/ra.h)
+    kernel = traced or (f"ra::k_fused<{dtype}>" if args.algo == "fused" else args.algo)
 
     result = {
         "metric": METRIC,
@@ -650,7 +655,7 @@ def main():
         "busbw_emulated_GBps": round(2 * (p - 1) / p * S / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "kernel": f"ra::k_fused<{dtype}>" if args.algo == "fused" else args.algo,
+                     "traffic": traffic, "kernel": kernel,
                      "algorithmic_bytes": kernel_bytes,
                      "launch_ms_mean": round(launch_ms, 4),
                      "launch_ms_min": round(min(per), 4),
@@ -670,6 +675,9 @@ def main():
         # steps (the library's default persistent grid: 3 workgroups per CU)
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         runs += [("ring_step_persistent", "ring_step", {"grid": 3 * cus})]
+        # the one-pass all-reduce without read/write phases (the library picks the
+        # phases by itself for this workload)
+        runs += [("fused_no_phases", "fused", {"flags": B.RA_FLAG_NO_PHASES})]
         runs += [("fused_wide_fp32_accumulate", "fused", {"wide": True}),
                  ("fused_avg", "fused", {"op": "avg"}), ("fused_max", "fused", {"op": "max"})]
         for name, algo, kw in runs:

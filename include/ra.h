@@ -146,6 +146,12 @@ typedef enum ra_algo {
                                      stream's ready counters are reallocated (fresh zeros)
                                      and the call's counter numbering starts at 2^31, as
                                      after about 16.7 million calls and a larger one */
+#define RA_FLAG_PHASES 16u        /* RA_ALGO_FUSED all-reduce: run the pass in read and
+                                     write phases (see RA_ALGO_FUSED) whenever the GPU
+                                     holds its grid, at any size and rank count (the
+                                     result is the same either way) */
+#define RA_FLAG_NO_PHASES 32u     /* RA_ALGO_FUSED all-reduce: never use the phases (wins
+                                     over RA_FLAG_PHASES) */
 #define RA_FLAG_WIDE_ACCUM 2u     /* RA_ALGO_FUSED, bfloat16 / float16 / float32 only:
                                      every term is widened exactly to float32
                                      (float64 for float32 buffers), the ring order
@@ -261,6 +267,15 @@ int ra_allreduce(void* const* bufs, int p, int64_t n, int dtype, int op,
  *         and those node sums over nodes d, d+1, ..., rounding every hop.  g = 1
  *         and g = p give the flat ring's bits.  A group that does not divide p:
  *         RA_ERR_INVALID_ARG.  RA_FLAG_WIDE_ACCUM is not available here.
+ *         FUSED, read and write phases: large streaming all-reduces of 6 to 8
+ *         ranks (at least 64 rounds of the grid below) run the same fold on a
+ *         resident grid of 8 workgroups per compute unit whose loads and stores
+ *         take turns chip-wide, in windows timed by the device's constant clock
+ *         and sized for the bytes one round moves at 6.42 TB/s.  The bits are
+ *         those of the plain pass.  The windows assume the call has the GPU's
+ *         memory to itself: work running beside it on other streams slows
+ *         both (RA_FLAG_NO_PHASES turns them off; RA_FLAG_PHASES forces them
+ *         for any size).
  *   opt   may be NULL (all defaults).
  */
 int ra_allreduce_ex(void* const* bufs, int p, int64_t n, int dtype, int op, int algo,

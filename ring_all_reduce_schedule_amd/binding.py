@@ -25,6 +25,8 @@ RA_FLAG_FORCE_TIMEOUT = 1
 RA_FLAG_WIDE_ACCUM = 2
 RA_FLAG_STRESS = 4
 RA_FLAG_RENEW_COUNTERS = 8
+RA_FLAG_PHASES = 16
+RA_FLAG_NO_PHASES = 32
 OPS = {"sum": RA_SUM, "max": RA_MAX, "avg": RA_AVG}
 
 ALGOS = {"default": -1, "ring_step": 0, "ring_pipelined": 1, "ring_bidir": 2,

@@ -165,6 +165,15 @@ int check_op(int op, int dtype) {
 
 bool wide_requested(const ra_options* opt) { return opt && (opt->flags & RA_FLAG_WIDE_ACCUM); }
 
+// The one-pass all-reduce's read/write phases as the options ask (no flag: the
+// library decides; RA_FLAG_NO_PHASES wins over RA_FLAG_PHASES).
+int phase_mode(const ra_options* opt) {
+  if (!opt) return ra::kPhasesAuto;
+  if (opt->flags & RA_FLAG_NO_PHASES) return ra::kPhasesOff;
+  if (opt->flags & RA_FLAG_PHASES) return ra::kPhasesForce;
+  return ra::kPhasesAuto;
+}
+
 // Wider accumulation exists for the one-pass algorithm, for bfloat16, float16
 // and float32 (a maximum is exact, so there it changes nothing).
 int check_wide(const ra_options* opt, int dtype, int algo) {
@@ -405,7 +414,8 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
     ra::RankPtrs P;
     fill_ptrs(bufs, p, &P);
     int grid = 0;
-    hipError_t e = ra::launch_fused(P, p, n, dtype, op, wide_requested(opt), mode, s, &grid);
+    hipError_t e = ra::launch_fused(P, p, n, dtype, op, wide_requested(opt), mode,
+                                    phase_mode(opt), s, &grid);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
     debug_line(call, algo, p, n, dtype, grid);
     return RA_OK;

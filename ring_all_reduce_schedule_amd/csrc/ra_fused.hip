@@ -9,6 +9,10 @@
 // one-GPU all-reduce can move.  All element traffic uses 16-byte vector
 // loads/stores with consecutive lanes on consecutive vectors; chunk edges that
 // fall inside a vector are handled element by element.  Indices are 64-bit.
+#include <cstdlib>
+#include <mutex>
+#include <unordered_map>
+
 #include "ra_elem.h"
 #include "ra_internal.h"
 
@@ -131,11 +135,170 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
 }
 
 
+// ---------------------------------------------------------------- read and write phases
+//
+// The same fold as k_fused on a resident grid whose reads and writes take turns
+// across the whole chip.  Iteration k of every wave (tile b + k * grid) loads
+// and folds in read window k and stores in write window k; the windows follow
+// each other every `period` ticks of the device's constant 100 MHz clock, the
+// read window taking kPhaseReadShare/256 of it.  Every wave places its first
+// window at the first multiple of the period (counted on the clock's low 32
+// bits) at least kPhaseLead ticks after its own start, so all waves keep one
+// grid of windows without exchanging anything: the launch needs no workspace
+// and can be captured in a HIP graph.  A wave whose loads land late stores at
+// once, and one that starts late simply joins a later window.
+//
+// Why: HBM streams 8 ranks' reads alone at 7.09 TB/s and their writes alone at
+// 6.67, but the one-shot pass, whose workgroups each read eight vectors and
+// then write eight, mixes the two at every instant and runs at 6.1-6.35 TB/s
+// (8 x 16 GB bfloat16); on a resident grid left to itself the mix is worse
+// (about 5.6).  With the turns enforced the same bytes moved at 6.39-6.45 TB/s
+// on every box measured, as long as the period leaves the memory enough time:
+// at 8 x 16 GB bfloat16 (134 MB per window pair) 2080-2100 ticks held window
+// for window in every run, 2075 fell behind in one run of three, 2050 in every
+// run, and a wave grid that falls behind runs like the resident grid left to
+// itself.  kPhaseRate sets the period from the bytes of one window pair, with
+// a margin over that edge; RA_PHASE_GBPS overrides it (measurements only).
+// Fewer ranks mean fewer streams at once and a milder mix: at 16 GB per rank
+// (ms, phases against the one-shot pass on one box) p = 8 39.95 / 40.84, p = 6
+// 30.26 / 30.61, p = 4 20.42 / 19.98 -- so the library picks the phases for 6
+// to 8 ranks only.
+constexpr int kPhasedPerCU = 8;                  // 256-thread workgroups: 8 waves per SIMD
+constexpr int64_t kPhaseRate = 6420000000000ll;  // bytes per second the windows are sized for
+constexpr int64_t kPhaseReadShare = 136;         // of 256: reads land up to a round trip late
+constexpr int64_t kMinPhasedIters = 64;          // window pairs a call needs to gain
+constexpr uint32_t kPhaseLead = 500;             // ticks: the grid's dispatch fits in 5 us
+constexpr uint64_t kMaxClockWait = 1000000;      // ticks (10 ms): a bound on any one wait
+constexpr int kPhasedMinRanks = 6, kPhasedMaxRanks = 8;   // where the library picks them
+
+__device__ __forceinline__ void wait_clock(uint64_t t) {
+  const uint64_t now = __builtin_amdgcn_s_memrealtime();
+  if (t <= now || t - now > kMaxClockWait) return;
+  while (__builtin_amdgcn_s_memrealtime() < t) __builtin_amdgcn_s_sleep(1);
+}
+
+template <int DT, int OP, bool WIDE, bool NT>
+__global__ __launch_bounds__(kBlock, kPhasedPerCU) void k_fused_phased(RankPtrs P, ChunkGeo g,
+                                                                      int p, int64_t T,
+                                                                      int64_t ntiles, int edges,
+                                                                      uint32_t period,
+                                                                      uint32_t rwin) {
+  typedef Fold<DT, OP, WIDE> F;
+  constexpr int V = Elem<DT>::V;
+  const int64_t b = blockIdx.x;
+  if (b < edges) fused_edges<DT, OP, WIDE, kAllReduce>(P, g, p, b);
+  uint64_t R = __builtin_amdgcn_s_memrealtime() + kPhaseLead;
+  R += period - (uint32_t)R % period;
+  const uint32_t T32 = (uint32_t)T;
+  const unsigned lane = threadIdx.x;
+  for (int64_t t = b; t < ntiles; t += gridDim.x, R += period) {
+    // the tile index passes through a register the compiler cannot see into:
+    // otherwise it keeps a running pointer per rank across iterations, and the
+    // kernel no longer fits 8 waves per SIMD without spilling
+    uint32_t tt = (uint32_t)t;
+    asm volatile("" : "+s"(tt));
+    const uint32_t c = tt / T32;
+    const int64_t j = (int64_t)(tt - c * T32);
+    const Span sp = split_span<V>(chunk_lo(g, (int)c), chunk_hi(g, (int)c));
+    const int64_t vt = sp.vb + j * kBlock;          // the tile's first vector
+    const bool in = vt + lane >= sp.v0 && vt + lane < sp.v1;
+    wait_clock(R);
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (in) {
+      typename F::A acc = F::start(ld16t<NT>(P.b[c], vt, lane), p);
+      fold_run<NT, F>(acc, P, 0, p, (int)c + 1, p - 1, vt, lane, p);
+      out = F::finish(acc);
+    }
+    wait_clock(R + rwin);
+    if (in) store_all<NT>(P, p, vt, lane, out, -1);
+  }
+}
+
+// Compute units and clock ticks per second of the current device (cached).
+static hipError_t phase_device(int* cus, int64_t* tick_hz) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::unordered_map<int, std::pair<int, int64_t>> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it == cache.end()) {
+    int n = 0, khz = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (e != hipSuccess || khz <= 0) khz = 100000;    // the gfx9 constant clock
+    it = cache.emplace(dev, std::make_pair(n, (int64_t)khz * 1000)).first;
+  }
+  *cus = it->second.first;
+  *tick_hz = it->second.second;
+  return hipSuccess;
+}
+
+static int64_t phase_rate() {
+  static const int64_t rate = [] {
+    const char* v = std::getenv("RA_PHASE_GBPS");
+    const double gbps = v ? std::atof(v) : 0.0;
+    return gbps > 100.0 && gbps < 100000.0 ? (int64_t)(gbps * 1e9) : kPhaseRate;
+  }();
+  return rate;
+}
+
+// The all-reduce as k_fused_phased when `phases` asks for it (kPhasesForce) or
+// allows it (kPhasesAuto: a streaming call of 6 to 8 ranks with at least
+// kMinPhasedIters window pairs) and the device holds the whole grid; *launched
+// false leaves the call to the one-shot kernel.
+template <int DT, int OP, bool WIDE, bool NT>
+static hipError_t phased_launch(const RankPtrs& P, const ChunkGeo& g, int p, int64_t T,
+                                int64_t ntiles, int edges, int phases, hipStream_t s,
+                                int* grid_used, bool* launched) {
+  *launched = false;
+  if (phases == kPhasesOff) return hipSuccess;
+  if (phases == kPhasesAuto && (p < kPhasedMinRanks || p > kPhasedMaxRanks || !NT))
+    return hipSuccess;
+  int cus = 0;
+  int64_t tick_hz = 0;
+  hipError_t e = phase_device(&cus, &tick_hz);
+  if (e != hipSuccess) return e;
+  const unsigned lds = edges ? (unsigned)sizeof(EdgeLds<DT>) : 0u;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &per_cu, reinterpret_cast<const void*>(k_fused_phased<DT, OP, WIDE, NT>), kBlock, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < kPhasedPerCU) return hipSuccess;
+  if (phases == kPhasesAuto) {
+    // a variant that spills registers to memory to fit 8 waves per SIMD (float64
+    // maximum) would stream its spills beside the data: left to the one-shot pass
+    hipFuncAttributes fa;
+    e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(k_fused_phased<DT, OP, WIDE, NT>));
+    if (e != hipSuccess) return e;
+    if (fa.localSizeBytes > 0) return hipSuccess;
+  }
+  const int64_t G = (int64_t)kPhasedPerCU * cus;
+  if (phases == kPhasesAuto && (ntiles + G - 1) / G < kMinPhasedIters) return hipSuccess;
+  // one window pair: G tiles, each p vectors read and p written per thread
+  const int64_t bytes = G * kBlock * 16 * 2 * (int64_t)p;
+  const int64_t rate = phase_rate();
+  const int64_t period = std::max<int64_t>(64, (bytes * (tick_hz / 1000) + rate / 1000 - 1) /
+                                                   (rate / 1000));
+  if (period > 0x7FFFFFFFll) return hipSuccess;
+  const uint32_t rwin = (uint32_t)(period * kPhaseReadShare / 256);
+  const int grid = (int)std::max<int64_t>(std::max<int64_t>(std::min<int64_t>(G, ntiles), edges), 1);
+  *grid_used = grid;
+  hipLaunchKernelGGL((k_fused_phased<DT, OP, WIDE, NT>), dim3(grid), dim3(kBlock), lds, s, P, g, p,
+                     T, ntiles, edges, (uint32_t)period, rwin);
+  *launched = true;
+  return hipGetLastError();
+}
+
+
 // One vector per thread.  Measured on MI355X at 8 x 16 GiB bf16: one vector per
 // thread with the most workgroups in flight streams best (6.40 TB/s on 2pS
 // against 6.35 with two and 6.30 with four).
 template <int DT, int OP, bool WIDE, int MODE>
-static hipError_t fused_launch(const RankPtrs& P, int p, int64_t n, hipStream_t s, int* grid_used) {
+static hipError_t fused_launch(const RankPtrs& P, int p, int64_t n, int phases, hipStream_t s,
+                               int* grid_used) {
   const int V = Elem<DT>::V;
   const ChunkGeo g = make_geo(0, n, p);
   int64_t widest = 0;
@@ -151,6 +314,16 @@ static hipError_t fused_launch(const RankPtrs& P, int p, int64_t n, hipStream_t 
   // the chunks' last tiles are short, in a launch whose tiles are all resident
   const int tail_last = ntiles <= kResidentTiles && short_tail(widest, kBlock);
   if (ntiles + edges > 0xFFFFFFFFll) return hipErrorInvalidValue;   // tile_of decodes 32 bits
+  if constexpr (MODE == kAllReduce) {
+    bool launched = false;
+    const hipError_t e =
+        streaming(p, n, DT)
+            ? phased_launch<DT, OP, WIDE, true>(P, g, p, T, ntiles, edges, phases, s, grid_used,
+                                                &launched)
+            : phased_launch<DT, OP, WIDE, false>(P, g, p, T, ntiles, edges, phases, s, grid_used,
+                                                 &launched);
+    if (e != hipSuccess || launched) return e;
+  }
   const int grid = (int)std::min<int64_t>(ntiles + edges, kMaxGrid);
   const int64_t e0 = edge_start(ntiles, p, tail_last, edges, grid);
   const unsigned lds = edges ? (unsigned)sizeof(EdgeLds<DT>) : 0u;
@@ -167,34 +340,34 @@ static hipError_t fused_launch(const RankPtrs& P, int p, int64_t n, hipStream_t 
 // (dtype, op, wide) combinations that exist: avg needs a float type, wide needs
 // bfloat16, float16 or float32 and a sum or an average (a maximum is exact).
 template <int DT, int MODE>
-static hipError_t fused_op(const RankPtrs& P, int p, int64_t n, int op, bool wide, hipStream_t s,
-                           int* grid_used) {
+static hipError_t fused_op(const RankPtrs& P, int p, int64_t n, int op, bool wide, int phases,
+                           hipStream_t s, int* grid_used) {
   constexpr bool kFloat = DT == 1 || DT == 2 || DT == 3 || DT == 4;
   constexpr bool kWide = DT == 1 || DT == 2 || DT == 3;
-  if (MODE == kAllGather) return fused_launch<DT, kSum, false, MODE>(P, p, n, s, grid_used);
-  if (op == kMax) return fused_launch<DT, kMax, false, MODE>(P, p, n, s, grid_used);
+  if (MODE == kAllGather) return fused_launch<DT, kSum, false, MODE>(P, p, n, phases, s, grid_used);
+  if (op == kMax) return fused_launch<DT, kMax, false, MODE>(P, p, n, phases, s, grid_used);
   if constexpr (kWide) {
     if (wide) {
-      if (op == kAvg) return fused_launch<DT, kAvg, true, MODE>(P, p, n, s, grid_used);
-      return fused_launch<DT, kSum, true, MODE>(P, p, n, s, grid_used);
+      if (op == kAvg) return fused_launch<DT, kAvg, true, MODE>(P, p, n, phases, s, grid_used);
+      return fused_launch<DT, kSum, true, MODE>(P, p, n, phases, s, grid_used);
     }
   }
   if constexpr (kFloat) {
-    if (op == kAvg) return fused_launch<DT, kAvg, false, MODE>(P, p, n, s, grid_used);
+    if (op == kAvg) return fused_launch<DT, kAvg, false, MODE>(P, p, n, phases, s, grid_used);
   }
-  return fused_launch<DT, kSum, false, MODE>(P, p, n, s, grid_used);
+  return fused_launch<DT, kSum, false, MODE>(P, p, n, phases, s, grid_used);
 }
 
 template <int MODE>
 static hipError_t fused_mode(const RankPtrs& P, int p, int64_t n, int dtype, int op, bool wide,
-                             hipStream_t s, int* grid_used) {
+                             int phases, hipStream_t s, int* grid_used) {
   switch (dtype) {
-    case 0: return fused_op<0, MODE>(P, p, n, op, wide, s, grid_used);
-    case 1: return fused_op<1, MODE>(P, p, n, op, wide, s, grid_used);
-    case 2: return fused_op<2, MODE>(P, p, n, op, wide, s, grid_used);
-    case 3: return fused_op<3, MODE>(P, p, n, op, wide, s, grid_used);
-    case 4: return fused_op<4, MODE>(P, p, n, op, wide, s, grid_used);
-    default: return fused_op<5, MODE>(P, p, n, op, wide, s, grid_used);
+    case 0: return fused_op<0, MODE>(P, p, n, op, wide, phases, s, grid_used);
+    case 1: return fused_op<1, MODE>(P, p, n, op, wide, phases, s, grid_used);
+    case 2: return fused_op<2, MODE>(P, p, n, op, wide, phases, s, grid_used);
+    case 3: return fused_op<3, MODE>(P, p, n, op, wide, phases, s, grid_used);
+    case 4: return fused_op<4, MODE>(P, p, n, op, wide, phases, s, grid_used);
+    default: return fused_op<5, MODE>(P, p, n, op, wide, phases, s, grid_used);
   }
 }
 
@@ -350,11 +523,12 @@ hipError_t launch_fused_hier(const RankPtrs& P, int p, int64_t n, int dtype, int
 }
 
 hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, int op, bool wide,
-                        int mode, hipStream_t s, int* grid_used) {
+                        int mode, int phases, hipStream_t s, int* grid_used) {
   switch (mode) {
-    case kReduceScatter: return fused_mode<kReduceScatter>(P, p, n, dtype, op, wide, s, grid_used);
-    case kAllGather: return fused_mode<kAllGather>(P, p, n, dtype, op, wide, s, grid_used);
-    default: return fused_mode<kAllReduce>(P, p, n, dtype, op, wide, s, grid_used);
+    case kReduceScatter:
+      return fused_mode<kReduceScatter>(P, p, n, dtype, op, wide, phases, s, grid_used);
+    case kAllGather: return fused_mode<kAllGather>(P, p, n, dtype, op, wide, phases, s, grid_used);
+    default: return fused_mode<kAllReduce>(P, p, n, dtype, op, wide, phases, s, grid_used);
   }
 }
 
