@@ -267,8 +267,9 @@ int ra_allreduce(void* const* bufs, int p, int64_t n, int dtype, int op,
  *         and those node sums over nodes d, d+1, ..., rounding every hop.  g = 1
  *         and g = p give the flat ring's bits.  A group that does not divide p:
  *         RA_ERR_INVALID_ARG.  RA_FLAG_WIDE_ACCUM is not available here.
- *         FUSED, read and write phases: large streaming all-reduces of 6 to 8
- *         ranks (at least 64 rounds of the grid below) run the same fold on a
+ *         FUSED, read and write phases: large streaming sum and maximum
+ *         all-reduces of 6 to 8 ranks (at least 64 rounds of the grid below;
+ *         averages only when forced) run the same fold on a
  *         resident grid of 8 workgroups per compute unit whose loads and stores
  *         take turns chip-wide, in windows timed by the device's constant clock
  *         and sized for the bytes one round moves at 6.42 TB/s.  The bits are

