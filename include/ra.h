@@ -146,12 +146,13 @@ typedef enum ra_algo {
                                      stream's ready counters are reallocated (fresh zeros)
                                      and the call's counter numbering starts at 2^31, as
                                      after about 16.7 million calls and a larger one */
-#define RA_FLAG_PHASES 16u        /* RA_ALGO_FUSED all-reduce: run the pass in read and
-                                     write phases (see RA_ALGO_FUSED) whenever the GPU
-                                     holds its grid, at any size and rank count (the
-                                     result is the same either way) */
-#define RA_FLAG_NO_PHASES 32u     /* RA_ALGO_FUSED all-reduce: never use the phases (wins
-                                     over RA_FLAG_PHASES) */
+#define RA_FLAG_PHASES 16u        /* RA_ALGO_FUSED (all-reduce, reduce-scatter, all-gather):
+                                     run the pass in read and write phases (see
+                                     ra_allreduce_ex) whenever the GPU holds its grid, at
+                                     any size and rank count (the result is the same
+                                     either way) */
+#define RA_FLAG_NO_PHASES 32u     /* RA_ALGO_FUSED: never use the phases (wins over
+                                     RA_FLAG_PHASES) */
 #define RA_FLAG_WIDE_ACCUM 2u     /* RA_ALGO_FUSED, bfloat16 / float16 / float32 only:
                                      every term is widened exactly to float32
                                      (float64 for float32 buffers), the ring order
@@ -234,7 +235,10 @@ int ra_reduce_scatter(void* const* bufs, int p, int64_t n, int dtype, int op,
  * (r + 1 - s) mod p overwrites rank r+1's copy; afterwards every rank holds every
  * owned chunk.  Only the owned chunks are read, whatever the other chunks hold,
  * so ra_reduce_scatter followed by ra_all_gather equals ra_allreduce for every
- * pairing of the algorithms.  FUSED (the default) moves p*S bytes.
+ * pairing of the algorithms.  FUSED (the default) moves p*S bytes; large
+ * streaming calls of 8 ranks run it in read and write phases (see
+ * ra_allreduce_ex), sized for 6.35 TB/s.  FUSED reduce-scatters take the phases
+ * only when RA_FLAG_PHASES asks (they measured no faster).
  */
 int ra_all_gather(void* const* bufs, int p, int64_t n, int dtype, hipStream_t stream);
 
@@ -268,8 +272,8 @@ int ra_allreduce(void* const* bufs, int p, int64_t n, int dtype, int op,
  *         and g = p give the flat ring's bits.  A group that does not divide p:
  *         RA_ERR_INVALID_ARG.  RA_FLAG_WIDE_ACCUM is not available here.
  *         FUSED, read and write phases: large streaming sum and maximum
- *         all-reduces of 6 to 8 ranks (at least 64 rounds of the grid below;
- *         averages only when forced) run the same fold on a
+ *         all-reduces of 8 ranks (at least 64 rounds of the grid below; other
+ *         rank counts and averages only when forced) run the same fold on a
  *         resident grid of 8 workgroups per compute unit whose loads and stores
  *         take turns chip-wide, in windows timed by the device's constant clock
  *         and sized for the bytes one round moves at 6.42 TB/s.  The bits are

@@ -159,17 +159,29 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
 // run, and a wave grid that falls behind runs like the resident grid left to
 // itself.  kPhaseRate sets the period from the bytes of one window pair, with
 // a margin over that edge; RA_PHASE_GBPS overrides it (measurements only).
-// Fewer ranks mean fewer streams at once and a milder mix: at 16 GB per rank
-// (ms, phases against the one-shot pass on one box) p = 8 39.95 / 40.84, p = 6
-// 30.26 / 30.61, p = 4 20.42 / 19.98 -- so the library picks the phases for 6
-// to 8 ranks only.
+// The rate the memory sustains in phases depends on the rank count and on where
+// the buffers lie.  At 16 GB per rank (ms, phases against the one-shot pass, two
+// boxes): p = 8 39.95 / 40.84 and 39.92 / 42.06, p = 7 38.28 / 38.45 and 38.39 /
+// 38.94, p = 6 30.26 / 30.61 and 36.59 / 35.10, p = 5 28.81 / 26.14, p = 4
+// 20.42 / 19.98; at 7 ranks and fewer the windows fell behind on some box, so
+// the library picks the phases for 8 ranks only, where they held on every box.
+// The standalone all-gather (one read, p - 1 writes per tile) gains as well at
+// p = 8: 20.03 and 20.22 ms sized for 6.4 and 6.35 TB/s against 21.02 and 21.37
+// (6.6 fell behind); it takes them, sized for 6.35.
+// The standalone reduce-scatter (p reads, one write) does not: at best 24.48
+// against 24.66 ms, and behind its windows from 6.6 TB/s up -- its short write
+// windows cost a memory round trip each -- so it takes them only when forced.
 constexpr int kPhasedPerCU = 8;                  // 256-thread workgroups: 8 waves per SIMD
-constexpr int64_t kPhaseRate = 6420000000000ll;  // bytes per second the windows are sized for
-constexpr int64_t kPhaseReadShare = 136;         // of 256: reads land up to a round trip late
+// bytes per second a window pair is sized for, and the read window's share of
+// the period (of 256), per mode: all-reduce (reads land up to a round trip
+// late), all-gather (one read in p), reduce-scatter (forced only)
+constexpr int64_t kPhaseRate = 6420000000000ll, kPhaseReadShare = 136;
+constexpr int64_t kPhaseRateAG = 6350000000000ll, kPhaseReadShareAG = 38;
+constexpr int64_t kPhaseRateRS = 6000000000000ll, kPhaseReadShareRS = 226;
 constexpr int64_t kMinPhasedIters = 64;          // window pairs a call needs to gain
 constexpr uint32_t kPhaseLead = 500;             // ticks: the grid's dispatch fits in 5 us
 constexpr uint64_t kMaxClockWait = 1000000;      // ticks (10 ms): a bound on any one wait
-constexpr int kPhasedMinRanks = 6, kPhasedMaxRanks = 8;   // where the library picks them
+constexpr int kPhasedRanks = 8;                  // the rank count the library picks them for
 
 __device__ __forceinline__ void wait_clock(uint64_t t) {
   const uint64_t now = __builtin_amdgcn_s_memrealtime();
@@ -177,7 +189,7 @@ __device__ __forceinline__ void wait_clock(uint64_t t) {
   while (__builtin_amdgcn_s_memrealtime() < t) __builtin_amdgcn_s_sleep(1);
 }
 
-template <int DT, int OP, bool WIDE, bool NT>
+template <int DT, int OP, bool WIDE, bool NT, int MODE>
 __global__ __launch_bounds__(kBlock, kPhasedPerCU) void k_fused_phased(RankPtrs P, ChunkGeo g,
                                                                       int p, int64_t T,
                                                                       int64_t ntiles, int edges,
@@ -186,7 +198,7 @@ __global__ __launch_bounds__(kBlock, kPhasedPerCU) void k_fused_phased(RankPtrs 
   typedef Fold<DT, OP, WIDE> F;
   constexpr int V = Elem<DT>::V;
   const int64_t b = blockIdx.x;
-  if (b < edges) fused_edges<DT, OP, WIDE, kAllReduce>(P, g, p, b);
+  if (b < edges) fused_edges<DT, OP, WIDE, MODE>(P, g, p, b);
   uint64_t R = __builtin_amdgcn_s_memrealtime() + kPhaseLead;
   R += period - (uint32_t)R % period;
   const uint32_t T32 = (uint32_t)T;
@@ -202,15 +214,25 @@ __global__ __launch_bounds__(kBlock, kPhasedPerCU) void k_fused_phased(RankPtrs 
     const Span sp = split_span<V>(chunk_lo(g, (int)c), chunk_hi(g, (int)c));
     const int64_t vt = sp.vb + j * kBlock;          // the tile's first vector
     const bool in = vt + lane >= sp.v0 && vt + lane < sp.v1;
+    const int owner = c == 0 ? p - 1 : (int)c - 1;
     wait_clock(R);
     u32x4 out = {0u, 0u, 0u, 0u};
     if (in) {
-      typename F::A acc = F::start(ld16t<NT>(P.b[c], vt, lane), p);
-      fold_run<NT, F>(acc, P, 0, p, (int)c + 1, p - 1, vt, lane, p);
-      out = F::finish(acc);
+      if (MODE == kAllGather) {
+        out = ld16t<NT>(P.b[owner], vt, lane);
+      } else {
+        typename F::A acc = F::start(ld16t<NT>(P.b[c], vt, lane), p);
+        fold_run<NT, F>(acc, P, 0, p, (int)c + 1, p - 1, vt, lane, p);
+        out = F::finish(acc);
+      }
     }
     wait_clock(R + rwin);
-    if (in) store_all<NT>(P, p, vt, lane, out, -1);
+    if (in) {
+      if (MODE == kReduceScatter)
+        st16t<NT>(P.b[owner], vt, lane, out);
+      else
+        store_all<NT>(P, p, vt, lane, out, MODE == kAllGather ? owner : -1);
+    }
   }
 }
 
@@ -236,26 +258,33 @@ static hipError_t phase_device(int* cus, int64_t* tick_hz) {
   return hipSuccess;
 }
 
-static int64_t phase_rate() {
-  static const int64_t rate = [] {
-    const char* v = std::getenv("RA_PHASE_GBPS");
-    const double gbps = v ? std::atof(v) : 0.0;
-    return gbps > 100.0 && gbps < 100000.0 ? (int64_t)(gbps * 1e9) : kPhaseRate;
-  }();
-  return rate;
+// The rate a window pair is sized for and the read window's share of it (of 256),
+// per mode, or RA_PHASE_GBPS / RA_PHASE_READ256 when set (measurements only).
+static void phase_shape(int mode, int64_t* rate, int64_t* read256) {
+  *rate = mode == kAllGather ? kPhaseRateAG : mode == kReduceScatter ? kPhaseRateRS : kPhaseRate;
+  *read256 = mode == kAllGather      ? kPhaseReadShareAG
+             : mode == kReduceScatter ? kPhaseReadShareRS
+                                      : kPhaseReadShare;
+  const char* v = std::getenv("RA_PHASE_GBPS");
+  const double gbps = v ? std::atof(v) : 0.0;
+  if (gbps > 100.0 && gbps < 100000.0) *rate = (int64_t)(gbps * 1e9);
+  const char* w = std::getenv("RA_PHASE_READ256");
+  const int share = w ? std::atoi(w) : 0;
+  if (share > 0 && share < 256) *read256 = share;
 }
 
-// The all-reduce as k_fused_phased when `phases` asks for it (kPhasesForce) or
-// allows it (kPhasesAuto: a streaming call of 6 to 8 ranks with at least
-// kMinPhasedIters window pairs) and the device holds the whole grid; *launched
-// false leaves the call to the one-shot kernel.
-template <int DT, int OP, bool WIDE, bool NT>
+// The pass as k_fused_phased when `phases` asks for it (kPhasesForce) or allows
+// it (kPhasesAuto: an all-reduce or all-gather that streams, of 8 ranks, with
+// at least kMinPhasedIters window pairs) and the device holds the whole
+// grid; *launched false leaves the call to the one-shot kernel.
+template <int DT, int OP, bool WIDE, bool NT, int MODE>
 static hipError_t phased_launch(const RankPtrs& P, const ChunkGeo& g, int p, int64_t T,
                                 int64_t ntiles, int edges, int phases, hipStream_t s,
                                 int* grid_used, bool* launched) {
   *launched = false;
   if (phases == kPhasesOff) return hipSuccess;
-  if (phases == kPhasesAuto && (p < kPhasedMinRanks || p > kPhasedMaxRanks || !NT))
+  if (phases == kPhasesAuto &&
+      (MODE == kReduceScatter || p != kPhasedRanks || !NT))
     return hipSuccess;
   int cus = 0;
   int64_t tick_hz = 0;
@@ -264,30 +293,37 @@ static hipError_t phased_launch(const RankPtrs& P, const ChunkGeo& g, int p, int
   const unsigned lds = edges ? (unsigned)sizeof(EdgeLds<DT>) : 0u;
   int per_cu = 0;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, reinterpret_cast<const void*>(k_fused_phased<DT, OP, WIDE, NT>), kBlock, lds);
+      &per_cu, reinterpret_cast<const void*>(k_fused_phased<DT, OP, WIDE, NT, MODE>), kBlock, lds);
   if (e != hipSuccess) return e;
   if (per_cu < kPhasedPerCU) return hipSuccess;
   if (phases == kPhasesAuto) {
     // a variant that spills registers to memory to fit 8 waves per SIMD (float64
     // maximum) would stream its spills beside the data: left to the one-shot pass
     hipFuncAttributes fa;
-    e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(k_fused_phased<DT, OP, WIDE, NT>));
+    e = hipFuncGetAttributes(&fa,
+                             reinterpret_cast<const void*>(k_fused_phased<DT, OP, WIDE, NT, MODE>));
     if (e != hipSuccess) return e;
     if (fa.localSizeBytes > 0) return hipSuccess;
   }
   const int64_t G = (int64_t)kPhasedPerCU * cus;
   if (phases == kPhasesAuto && (ntiles + G - 1) / G < kMinPhasedIters) return hipSuccess;
-  // one window pair: G tiles, each p vectors read and p written per thread
-  const int64_t bytes = G * kBlock * 16 * 2 * (int64_t)p;
-  const int64_t rate = phase_rate();
+  // one window pair: G tiles, each moving per thread p vectors read and p written
+  // (all-reduce), p read and 1 written (reduce-scatter), 1 read and p - 1 written
+  // (all-gather)
+  const int64_t per_tile = MODE == kAllReduce ? 2 * (int64_t)p : MODE == kReduceScatter
+                                                                      ? (int64_t)p + 1
+                                                                      : (int64_t)p;
+  const int64_t bytes = G * kBlock * 16 * per_tile;
+  int64_t rate = 0, read256 = 0;
+  phase_shape(MODE, &rate, &read256);
   const int64_t period = std::max<int64_t>(64, (bytes * (tick_hz / 1000) + rate / 1000 - 1) /
                                                    (rate / 1000));
   if (period > 0x7FFFFFFFll) return hipSuccess;
-  const uint32_t rwin = (uint32_t)(period * kPhaseReadShare / 256);
+  const uint32_t rwin = (uint32_t)(period * read256 / 256);
   const int grid = (int)std::max<int64_t>(std::max<int64_t>(std::min<int64_t>(G, ntiles), edges), 1);
   *grid_used = grid;
-  hipLaunchKernelGGL((k_fused_phased<DT, OP, WIDE, NT>), dim3(grid), dim3(kBlock), lds, s, P, g, p,
-                     T, ntiles, edges, (uint32_t)period, rwin);
+  hipLaunchKernelGGL((k_fused_phased<DT, OP, WIDE, NT, MODE>), dim3(grid), dim3(kBlock), lds, s, P,
+                     g, p, T, ntiles, edges, (uint32_t)period, rwin);
   *launched = true;
   return hipGetLastError();
 }
@@ -314,14 +350,14 @@ static hipError_t fused_launch(const RankPtrs& P, int p, int64_t n, int phases, 
   // the chunks' last tiles are short, in a launch whose tiles are all resident
   const int tail_last = ntiles <= kResidentTiles && short_tail(widest, kBlock);
   if (ntiles + edges > 0xFFFFFFFFll) return hipErrorInvalidValue;   // tile_of decodes 32 bits
-  if constexpr (MODE == kAllReduce) {
+  {
     bool launched = false;
     const hipError_t e =
         streaming(p, n, DT)
-            ? phased_launch<DT, OP, WIDE, true>(P, g, p, T, ntiles, edges, phases, s, grid_used,
-                                                &launched)
-            : phased_launch<DT, OP, WIDE, false>(P, g, p, T, ntiles, edges, phases, s, grid_used,
-                                                 &launched);
+            ? phased_launch<DT, OP, WIDE, true, MODE>(P, g, p, T, ntiles, edges, phases, s,
+                                                      grid_used, &launched)
+            : phased_launch<DT, OP, WIDE, false, MODE>(P, g, p, T, ntiles, edges, phases, s,
+                                                       grid_used, &launched);
     if (e != hipSuccess || launched) return e;
   }
   const int grid = (int)std::min<int64_t>(ntiles + edges, kMaxGrid);

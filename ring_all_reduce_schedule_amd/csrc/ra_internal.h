@@ -34,16 +34,15 @@ struct SyncCfg {
 
 // Launch descriptions return the number of workgroups used through *grid_used.
 
-// Whether the one-pass all-reduce runs with read and write phases
-// (k_fused_phased): where the library finds it pays, always where the grid fits,
-// or never.
+// Whether a one-pass call runs with read and write phases (k_fused_phased):
+// where the library finds it pays, always where the grid fits, or never.
 enum PhaseMode { kPhasesAuto = 0, kPhasesForce = 1, kPhasesOff = 2 };
 
 // One pass: each element folded in its chunk's ring order with reduction `op`
 // (wide: accumulated in the wider type).  mode 0 stores the result to all ranks
 // (all-reduce), 1 only to the chunk's owner (reduce-scatter), 2 copies each
 // owner's chunk to the other ranks (all-gather; op and wide unused).  phases: a
-// PhaseMode, used by mode 0 only.
+// PhaseMode.
 hipError_t launch_fused(const RankPtrs& P, int p, int64_t n, int dtype, int op, bool wide,
                         int mode, int phases, hipStream_t s, int* grid_used);
 

@@ -4,8 +4,8 @@ RA_FLAG_PHASES forces the phased kernel at any size, so these cases reach it wit
 one rank, ragged chunks, chunk edge elements, more ranks than one batch of loads
 (9, 16, 64), every element type and reduction and the wide accumulation; each
 result must equal the oracle's ring order bit for bit, as the plain pass does.
-The library picks the phases by itself only for large streaming calls of 6 to 8
-ranks: the full-size workload tests (8 x 16 GB bfloat16) check that default path,
+The library picks the phases by itself only for large streaming all-reduces and
+all-gathers of 8 ranks: the full-size workload tests (8 x 16 GB bfloat16) check that default path,
 and a 1.6 GB case here compares the phases with the plain pass on the same inputs.
 """
 
@@ -129,3 +129,34 @@ def test_forced_phases_graph_replays():
         torch.cuda.synchronize()
         for r, got in enumerate(from_dev(bufs, dtype)):
             assert same_bits(got, want, dtype), f"replay {k} rank {r} at {first_diff(got, want, dtype)}"
+
+
+@pytest.mark.parametrize("p,n,dtype", [(2, 7, "float32"), (3, 1_003, "int32"),
+                                       (8, 100_003, "bfloat16"), (9, 300_001, "float32"),
+                                       (16, 70_001, "bfloat16")])
+def test_forced_phases_reduce_scatter_then_all_gather(p, n, dtype):
+    """The fused reduce-scatter (each rank's owned chunk folded in ring order, the
+    other chunks left as they were) and the fused all-gather (each owner's chunk
+    copied to the other ranks) in phases, against the oracle."""
+    require_gpu()
+    xs = inputs.make_inputs(p, n, dtype, seed=31 * p + n, sigma=1.0)
+    t = to_dev(xs, dtype)
+    print(f"[case] RS/AG fused phases p={p} n={n} dtype={dtype}", flush=True)
+    B.ra_reduce_scatter_ex(t, algo="fused", flags=PHASES)
+    B.ra_stream_status()
+    got = from_dev(t, dtype)
+    for r in range(p):
+        want = oracle.rs_owned(xs, dtype, r)
+        assert same_bits(got[r], want, dtype), f"rank {r} at {first_diff(got[r], want, dtype)}"
+    B.ra_all_gather_ex(t, algo="fused", flags=PHASES)
+    B.ra_stream_status()
+    want = oracle.ring_fold(xs, dtype)
+    for r, f in enumerate(from_dev(t, dtype)):
+        assert same_bits(f, want, dtype), f"rank {r} at {first_diff(f, want, dtype)}"
+    # the all-gather alone on buffers that hold arbitrary values
+    t = to_dev(xs, dtype)
+    B.ra_all_gather_ex(t, algo="fused", flags=PHASES)
+    B.ra_stream_status()
+    want, _ = oracle.all_gather(xs, dtype)
+    for r, g in enumerate(from_dev(t, dtype)):
+        assert same_bits(g, want[r], dtype), f"all-gather rank {r} at {first_diff(g, want[r], dtype)}"
