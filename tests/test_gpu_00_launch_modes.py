@@ -1,4 +1,5 @@
-"""Which launches the step algorithms choose (through the C ABI, RA_DEBUG=1).
+"""Which launches the step algorithms and the one-pass calls choose (through the C
+ABI, RA_DEBUG=1).
 
 With RA_DEBUG=1 the library prints one line per call with the grid and the
 number of kernel launches.  A child process runs a few calls and the test checks
@@ -12,6 +13,10 @@ the documented choices:
   from 4 MiB per rank, 1024-thread ones from 16 MiB (1 per compute unit);
 * the slice-carrying pipelined ring: one launch, one workgroup per 4 KiB slice
   of every chunk.
+* the one-pass all-reduce and all-gather of 8 ranks on streaming sizes with at
+  least 64 rounds of the phased grid: 8 workgroups per compute unit (read/write
+  phases); averages, reduce-scatters, other rank counts and small calls: one
+  workgroup per tile, unless RA_FLAG_PHASES forces the phases.
 
 Every launch is an ordinary one (persistent grids are sized to stay resident,
 not launched cooperatively), so the child can run while the test process holds
@@ -78,3 +83,52 @@ def test_step_launch_choices():
     # 10 Mi bf16 per rank: 40 tiles of 1024 x 4 per chunk, one workgroup per compute unit
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     assert got[7] == ("ring_channels", 10 << 20, min(cus, 8 * 40), 1)
+
+
+PHASE_CHILD = r"""
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+from ring_all_reduce_schedule_amd import binding as B
+def bufs(p, n):
+    return [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
+big = bufs(8, 1 << 29)              # 1 GiB per rank: 262,144 tiles, 128 rounds of 2048
+B.ra_allreduce_ex(big, algo="fused")                                   # phases
+B.ra_allreduce_ex(big, algo="fused", flags=B.RA_FLAG_NO_PHASES)        # one-shot
+B.ra_allreduce_ex(big, algo="fused", op="avg")                         # averages: one-shot
+B.ra_all_gather_ex(big, algo="fused")                                  # phases
+B.ra_reduce_scatter_ex(big, algo="fused")                              # one-shot
+B.ra_allreduce_ex(big[:7], algo="fused")                               # 7 ranks: one-shot
+small = bufs(8, 1 << 23)            # 128 MiB in all: cached, 4096 tiles
+B.ra_allreduce_ex(small, algo="fused")                                 # one-shot
+B.ra_allreduce_ex(small, algo="fused", flags=B.RA_FLAG_PHASES)         # forced
+B.ra_stream_status()
+torch.cuda.synchronize()
+"""
+
+
+def test_fused_phase_choices():
+    """The one-pass calls that run in read/write phases show the phased grid,
+    8 workgroups per compute unit; the others one workgroup per tile."""
+    require_gpu()
+    env = dict(os.environ, RA_DEBUG="1")
+    print("[case] child process with RA_DEBUG=1 (phase choices)", flush=True)
+    res = subprocess.run([sys.executable, "-c", PHASE_CHILD, ROOT], env=env, capture_output=True,
+                         text=True, timeout=300)
+    assert res.returncode == 0, res.stderr[-2000:]
+    got = []
+    for ln in res.stderr.splitlines():
+        m = re.match(r"\[ra\] (\w+) algo=(\w+) p=(\d+) n=(\d+) dtype=\d+ grid=(\d+)", ln)
+        if m:
+            got.append((m.group(1), int(m.group(3)), int(m.group(5))))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    phased = 8 * cus
+    tiles = 8 * ((1 << 29) // 8 // 8 // 256)
+    assert got[0] == ("allreduce", 8, phased)
+    assert got[1] == ("allreduce", 8, tiles)
+    assert got[2] == ("allreduce", 8, tiles)
+    assert got[3] == ("all_gather", 8, phased)
+    assert got[4] == ("reduce_scatter", 8, tiles)
+    assert got[5][:2] == ("allreduce", 7) and got[5][2] > phased
+    assert got[6] == ("allreduce", 8, 8 * ((1 << 23) // 8 // 8 // 256))
+    assert got[7] == ("allreduce", 8, min(phased, 4096))
+    assert len(got) == 8, got
