@@ -160,3 +160,26 @@ def test_forced_phases_reduce_scatter_then_all_gather(p, n, dtype):
     want, _ = oracle.all_gather(xs, dtype)
     for r, g in enumerate(from_dev(t, dtype)):
         assert same_bits(g, want[r], dtype), f"all-gather rank {r} at {first_diff(g, want[r], dtype)}"
+
+
+def test_forced_phases_on_two_streams_at_once():
+    """Two phased all-reduces on separate buffers and streams, enqueued together:
+    their grids share the compute units (the kernel has no waits between
+    workgroups, so a workgroup that starts late only joins a later window), and
+    each result must still equal the oracle's."""
+    require_gpu()
+    dtype = "bfloat16"
+    cases = [inputs.make_inputs(8, 400_003, dtype, seed=41), inputs.make_inputs(8, 250_001, dtype, seed=43)]
+    devs = [to_dev(xs, dtype) for xs in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    print("[case] two streams, forced phases", flush=True)
+    torch.cuda.synchronize()
+    for t, st in zip(devs, streams):
+        B.ra_allreduce_ex(t, algo="fused", flags=PHASES, stream=st)
+    for st in streams:
+        B.ra_stream_status(st)
+    torch.cuda.synchronize()
+    for xs, t in zip(cases, devs):
+        want = oracle.ring_fold(xs, dtype)
+        for r, g in enumerate(from_dev(t, dtype)):
+            assert same_bits(g, want, dtype), f"rank {r} first diff {first_diff(g, want, dtype)}"
