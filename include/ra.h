@@ -235,8 +235,8 @@ int ra_reduce_scatter(void* const* bufs, int p, int64_t n, int dtype, int op,
  * (r + 1 - s) mod p overwrites rank r+1's copy; afterwards every rank holds every
  * owned chunk.  Only the owned chunks are read, whatever the other chunks hold,
  * so ra_reduce_scatter followed by ra_all_gather equals ra_allreduce for every
- * pairing of the algorithms.  FUSED (the default) moves p*S bytes; large
- * streaming calls of 8 ranks run it in read and write phases (see
+ * pairing of the algorithms.  FUSED (the default) moves p*S bytes; calls of 8
+ * ranks of at least 12 GiB each run it in read and write phases (see
  * ra_allreduce_ex), sized for 6.35 TB/s.  FUSED reduce-scatters take the phases
  * only when RA_FLAG_PHASES asks (they measured no faster).
  */
@@ -271,9 +271,9 @@ int ra_allreduce(void* const* bufs, int p, int64_t n, int dtype, int op,
  *         and those node sums over nodes d, d+1, ..., rounding every hop.  g = 1
  *         and g = p give the flat ring's bits.  A group that does not divide p:
  *         RA_ERR_INVALID_ARG.  RA_FLAG_WIDE_ACCUM is not available here.
- *         FUSED, read and write phases: large streaming sum and maximum
- *         all-reduces of 8 ranks (at least 64 rounds of the grid below; other
- *         rank counts and averages only when forced) run the same fold on a
+ *         FUSED, read and write phases: sum and maximum all-reduces of 8
+ *         ranks of at least 12 GiB each (other sizes, rank counts and averages
+ *         only when forced) run the same fold on a
  *         resident grid of 8 workgroups per compute unit whose loads and stores
  *         take turns chip-wide, in windows timed by the device's constant clock
  *         and sized for the bytes one round moves at 6.42 TB/s.  The bits are

@@ -168,6 +168,13 @@ __global__ __launch_bounds__(kBlock) void k_fused(RankPtrs P, ChunkGeo g, int p,
 // The standalone all-gather (one read, p - 1 writes per tile) gains as well at
 // p = 8: 20.03 and 20.22 ms sized for 6.4 and 6.35 TB/s against 21.02 and 21.37
 // (6.6 fell behind); it takes them, sized for 6.35.
+// Smaller buffers lie closer together, and eight streams at the same offsets of
+// buffers less than about 12 GiB apart meet on the same HBM channels: the
+// one-shot pass slows down, but the phases fall behind their windows and lose
+// more.  At 8 ranks (ms, phases / one-shot, one box): 512 MiB per rank 1.761 /
+// 1.559, 1 GiB 3.546 / 3.161, 2 GiB 7.110 / 6.405, 4 GiB 13.27 / 12.57, 8 GiB
+// 21.79 / 21.36, 16 GB 39.94 / 41.57; so the library picks them from 12 GiB per
+// rank.
 // The standalone reduce-scatter (p reads, one write) does not: at best 24.48
 // against 24.66 ms, and behind its windows from 6.6 TB/s up -- its short write
 // windows cost a memory round trip each -- so it takes them only when forced.
@@ -178,7 +185,7 @@ constexpr int kPhasedPerCU = 8;                  // 256-thread workgroups: 8 wav
 constexpr int64_t kPhaseRate = 6420000000000ll, kPhaseReadShare = 136;
 constexpr int64_t kPhaseRateAG = 6350000000000ll, kPhaseReadShareAG = 38;
 constexpr int64_t kPhaseRateRS = 6000000000000ll, kPhaseReadShareRS = 226;
-constexpr int64_t kMinPhasedIters = 64;          // window pairs a call needs to gain
+constexpr int64_t kPhasedMinRankBytes = 12ll << 30;   // bytes per rank the library picks them from
 constexpr uint32_t kPhaseLead = 500;             // ticks: the grid's dispatch fits in 5 us
 constexpr uint64_t kMaxClockWait = 1000000;      // ticks (10 ms): a bound on any one wait
 constexpr int kPhasedRanks = 8;                  // the rank count the library picks them for
@@ -274,17 +281,17 @@ static void phase_shape(int mode, int64_t* rate, int64_t* read256) {
 }
 
 // The pass as k_fused_phased when `phases` asks for it (kPhasesForce) or allows
-// it (kPhasesAuto: an all-reduce or all-gather that streams, of 8 ranks, with
-// at least kMinPhasedIters window pairs) and the device holds the whole
-// grid; *launched false leaves the call to the one-shot kernel.
+// it (kPhasesAuto: an all-reduce or all-gather of 8 ranks of at least
+// kPhasedMinRankBytes each) and the device holds the whole grid; *launched false
+// leaves the call to the one-shot kernel.
 template <int DT, int OP, bool WIDE, bool NT, int MODE>
-static hipError_t phased_launch(const RankPtrs& P, const ChunkGeo& g, int p, int64_t T,
-                                int64_t ntiles, int edges, int phases, hipStream_t s,
+static hipError_t phased_launch(const RankPtrs& P, const ChunkGeo& g, int p, int64_t n,
+                                int64_t T, int64_t ntiles, int edges, int phases, hipStream_t s,
                                 int* grid_used, bool* launched) {
   *launched = false;
   if (phases == kPhasesOff) return hipSuccess;
-  if (phases == kPhasesAuto &&
-      (MODE == kReduceScatter || p != kPhasedRanks || !NT))
+  if (phases == kPhasesAuto && (MODE == kReduceScatter || p != kPhasedRanks || !NT ||
+                                n * (int64_t)sizeof(typename Elem<DT>::S) < kPhasedMinRankBytes))
     return hipSuccess;
   int cus = 0;
   int64_t tick_hz = 0;
@@ -306,7 +313,6 @@ static hipError_t phased_launch(const RankPtrs& P, const ChunkGeo& g, int p, int
     if (fa.localSizeBytes > 0) return hipSuccess;
   }
   const int64_t G = (int64_t)kPhasedPerCU * cus;
-  if (phases == kPhasesAuto && (ntiles + G - 1) / G < kMinPhasedIters) return hipSuccess;
   // one window pair: G tiles, each moving per thread p vectors read and p written
   // (all-reduce), p read and 1 written (reduce-scatter), 1 read and p - 1 written
   // (all-gather)
@@ -354,9 +360,9 @@ static hipError_t fused_launch(const RankPtrs& P, int p, int64_t n, int phases, 
     bool launched = false;
     const hipError_t e =
         streaming(p, n, DT)
-            ? phased_launch<DT, OP, WIDE, true, MODE>(P, g, p, T, ntiles, edges, phases, s,
+            ? phased_launch<DT, OP, WIDE, true, MODE>(P, g, p, n, T, ntiles, edges, phases, s,
                                                       grid_used, &launched)
-            : phased_launch<DT, OP, WIDE, false, MODE>(P, g, p, T, ntiles, edges, phases, s,
+            : phased_launch<DT, OP, WIDE, false, MODE>(P, g, p, n, T, ntiles, edges, phases, s,
                                                        grid_used, &launched);
     if (e != hipSuccess || launched) return e;
   }

@@ -13,10 +13,10 @@ the documented choices:
   from 4 MiB per rank, 1024-thread ones from 16 MiB (1 per compute unit);
 * the slice-carrying pipelined ring: one launch, one workgroup per 4 KiB slice
   of every chunk.
-* the one-pass all-reduce and all-gather of 8 ranks on streaming sizes with at
-  least 64 rounds of the phased grid: 8 workgroups per compute unit (read/write
-  phases); averages, reduce-scatters, other rank counts and small calls: one
-  workgroup per tile, unless RA_FLAG_PHASES forces the phases.
+* the one-pass all-reduce and all-gather of 8 ranks of at least 12 GiB each:
+  8 workgroups per compute unit (read/write phases); averages, reduce-scatters,
+  other rank counts and smaller calls: one workgroup per tile, unless
+  RA_FLAG_PHASES forces the phases.
 
 Every launch is an ordinary one (persistent grids are sized to stay resident,
 not launched cooperatively), so the child can run while the test process holds
@@ -91,13 +91,14 @@ sys.path.insert(0, sys.argv[1])
 from ring_all_reduce_schedule_amd import binding as B
 def bufs(p, n):
     return [torch.zeros(n, dtype=torch.bfloat16, device="cuda") for _ in range(p)]
-big = bufs(8, 1 << 29)              # 1 GiB per rank: 262,144 tiles, 128 rounds of 2048
+big = bufs(8, 6 << 30)              # 12 GiB per rank: the smallest the phases are picked for
 B.ra_allreduce_ex(big, algo="fused")                                   # phases
 B.ra_allreduce_ex(big, algo="fused", flags=B.RA_FLAG_NO_PHASES)        # one-shot
 B.ra_allreduce_ex(big, algo="fused", op="avg")                         # averages: one-shot
 B.ra_all_gather_ex(big, algo="fused")                                  # phases
 B.ra_reduce_scatter_ex(big, algo="fused")                              # one-shot
 B.ra_allreduce_ex(big[:7], algo="fused")                               # 7 ranks: one-shot
+del big
 small = bufs(8, 1 << 23)            # 128 MiB in all: cached, 4096 tiles
 B.ra_allreduce_ex(small, algo="fused")                                 # one-shot
 B.ra_allreduce_ex(small, algo="fused", flags=B.RA_FLAG_PHASES)         # forced
@@ -122,7 +123,7 @@ def test_fused_phase_choices():
             got.append((m.group(1), int(m.group(3)), int(m.group(5))))
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     phased = 8 * cus
-    tiles = 8 * ((1 << 29) // 8 // 8 // 256)
+    tiles = 8 * ((6 << 30) // 8 // 8 // 256)
     assert got[0] == ("allreduce", 8, phased)
     assert got[1] == ("allreduce", 8, tiles)
     assert got[2] == ("allreduce", 8, tiles)

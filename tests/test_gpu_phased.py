@@ -4,8 +4,8 @@ RA_FLAG_PHASES forces the phased kernel at any size, so these cases reach it wit
 one rank, ragged chunks, chunk edge elements, more ranks than one batch of loads
 (9, 16, 64), every element type and reduction and the wide accumulation; each
 result must equal the oracle's ring order bit for bit, as the plain pass does.
-The library picks the phases by itself only for large streaming all-reduces and
-all-gathers of 8 ranks: the full-size workload tests (8 x 16 GB bfloat16) check that default path,
+The library picks the phases by itself only for all-reduces and all-gathers of 8
+ranks of at least 12 GiB each: the full-size workload tests (8 x 16 GB bfloat16) check that default path,
 and a 1.6 GB case here compares the phases with the plain pass on the same inputs.
 """
 
