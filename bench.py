@@ -349,18 +349,24 @@ def phase_measure(bufs, S, p, torch, B):
     """Standalone reduce-scatter and all-gather on the workload's buffers, each
     rated on its own byte floor and on the bytes it moves (phase_bytes)."""
     out = {}
-    for call, algo in (("reduce_scatter", "fused"), ("all_gather", "fused"),
-                       ("reduce_scatter", "ring_pipelined"), ("all_gather", "ring_pipelined"),
-                       ("reduce_scatter", "ring_step"), ("all_gather", "ring_step")):
+    # the fused all-gather twice: as the library picks it (read/write phases at
+    # this workload) and with the phases turned off, on the same buffers
+    for call, algo, name, flags in (
+            ("reduce_scatter", "fused", "fused", 0), ("all_gather", "fused", "fused", 0),
+            ("all_gather", "fused", "fused_no_phases", B.RA_FLAG_NO_PHASES),
+            ("reduce_scatter", "ring_pipelined", "ring_pipelined", 0),
+            ("all_gather", "ring_pipelined", "ring_pipelined", 0),
+            ("reduce_scatter", "ring_step", "ring_step", 0),
+            ("all_gather", "ring_step", "ring_step", 0)):
         floor, moved = phase_bytes(call, algo, p, S)
         f = B.ra_reduce_scatter_ex if call == "reduce_scatter" else B.ra_all_gather_ex
-        fn = lambda f=f, a=algo: f(bufs, algo=a)
+        fn = lambda f=f, a=algo, fl=flags: f(bufs, algo=a, flags=fl)
         fn()
         B.ra_stream_status()
         per, _ = time_calls(fn, 3, torch)
         B.ra_stream_status()
         t = sum(per) / len(per)
-        out[f"{call}_{algo}"] = {"ms": round(t, 3), "bytes_floor": floor,
+        out[f"{call}_{name}"] = {"ms": round(t, 3), "bytes_floor": floor,
                                  "GBps_on_floor": round(floor / (t * 1e-3) / 1e9, 1),
                                  "pct_peak": round(100 * floor / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
                                  "hbm_bytes": moved,
