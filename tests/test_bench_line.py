@@ -108,3 +108,14 @@ def test_summary_line_drops_optional_parts_before_growing_too_long():
     line = json.dumps(bench.summary_line(r))
     assert len(line) <= bench.SUMMARY_MAX_CHARS
     assert json.loads(line)["roofline"]["frac"] == 0.7899
+
+
+def test_counter_summary_matches_the_kernel_sources():
+    """The committed counter summary of the headline kernel was taken on the
+    current one-pass kernel sources: bench.py fills `roofline.traffic` (and the
+    traced kernel's name) from it only while their hash matches, so a change to
+    those sources must come with a new summary."""
+    traffic, kernel = bench.read_traffic(bench.kernel_source_sha(), 2 * 8 * 16_000_000_000)
+    assert traffic is not None, "profiles/fused_p8_bf16_16GB_hbm_traffic.md is stale"
+    assert abs(traffic / (2 * 8 * 16e9) - 1) < 0.01
+    assert kernel and kernel.startswith("ra::k_fused")
